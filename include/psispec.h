@@ -1,0 +1,160 @@
+/*
+ * psispec.h -- C ABI of the Psi-Spec verify step on MI355X (gfx950).
+ *
+ * The verify step of Uno's Psi-Spec sampler: a frozen AR model has scored a block of B drafted
+ * tokens (plus the row after the block) in one pass; the verifier applies an acceptance test to the
+ * drafts in order, keeps the longest accepted run from the start, draws a replacement token from a
+ * corrected residual distribution at the first rejection and discards the rest, or draws one extra
+ * token from the block-end row when every draft passes.  Sources, cited by page title and section:
+ *
+ *   [alphalab] "Uno Ψ-Spec 是什麼？Diffusion-Augmented LLM 如何保留 AR 分布、一次驗證多個 Token":
+ *              §"Uno Ψ-Spec 怎麼運作？完整走一次四個 Token" (steps 1-4 and the full-accept paragraph),
+ *              §"為什麼 lossless 不等於答案完全一樣？" (the output law equals the AR's),
+ *              §"Linear 與 Tree sampler" (one candidate per position vs a pruned prefix tree).
+ *   [lanes]    "Uno / Ψ-Spec — 같은 모델 안에서 초안 뽑고 AR로 도장 찍기":
+ *              §"Ψ-Spec이 한 스텝에서 하는 일" (frozen AR verifies, longest prefix kept),
+ *              §"어디서 왔나" (speculative sampling of Leviathan et al. 2023 as the lineage).
+ *
+ * The pages print no formula.  The rule implemented is the speculative-sampling rule of that
+ * lineage: accept draft d at position i when u_i < min(1, p'_i(d) / q'_i(d)); at the first rejected
+ * position k draw from max(0, p'_k - q'_k) renormalised; after a full accept draw from p'_B.  p' and
+ * q' are softmax(logits / temperature), optionally truncated to the tie-inclusive nucleus of mass
+ * top_p and renormalised.  Uniforms come from Philox4x32-10 (Salmon et al., SC'11) with key = seed
+ * and counter = (request_base + request, position, purpose, step); u = top 53 bits of
+ * (word0 << 32 | word1) times 2^-53.  Purposes: 0 = accept test, 1 = final draw.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; rows are contiguous with V elements.
+ *     The library never allocates or frees: its scratch lives in the caller's `workspace`
+ *     (device memory, >= the size returned by the matching *_workspace query, 256-byte aligned).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream), never
+ *     synchronise the host, and are reentrant.  Concurrent calls need distinct workspaces.
+ *     Outputs are a pure function of the inputs and (seed, step, request_base): reruns are bitwise
+ *     identical.
+ *   - Host-detectable errors (null pointers, bad sizes, temperature <= 0 or not finite, top_p
+ *     outside (0, 1], bad dtype, small workspace) return a negative code and launch nothing;
+ *     a failed launch returns PSISPEC_EHIP.
+ *   - Data errors found on the device never abort: they set bits in status[request] and leave that
+ *     request's other outputs unspecified (but in bounds).  When an input error is flagged
+ *     (NONFINITE, BAD_TOKEN, BAD_PARENT) the remaining status bits are unspecified as well.
+ */
+#ifndef PSISPEC_H
+#define PSISPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PSISPEC_OK = 0,
+  PSISPEC_EINVAL = -1,       /* bad pointer, size or sampling parameter */
+  PSISPEC_EDTYPE = -2,       /* unsupported element type */
+  PSISPEC_EWORKSPACE = -3,   /* workspace missing, too small or misaligned */
+  PSISPEC_EHIP = -4,         /* a HIP call or kernel launch failed */
+  PSISPEC_EUNSUPPORTED = -5  /* a mode that is not implemented */
+} psispec_status;
+
+typedef enum { PSISPEC_F32 = 0, PSISPEC_BF16 = 1 } psispec_dtype;
+
+/* flags */
+#define PSISPEC_FIRST_FROM_TARGET 1u /* Uno layout: position 0 is the AR's own sample and is always
+                                        kept ([alphalab] walkthrough step 1); q row 0 is not read */
+
+/* per-request status bits */
+#define PSISPEC_ST_NONFINITE 1   /* a row read by the request holds NaN/+Inf or no finite logit */
+#define PSISPEC_ST_BAD_TOKEN 2   /* a drafted / node token outside [0, V) */
+#define PSISPEC_ST_Q_ZERO 4      /* the draft probability of a drafted token is 0 (ratio set to
+                                    1 if the target probability is positive, else 0) */
+#define PSISPEC_ST_RESID_ZERO 8  /* residual mass 0 at a rejection: drew from the target row */
+#define PSISPEC_ST_BAD_PARENT 16 /* tree: parent[j] outside [-1, j-1] or depth beyond max_depth */
+
+typedef struct {
+  double temperature;    /* > 0 and finite: logits are divided by it */
+  double top_p;          /* (0, 1]; 1 disables the nucleus truncation */
+  uint64_t seed;         /* Philox key */
+  uint32_t step;         /* Philox counter word 3 */
+  uint32_t request_base; /* global id of request 0 (counter word 0 = request_base + request) */
+  uint32_t flags;        /* PSISPEC_FIRST_FROM_TARGET or 0 */
+  uint32_t reserved;     /* must be 0 */
+} psispec_sampling;
+
+/*
+ * Linear verify ([alphalab] §"Linear 與 Tree sampler": one candidate per position;
+ * walkthrough steps 3-4 and the full-accept paragraph).
+ *
+ *   p_logits     [batch][B+1][V]  target (AR) logits; row i scores draft i, row B is the block end
+ *   q_logits     [batch][B][V]    draft logits; row i is the distribution draft i was drawn from
+ *   dtype        element type of p_logits and q_logits (PSISPEC_F32 or PSISPEC_BF16)
+ *   draft_tokens [batch][B] int32 drafted tokens
+ *   B            1..64;  V >= 1;  batch >= 0 (0 launches nothing)
+ *   s            host pointer to the sampling parameters
+ * Outputs (device):
+ *   accept_len   [batch] int32    k = number of leading drafts kept, in [0, B]
+ *   out_tokens   [batch][B+1]     d_0..d_{k-1}, then the correction (k < B) or bonus (k = B) token,
+ *                                 then -1; k+1 tokens are committed
+ *   ratios       [batch][B] f32   min(1, p'_i(d_i)/q'_i(d_i)) for every i (also past k); nullable
+ *   accept_mask  [batch] u64      bit i set when u_i < ratio_i (every i); nullable
+ *   status       [batch] int32    PSISPEC_ST_* bits; nullable
+ */
+size_t psispec_verify_linear_workspace(int32_t batch, int32_t B, int32_t V, psispec_dtype dtype);
+
+psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits, psispec_dtype dtype,
+                                     const int32_t* draft_tokens, int32_t batch, int32_t B,
+                                     int32_t V, const psispec_sampling* s, int32_t* accept_len,
+                                     int32_t* out_tokens, float* ratios, uint64_t* accept_mask,
+                                     int32_t* status, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/*
+ * Tree verify ([alphalab] §"Linear 與 Tree sampler": several likely candidates per position,
+ * pruned to a finite prefix tree verified at once).  The rule for candidates chosen
+ * deterministically (e.g. top-k of the draft): at node v, children are tried in ascending node
+ * index; child c is kept when u_c < res(tok_c) / R, where res is p'_v with the tokens of the
+ * already rejected siblings removed and R = 1 - their mass; a rejected child's token is removed
+ * from res; when no child is kept (or v is a leaf) one token is drawn from res.  Node ratios are
+ * computed for every node as if all its earlier siblings were rejected.
+ *
+ *   p_logits     [batch][N+1][V]  row 0 = root, row j+1 = node j
+ *   q_logits     must be NULL (sampled-candidate trees are not implemented: PSISPEC_EUNSUPPORTED)
+ *   parent       [batch][N] int32 parent node of node j, -1 = root, must be < j
+ *   node_tokens  [batch][N] int32 token of node j
+ *   max_depth    bound on the depth of any node (1..64)
+ * Uniforms: node c's test at (request, c+1, accept); the final draw at (request, row, draw) where
+ * row is the stopping node's row.
+ * Outputs (device):
+ *   accept_len   [batch] int32            depth of the kept path
+ *   accept_nodes [batch][max_depth]       the kept nodes in order, then -1
+ *   out_tokens   [batch][max_depth+1]     their tokens, then the drawn token, then -1
+ *   node_ratios  [batch][N] f32           nullable
+ *   status       [batch] int32            nullable
+ */
+size_t psispec_verify_tree_workspace(int32_t batch, int32_t N, int32_t V, psispec_dtype dtype);
+
+psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, psispec_dtype dtype,
+                                   const int32_t* parent, const int32_t* node_tokens, int32_t batch,
+                                   int32_t N, int32_t V, int32_t max_depth,
+                                   const psispec_sampling* s, int32_t* accept_len,
+                                   int32_t* accept_nodes, int32_t* out_tokens, float* node_ratios,
+                                   int32_t* status, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* Message for a return code (static string). */
+const char* psispec_strerror(psispec_status code);
+
+/*
+ * Kernel timing (for benchmarks).  While enabled, every kernel launch of the library is bracketed
+ * by HIP events recorded on the call's stream.  psispec_timing_read synchronises those events and
+ * returns, per kernel name, the summed device milliseconds and the launch count since the last
+ * enable; it returns the number of kernels written (at most max_kernels).  names receives
+ * max_kernels fixed slots of 64 bytes (NUL-terminated).
+ */
+psispec_status psispec_timing_enable(int32_t on);
+int32_t psispec_timing_read(char* names, float* total_ms, int32_t* launches, int32_t max_kernels);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PSISPEC_H */

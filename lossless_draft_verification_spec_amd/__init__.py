@@ -1,0 +1,209 @@
+"""Psi-Spec verify step on MI355X: Python binding of libpsispec (HIP, gfx950).
+
+The functions below only marshal arguments: they check shapes, allocate outputs and the workspace
+with torch on the tensors' device, and call the C ABI declared in include/psispec.h on torch's
+current stream.  Every step of the verify runs in the library's HIP kernels; there is no fallback:
+if libpsispec.so is missing or a tensor is not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpsispec.so")
+
+PSISPEC_F32, PSISPEC_BF16 = 0, 1
+PSISPEC_FIRST_FROM_TARGET = 1
+ST_NONFINITE, ST_BAD_TOKEN, ST_Q_ZERO, ST_RESID_ZERO, ST_BAD_PARENT = 1, 2, 4, 8, 16
+
+EXPORTS = ("psispec_verify_linear_workspace", "psispec_verify_linear",
+           "psispec_verify_tree_workspace", "psispec_verify_tree", "psispec_strerror",
+           "psispec_timing_enable", "psispec_timing_read")
+
+
+class PsispecError(RuntimeError):
+    pass
+
+
+class psispec_sampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_double), ("top_p", ctypes.c_double),
+                ("seed", ctypes.c_uint64), ("step", ctypes.c_uint32),
+                ("request_base", ctypes.c_uint32), ("flags", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libpsispec.so (built in-tree by `python -m lossless_draft_verification_spec_amd.build`)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise PsispecError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m lossless_draft_verification_spec_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.psispec_verify_linear_workspace.argtypes = [i32, i32, i32, i32]
+        L.psispec_verify_linear_workspace.restype = sz
+        L.psispec_verify_linear.argtypes = [P, P, i32, P, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
+        L.psispec_verify_linear.restype = i32
+        L.psispec_verify_tree_workspace.argtypes = [i32, i32, i32, i32]
+        L.psispec_verify_tree_workspace.restype = sz
+        L.psispec_verify_tree.argtypes = [P, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P,
+                                          sz, P]
+        L.psispec_verify_tree.restype = i32
+        L.psispec_strerror.argtypes = [i32]
+        L.psispec_strerror.restype = ctypes.c_char_p
+        L.psispec_timing_enable.argtypes = [i32]
+        L.psispec_timing_enable.restype = i32
+        L.psispec_timing_read.argtypes = [P, P, P, i32]
+        L.psispec_timing_read.restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise PsispecError(f"{what}: {lib().psispec_strerror(rc).decode()} (code {rc})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PSISPEC_BF16
+    if t.dtype == torch.float32:
+        return PSISPEC_F32
+    raise PsispecError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise PsispecError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise PsispecError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _sampling(temperature, top_p, seed, step, request_base, flags):
+    return psispec_sampling(float(temperature), float(top_p), int(seed) & (2**64 - 1),
+                            int(step) & 0xFFFFFFFF, int(request_base) & 0xFFFFFFFF, int(flags), 0)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def linear_workspace_bytes(batch, B, V, dtype) -> int:
+    return int(lib().psispec_verify_linear_workspace(batch, B, V, dtype))
+
+
+def tree_workspace_bytes(batch, N, V, dtype) -> int:
+    return int(lib().psispec_verify_tree_workspace(batch, N, V, dtype))
+
+
+def psispec_verify_linear(p_logits: torch.Tensor, q_logits: torch.Tensor, draft_tokens: torch.Tensor,
+                          temperature: float = 1.0, top_p: float = 1.0, seed: int = 0, step: int = 0,
+                          request_base: int = 0, flags: int = 0, workspace: torch.Tensor | None = None,
+                          out: dict | None = None, stream=None) -> dict:
+    """Linear verify.  p_logits [batch][B+1][V], q_logits [batch][B][V] (bf16 or fp32, same dtype),
+    draft_tokens [batch][B] int32, all on one GPU.  Returns accept_len [batch], out_tokens
+    [batch][B+1], ratios [batch][B] (fp32), accept_mask [batch] (int64 bit pattern), status [batch].
+    Asynchronous on the current stream."""
+    if p_logits.dim() != 3 or q_logits.dim() != 3:
+        raise PsispecError("p_logits must be [batch][B+1][V] and q_logits [batch][B][V]")
+    batch, Bp1, V = p_logits.shape
+    B = Bp1 - 1
+    if tuple(q_logits.shape) != (batch, B, V) or q_logits.dtype != p_logits.dtype:
+        raise PsispecError("q_logits must be [batch][B][V] with the dtype of p_logits")
+    if tuple(draft_tokens.shape) != (batch, B) or draft_tokens.dtype != torch.int32:
+        raise PsispecError("draft_tokens must be int32 [batch][B]")
+    dt = _dtype_code(p_logits)
+    dev = p_logits.device
+    for name, t in (("p_logits", p_logits), ("q_logits", q_logits), ("draft_tokens", draft_tokens)):
+        _dev(t, name)
+        if t.device != dev:
+            raise PsispecError(f"{name} is on {t.device}, expected {dev}")
+    if out is None:
+        out = dict(accept_len=torch.empty(batch, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty(batch, B + 1, dtype=torch.int32, device=dev),
+                   ratios=torch.empty(batch, B, dtype=torch.float32, device=dev),
+                   accept_mask=torch.empty(batch, dtype=torch.int64, device=dev),
+                   status=torch.empty(batch, dtype=torch.int32, device=dev))
+    need = linear_workspace_bytes(batch, B, V, dt)
+    if need == 0:
+        raise PsispecError("unsupported sizes (B must be 1..64)")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = _sampling(temperature, top_p, seed, step, request_base, flags)
+    rc = lib().psispec_verify_linear(
+        _ptr(p_logits), _ptr(q_logits), dt, _ptr(draft_tokens), batch, B, V, ctypes.byref(s),
+        _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out.get("ratios")),
+        _ptr(out.get("accept_mask")), _ptr(out.get("status")), _ptr(workspace),
+        workspace.numel(), _stream(stream))
+    _check(rc, "psispec_verify_linear")
+    return out
+
+
+def psispec_verify_tree(p_logits: torch.Tensor, parent: torch.Tensor, node_tokens: torch.Tensor,
+                        max_depth: int, temperature: float = 1.0, top_p: float = 1.0, seed: int = 0,
+                        step: int = 0, request_base: int = 0, q_logits: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, out: dict | None = None,
+                        stream=None) -> dict:
+    """Tree verify.  p_logits [batch][N+1][V] (row 0 = root, row j+1 = node j), parent and
+    node_tokens int32 [batch][N].  Returns accept_len, accept_nodes [batch][max_depth],
+    out_tokens [batch][max_depth+1], node_ratios [batch][N], status."""
+    if p_logits.dim() != 3:
+        raise PsispecError("p_logits must be [batch][N+1][V]")
+    batch, Np1, V = p_logits.shape
+    N = Np1 - 1
+    for name, t in (("parent", parent), ("node_tokens", node_tokens)):
+        if tuple(t.shape) != (batch, N) or t.dtype != torch.int32:
+            raise PsispecError(f"{name} must be int32 [batch][N]")
+        _dev(t, name)
+    dt = _dtype_code(p_logits)
+    dev = p_logits.device
+    _dev(p_logits, "p_logits")
+    if out is None:
+        out = dict(accept_len=torch.empty(batch, dtype=torch.int32, device=dev),
+                   accept_nodes=torch.empty(batch, max_depth, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty(batch, max_depth + 1, dtype=torch.int32, device=dev),
+                   node_ratios=torch.empty(batch, N, dtype=torch.float32, device=dev),
+                   status=torch.empty(batch, dtype=torch.int32, device=dev))
+    need = tree_workspace_bytes(batch, N, V, dt)
+    if need == 0:
+        raise PsispecError("unsupported sizes (N must be 1..1024)")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = _sampling(temperature, top_p, seed, step, request_base, 0)
+    rc = lib().psispec_verify_tree(
+        _ptr(p_logits), _ptr(q_logits), dt, _ptr(parent), _ptr(node_tokens), batch, N, V,
+        int(max_depth), ctypes.byref(s), _ptr(out["accept_len"]), _ptr(out["accept_nodes"]),
+        _ptr(out["out_tokens"]), _ptr(out.get("node_ratios")), _ptr(out.get("status")),
+        _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "psispec_verify_tree")
+    return out
+
+
+def timing_enable(on: bool = True):
+    _check(lib().psispec_timing_enable(1 if on else 0), "psispec_timing_enable")
+
+
+def timing_read(max_kernels: int = 32) -> dict:
+    """{kernel name: (total device ms, launches)} since timing_enable (synchronises)."""
+    names = ctypes.create_string_buffer(64 * max_kernels)
+    ms = (ctypes.c_float * max_kernels)()
+    cnt = (ctypes.c_int32 * max_kernels)()
+    n = lib().psispec_timing_read(names, ms, cnt, max_kernels)
+    res = {}
+    for i in range(n):
+        nm = names.raw[64 * i:64 * (i + 1)].split(b"\0", 1)[0].decode()
+        res[nm] = (float(ms[i]), int(cnt[i]))
+    return res

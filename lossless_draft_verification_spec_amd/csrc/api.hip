@@ -1,0 +1,398 @@
+// api.hip -- the C ABI of libpsispec: argument checks, workspace layout, launch order, timing.
+//
+// Launch order of a verify call (all on the caller's stream, no host synchronisation):
+//   rowstats  -- one HBM pass over every p and q row: per (row, chunk) online (max, sum exp);
+//   topp      -- (top_p < 1) nucleus threshold and mass per row;
+//   decide    -- per request: ratios, accept bits, first rejection (linear) or the tree walk;
+//   draw      -- fp64 normalisers, residual sub-chunk sums, inverse-CDF select of the final token.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+namespace psispec {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int nchunk, chunk_elems;          // main pass split of a row
+  int nchunk_draw, chunk_elems_draw, nsub;
+  size_t off_part, off_rowstat, off_topp, off_desc, off_excl, off_esum, off_subsum, off_sublast;
+  size_t total;
+};
+
+// Row split of the HBM pass: chunks of about 32 KiB so that even a few hundred rows give
+// thousands of workgroups; chunk starts stay 16-byte aligned (multiples of 64 elements).
+Plan make_plan(int64_t rows, int batch, int V, size_t es, int excl_stride) {
+  Plan pl{};
+  const size_t row_bytes = (size_t)V * es;
+  int nchunk = (int)((row_bytes + 32767) / 32768);
+  if (nchunk < 1) nchunk = 1;
+  int ce = (V + nchunk - 1) / nchunk;
+  ce = (ce + 63) / 64 * 64;
+  pl.nchunk = (V + ce - 1) / ce;
+  pl.chunk_elems = ce;
+  pl.nsub = (V + kSub - 1) / kSub;
+  int nd = batch > 0 ? (2048 + batch - 1) / batch : 1;
+  if (nd > pl.nsub) nd = pl.nsub;
+  if (nd < 1) nd = 1;
+  const int sub_per = (pl.nsub + nd - 1) / nd;
+  pl.chunk_elems_draw = sub_per * kSub;
+  pl.nchunk_draw = (V + pl.chunk_elems_draw - 1) / pl.chunk_elems_draw;
+  size_t off = 0;
+  pl.off_part = off;
+  off = align_up(off + sizeof(float2) * (size_t)rows * pl.nchunk);
+  pl.off_rowstat = off;
+  off = align_up(off + sizeof(RowStat) * (size_t)rows);
+  pl.off_topp = off;
+  off = align_up(off + sizeof(ToppStat) * (size_t)rows);
+  pl.off_desc = off;
+  off = align_up(off + sizeof(DrawDesc) * (size_t)batch);
+  pl.off_excl = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)batch * (size_t)excl_stride);
+  pl.off_esum = off;
+  off = align_up(off + sizeof(double2) * (size_t)batch * pl.nchunk_draw);
+  pl.off_subsum = off;
+  off = align_up(off + sizeof(double) * (size_t)batch * pl.nsub);
+  pl.off_sublast = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)batch * pl.nsub);
+  pl.total = off + kAlign;
+  return pl;
+}
+
+size_t elem_size(psispec_dtype d) { return d == PSISPEC_BF16 ? 2 : 4; }
+
+bool sampling_ok(const psispec_sampling* s) {
+  if (!s) return false;
+  if (!(s->temperature > 0.0) || !isfinite(s->temperature)) return false;
+  if (!(s->top_p > 0.0) || !(s->top_p <= 1.0)) return false;
+  if (s->reserved != 0) return false;
+  if (s->flags & ~PSISPEC_FIRST_FROM_TARGET) return false;
+  return true;
+}
+
+template <typename P>
+P* carve(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+// ----------------------------------------------------------------------------------------------
+// kernel timing
+// ----------------------------------------------------------------------------------------------
+struct TimedLaunch {
+  std::string name;
+  hipEvent_t start, stop;
+};
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TimedLaunch> pending;
+  std::vector<hipEvent_t> pool;
+  std::vector<std::string> names;
+  std::vector<double> total_ms;
+  std::vector<int> launches;
+  std::vector<std::pair<std::string, hipEvent_t>> open;  // begun, not yet ended
+};
+
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+hipEvent_t take_event(Timing& t) {
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  hipEventCreate(&e);
+  return e;
+}
+
+void drain(Timing& t) {
+  for (auto& tl : t.pending) {
+    hipEventSynchronize(tl.stop);
+    float ms = 0.f;
+    hipEventElapsedTime(&ms, tl.start, tl.stop);
+    size_t i = 0;
+    for (; i < t.names.size(); ++i)
+      if (t.names[i] == tl.name) break;
+    if (i == t.names.size()) {
+      t.names.push_back(tl.name);
+      t.total_ms.push_back(0.0);
+      t.launches.push_back(0);
+    }
+    t.total_ms[i] += ms;
+    t.launches[i] += 1;
+    t.pool.push_back(tl.start);
+    t.pool.push_back(tl.stop);
+  }
+  t.pending.clear();
+}
+
+}  // namespace
+
+void timing_begin(const char* name, hipStream_t stream) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.on) return;
+  hipEvent_t e = take_event(t);
+  hipEventRecord(e, stream);
+  t.open.emplace_back(name, e);
+}
+
+void timing_end(const char* name, hipStream_t stream) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.on) return;
+  for (size_t i = t.open.size(); i-- > 0;) {
+    if (t.open[i].first == name) {
+      hipEvent_t e = take_event(t);
+      hipEventRecord(e, stream);
+      t.pending.push_back(TimedLaunch{name, t.open[i].second, e});
+      t.open.erase(t.open.begin() + (long)i);
+      break;
+    }
+  }
+  if (t.pending.size() > 4096) drain(t);
+}
+
+}  // namespace psispec
+
+using namespace psispec;
+
+extern "C" {
+
+const char* psispec_strerror(psispec_status code) {
+  switch (code) {
+    case PSISPEC_OK: return "ok";
+    case PSISPEC_EINVAL: return "invalid argument (pointer, size or sampling parameter)";
+    case PSISPEC_EDTYPE: return "unsupported element type";
+    case PSISPEC_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case PSISPEC_EHIP: return "HIP launch or runtime error";
+    case PSISPEC_EUNSUPPORTED: return "mode not implemented";
+  }
+  return "unknown status";
+}
+
+psispec_status psispec_timing_enable(int32_t on) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  drain(t);
+  t.on = on != 0;
+  t.names.clear();
+  t.total_ms.clear();
+  t.launches.clear();
+  t.open.clear();
+  return PSISPEC_OK;
+}
+
+int32_t psispec_timing_read(char* names, float* total_ms, int32_t* launches, int32_t max_kernels) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  drain(t);
+  int32_t n = 0;
+  for (size_t i = 0; i < t.names.size() && n < max_kernels; ++i, ++n) {
+    if (names) {
+      strncpy(names + 64 * n, t.names[i].c_str(), 63);
+      names[64 * n + 63] = '\0';
+    }
+    if (total_ms) total_ms[n] = (float)t.total_ms[i];
+    if (launches) launches[n] = t.launches[i];
+  }
+  return n;
+}
+
+size_t psispec_verify_linear_workspace(int32_t batch, int32_t B, int32_t V, psispec_dtype dtype) {
+  if (batch < 0 || B < 1 || B > 64 || V < 1) return 0;
+  if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return 0;
+  const int64_t rows = (int64_t)batch * (2 * B + 1);
+  return make_plan(rows, batch, V, elem_size(dtype), 0).total;
+}
+
+size_t psispec_verify_tree_workspace(int32_t batch, int32_t N, int32_t V, psispec_dtype dtype) {
+  if (batch < 0 || N < 1 || N > 1024 || V < 1) return 0;
+  if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return 0;
+  const int64_t rows = (int64_t)batch * (N + 1);
+  return make_plan(rows, batch, V, elem_size(dtype), N).total;
+}
+
+psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits, psispec_dtype dtype,
+                                     const int32_t* draft_tokens, int32_t batch, int32_t B,
+                                     int32_t V, const psispec_sampling* s, int32_t* accept_len,
+                                     int32_t* out_tokens, float* ratios, uint64_t* accept_mask,
+                                     int32_t* status, void* workspace, size_t workspace_bytes,
+                                     void* stream_ptr) {
+  if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return PSISPEC_EDTYPE;
+  if (batch < 0 || B < 1 || B > 64 || V < 1) return PSISPEC_EINVAL;
+  if (!sampling_ok(s)) return PSISPEC_EINVAL;
+  if (batch == 0) return PSISPEC_OK;
+  if (!p_logits || !q_logits || !draft_tokens || !accept_len || !out_tokens) return PSISPEC_EINVAL;
+  const int64_t nP = (int64_t)batch * (B + 1), nQ = (int64_t)batch * B;
+  const Plan pl = make_plan(nP + nQ, batch, V, elem_size(dtype), 0);
+  if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace % kAlign) != 0)
+    return PSISPEC_EWORKSPACE;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const double T = s->temperature;
+  const float c = (float)(1.4426950408889634074 / T);
+  const bool use_topp = s->top_p < 1.0;
+
+  RowSet rs{p_logits, q_logits, nP, nQ, V, B, (s->flags & PSISPEC_FIRST_FROM_TARGET) ? 1 : 0};
+  float2* part = carve<float2>(workspace, pl.off_part);
+  RowStat* rowstat = carve<RowStat>(workspace, pl.off_rowstat);
+  ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
+  DrawDesc* desc = carve<DrawDesc>(workspace, pl.off_desc);
+
+  if (launch_rowstats(rs, dtype, pl.nchunk, pl.chunk_elems, c, part, stream) != hipSuccess)
+    return PSISPEC_EHIP;
+  if (use_topp && launch_topp(rs, dtype, pl.nchunk, c, s->top_p, part, topp, stream) != hipSuccess)
+    return PSISPEC_EHIP;
+
+  LinearArgs la{};
+  la.rs = rs;
+  la.draft = draft_tokens;
+  la.batch = batch;
+  la.B = B;
+  la.V = V;
+  la.nchunk = pl.nchunk;
+  la.c = c;
+  la.inv_T = 1.0 / T;
+  la.use_topp = use_topp;
+  la.seed = s->seed;
+  la.step = s->step;
+  la.request_base = s->request_base;
+  la.flags = s->flags;
+  la.part = part;
+  la.topp = topp;
+  la.rowstat = rowstat;
+  la.desc = desc;
+  la.accept_len = accept_len;
+  la.out_tokens = out_tokens;
+  la.ratios = ratios;
+  la.accept_mask = accept_mask;
+  if (launch_decide_linear(la, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
+
+  DrawArgs da{};
+  da.rs = rs;
+  da.batch = batch;
+  da.V = V;
+  da.nchunk_draw = pl.nchunk_draw;
+  da.chunk_elems_draw = pl.chunk_elems_draw;
+  da.nsub = pl.nsub;
+  da.inv_T = 1.0 / T;
+  da.use_topp = use_topp;
+  da.seed = s->seed;
+  da.step = s->step;
+  da.request_base = s->request_base;
+  da.rowstat = rowstat;
+  da.topp = topp;
+  da.desc = desc;
+  da.excl = nullptr;
+  da.excl_stride = 0;
+  da.esum = carve<double2>(workspace, pl.off_esum);
+  da.subsum = carve<double>(workspace, pl.off_subsum);
+  da.sublast = carve<int32_t>(workspace, pl.off_sublast);
+  da.out_tokens = out_tokens;
+  da.status = status;
+  if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
+  return PSISPEC_OK;
+}
+
+psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, psispec_dtype dtype,
+                                   const int32_t* parent, const int32_t* node_tokens, int32_t batch,
+                                   int32_t N, int32_t V, int32_t max_depth,
+                                   const psispec_sampling* s, int32_t* accept_len,
+                                   int32_t* accept_nodes, int32_t* out_tokens, float* node_ratios,
+                                   int32_t* status, void* workspace, size_t workspace_bytes,
+                                   void* stream_ptr) {
+  if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return PSISPEC_EDTYPE;
+  if (q_logits) return PSISPEC_EUNSUPPORTED;
+  if (batch < 0 || N < 1 || N > 1024 || V < 1 || max_depth < 1 || max_depth > 64)
+    return PSISPEC_EINVAL;
+  if (!sampling_ok(s) || (s->flags & PSISPEC_FIRST_FROM_TARGET)) return PSISPEC_EINVAL;
+  if (batch == 0) return PSISPEC_OK;
+  if (!p_logits || !parent || !node_tokens || !accept_len || !accept_nodes || !out_tokens)
+    return PSISPEC_EINVAL;
+  const int64_t nP = (int64_t)batch * (N + 1);
+  const Plan pl = make_plan(nP, batch, V, elem_size(dtype), N);
+  if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace % kAlign) != 0)
+    return PSISPEC_EWORKSPACE;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const double T = s->temperature;
+  const float c = (float)(1.4426950408889634074 / T);
+  const bool use_topp = s->top_p < 1.0;
+
+  RowSet rs{p_logits, nullptr, nP, 0, V, 1, 0};
+  float2* part = carve<float2>(workspace, pl.off_part);
+  RowStat* rowstat = carve<RowStat>(workspace, pl.off_rowstat);
+  ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
+  DrawDesc* desc = carve<DrawDesc>(workspace, pl.off_desc);
+  int32_t* excl = carve<int32_t>(workspace, pl.off_excl);
+
+  if (launch_rowstats(rs, dtype, pl.nchunk, pl.chunk_elems, c, part, stream) != hipSuccess)
+    return PSISPEC_EHIP;
+  if (use_topp && launch_topp(rs, dtype, pl.nchunk, c, s->top_p, part, topp, stream) != hipSuccess)
+    return PSISPEC_EHIP;
+
+  TreeArgs ta{};
+  ta.rs = rs;
+  ta.parent = parent;
+  ta.node_tokens = node_tokens;
+  ta.batch = batch;
+  ta.N = N;
+  ta.V = V;
+  ta.max_depth = max_depth;
+  ta.nchunk = pl.nchunk;
+  ta.c = c;
+  ta.inv_T = 1.0 / T;
+  ta.use_topp = use_topp;
+  ta.seed = s->seed;
+  ta.step = s->step;
+  ta.request_base = s->request_base;
+  ta.part = part;
+  ta.topp = topp;
+  ta.rowstat = rowstat;
+  ta.desc = desc;
+  ta.excl = excl;
+  ta.accept_len = accept_len;
+  ta.accept_nodes = accept_nodes;
+  ta.out_tokens = out_tokens;
+  ta.node_ratios = node_ratios;
+  if (launch_decide_tree(ta, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
+
+  DrawArgs da{};
+  da.rs = rs;
+  da.batch = batch;
+  da.V = V;
+  da.nchunk_draw = pl.nchunk_draw;
+  da.chunk_elems_draw = pl.chunk_elems_draw;
+  da.nsub = pl.nsub;
+  da.inv_T = 1.0 / T;
+  da.use_topp = use_topp;
+  da.seed = s->seed;
+  da.step = s->step;
+  da.request_base = s->request_base;
+  da.rowstat = rowstat;
+  da.topp = topp;
+  da.desc = desc;
+  da.excl = excl;
+  da.excl_stride = N;
+  da.esum = carve<double2>(workspace, pl.off_esum);
+  da.subsum = carve<double>(workspace, pl.off_subsum);
+  da.sublast = carve<int32_t>(workspace, pl.off_sublast);
+  da.out_tokens = out_tokens;
+  da.status = status;
+  if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
+  return PSISPEC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// internal.h -- types and device helpers shared by the HIP kernels of libpsispec (gfx950 only).
+//
+// Citations use page titles and sections:
+//   [alphalab] "Uno Ψ-Spec 是什麼？Diffusion-Augmented LLM 如何保留 AR 分布、一次驗證多個 Token"
+//   [lanes]    "Uno / Ψ-Spec — 같은 모델 안에서 초안 뽑고 AR로 도장 찍기"
+//   [philox]   Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "psispec.h"
+
+namespace psispec {
+
+constexpr int kThreads = 256;       // workgroup size of the streaming kernels (4 wave64)
+constexpr int kSub = 1024;          // tokens per sub-chunk of the fp64 residual prefix sums
+constexpr float kNegBig = -3.40282346638528859812e+38f;  // running-max floor (finite: -inf - floor = -inf)
+
+enum : uint32_t { kPurposeAccept = 0, kPurposeDraw = 1 };
+
+// Rows of one call: rows [0, nP) live in p, rows [nP, nP + nQ) in q, each V contiguous elements.
+struct RowSet {
+  const void* p;
+  const void* q;
+  int64_t nP;
+  int64_t nQ;
+  int V;
+  int qB;        // q rows per request (linear: B), used to skip position-0 q rows
+  int skip_q0;   // 1: q rows at position 0 are not read (first-from-target layout)
+};
+
+// Per-row softmax statistics of the raw logits: lmax = max logit, Z = sum exp((l - lmax) / T).
+struct RowStat {
+  float lmax;
+  int32_t st;
+  double Z;
+};
+
+// Per-row nucleus: tokens with logit >= thr are kept; M = their mass under softmax(l / T).
+struct ToppStat {
+  float thr;
+  int32_t pad;
+  double M;
+};
+
+// What the final draw of a request needs: the stopping row of p (and of q, or -1), the Philox
+// position of the draw, and the tokens removed from the residual (tree: rejected children).
+struct DrawDesc {
+  int32_t prow;
+  int32_t qrow;
+  int32_t pos;      // Philox counter word 1 for the draw
+  int32_t st;       // status bits found before the draw
+  int32_t nexcl;    // number of excluded tokens
+  int32_t out_idx;  // where the drawn token goes in out_tokens (flat index), -1 = nowhere
+};
+
+// ---------------------------------------------------------------------------------------------
+// Philox4x32-10 [philox]: ten rounds; each multiplies counter words 0 and 2 by the two published
+// multipliers, swaps, and xors the high halves with words 1/3 and the round key; the key advances
+// by the two published Weyl increments between rounds.
+// ---------------------------------------------------------------------------------------------
+__device__ inline uint4 philox4x32_10(uint4 ctr, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t a = ctr.x, c = ctr.z;
+    const uint32_t hi_a = __umulhi(0xD2511F53u, a), lo_a = 0xD2511F53u * a;
+    const uint32_t hi_c = __umulhi(0xCD9E8D57u, c), lo_c = 0xCD9E8D57u * c;
+    ctr = make_uint4(hi_c ^ ctr.y ^ k0, lo_c, hi_a ^ ctr.w ^ k1, lo_a);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return ctr;
+}
+
+// u in [0, 1): the 53 high bits of (word0 << 32 | word1) scaled by 2^-53 (exact in fp64).
+__device__ inline double philox_uniform(uint64_t seed, uint32_t request, uint32_t position,
+                                        uint32_t purpose, uint32_t step) {
+  const uint4 x = philox4x32_10(make_uint4(request, position, purpose, step),
+                                (uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32));
+  const uint64_t bits = ((uint64_t)x.x << 32) | (uint64_t)x.y;
+  return (double)(bits >> 11) * 0x1.0p-53;
+}
+
+// ---------------------------------------------------------------------------------------------
+// element access
+// ---------------------------------------------------------------------------------------------
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.bits << 16); }
+
+template <typename T>
+__device__ inline const T* row_ptr(const RowSet& rs, int64_t row) {
+  if (row < rs.nP) return static_cast<const T*>(rs.p) + row * (int64_t)rs.V;
+  return static_cast<const T*>(rs.q) + (row - rs.nP) * (int64_t)rs.V;
+}
+
+__device__ inline bool row_skipped(const RowSet& rs, int64_t row) {
+  return rs.skip_q0 && row >= rs.nP && ((row - rs.nP) % rs.qB) == 0;
+}
+
+// order-preserving integer key of a logit (larger logit <-> larger key)
+__device__ inline uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline uint32_t order_key16(uint16_t b) {
+  return (b & 0x8000u) ? (uint32_t)(~b & 0xffffu) : (uint32_t)(b | 0x8000u);
+}
+__device__ inline float key_to_float(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+__device__ inline float key16_to_float(uint32_t k) {
+  const uint32_t b = (k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu);
+  return __uint_as_float(b << 16);
+}
+
+// online softmax accumulation: (m, s) with s = sum exp2((x - m) * c)
+__device__ inline void os_combine(float& m, float& s, float m2, float s2, float c) {
+  const float mn = fmaxf(m, m2);
+  s = s * exp2f((m - mn) * c) + s2 * exp2f((m2 - mn) * c);
+  m = mn;
+}
+
+template <typename F>
+__device__ inline void wave_allreduce(F& v, F (*op)(F, F)) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = op(v, __shfl_xor(v, off, 64));
+}
+
+}  // namespace psispec

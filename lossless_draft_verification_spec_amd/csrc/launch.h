@@ -1,0 +1,87 @@
+// launch.h -- host-side launchers of the kernels (one per .hip translation unit).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace psispec {
+
+// Kernel timing hooks (api.cpp): bracket a launch with events when timing is enabled.
+void timing_begin(const char* name, hipStream_t stream);
+void timing_end(const char* name, hipStream_t stream);
+
+// rows.hip
+hipError_t launch_rowstats(const RowSet& rs, psispec_dtype dtype, int nchunk, int chunk_elems,
+                           float c, float2* part, hipStream_t stream);
+hipError_t launch_topp(const RowSet& rs, psispec_dtype dtype, int nchunk, float c, double top_p,
+                       const float2* part, ToppStat* topp, hipStream_t stream);
+
+// linear.hip
+struct LinearArgs {
+  RowSet rs;
+  const int32_t* draft;
+  int batch, B, V, nchunk;
+  float c;            // log2(e) / T in fp32 (main-pass exponent scale)
+  double inv_T;       // 1 / T in fp64
+  int use_topp;
+  uint64_t seed;
+  uint32_t step, request_base, flags;
+  const float2* part;
+  const ToppStat* topp;
+  RowStat* rowstat;
+  DrawDesc* desc;
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  float* ratios;
+  uint64_t* accept_mask;
+};
+hipError_t launch_decide_linear(const LinearArgs& a, psispec_dtype dtype, hipStream_t stream);
+
+// tree.hip
+struct TreeArgs {
+  RowSet rs;
+  const int32_t* parent;
+  const int32_t* node_tokens;
+  int batch, N, V, max_depth, nchunk;
+  float c;
+  double inv_T;
+  int use_topp;
+  uint64_t seed;
+  uint32_t step, request_base;
+  const float2* part;
+  const ToppStat* topp;
+  RowStat* rowstat;
+  DrawDesc* desc;
+  int32_t* excl;      // [batch][N] excluded tokens of the stopping node
+  int32_t* accept_len;
+  int32_t* accept_nodes;
+  int32_t* out_tokens;
+  float* node_ratios;
+};
+hipError_t launch_decide_tree(const TreeArgs& a, psispec_dtype dtype, hipStream_t stream);
+
+// resample.hip -- the fp64 final draw shared by both entry points
+struct DrawArgs {
+  RowSet rs;
+  int batch, V, nchunk_draw, chunk_elems_draw, nsub;
+  double inv_T;
+  int use_topp;
+  uint64_t seed;
+  uint32_t step, request_base;
+  const RowStat* rowstat;
+  const ToppStat* topp;
+  const DrawDesc* desc;
+  const int32_t* excl;
+  int excl_stride;
+  double2* esum;      // [batch][nchunk_draw] partial normalisers (p, q)
+  double* subsum;     // [batch][nsub] residual mass per sub-chunk
+  int32_t* sublast;   // [batch][nsub] last token with positive residual weight per sub-chunk
+  int32_t* out_tokens;
+  int32_t* status;
+};
+hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t stream);
+
+}  // namespace psispec

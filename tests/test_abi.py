@@ -1,0 +1,69 @@
+"""The C-ABI library loads and exports every function that include/*.h declares (no GPU needed:
+nothing is called but the host-only argument checks and the workspace queries)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        for m in re.finditer(r"\b(psispec_[a-z0-9_]+)\s*\(", text):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def libpsispec():
+    import lossless_draft_verification_spec_amd as pkg
+    return pkg.lib()
+
+
+def test_every_declared_symbol_is_exported(libpsispec):
+    names = _declared()
+    assert {"psispec_verify_linear", "psispec_verify_tree", "psispec_strerror"} <= names
+    for n in sorted(names):
+        assert hasattr(libpsispec, n), n
+
+
+def test_workspace_queries_and_host_checks(libpsispec):
+    import lossless_draft_verification_spec_amd as pkg
+    assert pkg.linear_workspace_bytes(64, 8, 151936, pkg.PSISPEC_BF16) > 0
+    assert pkg.linear_workspace_bytes(64, 65, 151936, pkg.PSISPEC_BF16) == 0  # B > 64
+    assert pkg.linear_workspace_bytes(64, 8, 151936, 7) == 0                  # bad dtype
+    assert pkg.tree_workspace_bytes(8, 32, 151936, pkg.PSISPEC_F32) > 0
+    assert pkg.tree_workspace_bytes(8, 2000, 151936, pkg.PSISPEC_F32) == 0
+    # argument errors are caught on the host before anything is launched
+    L = libpsispec
+    s = pkg.psispec_sampling(0.0, 1.0, 0, 0, 0, 0, 0)  # temperature 0
+    rc = L.psispec_verify_linear(None, None, 1, None, 1, 4, 10, ctypes.byref(s), None, None, None,
+                                 None, None, None, 0, None)
+    assert rc == -1
+    s = pkg.psispec_sampling(1.0, 1.5, 0, 0, 0, 0, 0)  # top_p > 1
+    rc = L.psispec_verify_linear(None, None, 1, None, 1, 4, 10, ctypes.byref(s), None, None, None,
+                                 None, None, None, 0, None)
+    assert rc == -1
+    s = pkg.psispec_sampling(1.0, 1.0, 0, 0, 0, 0, 0)
+    rc = L.psispec_verify_linear(None, None, 5, None, 1, 4, 10, ctypes.byref(s), None, None, None,
+                                 None, None, None, 0, None)
+    assert rc == -2  # dtype
+    rc = L.psispec_verify_linear(ctypes.c_void_p(16), ctypes.c_void_p(16), 1, ctypes.c_void_p(16),
+                                 1, 4, 10, ctypes.byref(s), ctypes.c_void_p(16),
+                                 ctypes.c_void_p(16), None, None, None, None, 0, None)
+    assert rc == -3  # no workspace
+    rc = L.psispec_verify_tree(ctypes.c_void_p(16), ctypes.c_void_p(16), 0, None, None, 1, 4, 10, 4,
+                               ctypes.byref(s), None, None, None, None, None, None, 0, None)
+    assert rc == -5  # sampled-candidate trees not implemented
+    assert L.psispec_strerror(-3).decode().startswith("workspace")
+    # batch 0 is a no-op that succeeds without touching anything
+    rc = L.psispec_verify_linear(None, None, 1, None, 0, 4, 10, ctypes.byref(s), None, None, None,
+                                 None, None, None, 0, None)
+    assert rc == 0

@@ -1,0 +1,280 @@
+"""Parity of the HIP library (through its C ABI) with the CPU oracle on seeded inputs.
+
+Small and ragged shapes are compared on every request; the full-size workloads (batch 64 x B=8,
+batch 256 x B=8 and batch 256 x B=16 with top-p at V = 151,936, and the 32-node trees) run on the
+GPU at full size and are compared on sampled requests, which the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lossless_draft_verification_spec_amd import PSISPEC_FIRST_FROM_TARGET
+from lossless_draft_verification_spec_amd import psispec_verify_linear, psispec_verify_tree
+from lossless_draft_verification_spec_amd import workloads
+from parity import (Tally, compare_linear, compare_tree, gpu_linear_numpy, host_logits,
+                    oracle_linear_requests, oracle_tree_requests)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _rand_linear(batch, B, V, dtype, seed, sigma=1.0, scale=3.0):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    p = torch.randn(batch, B + 1, V, generator=g) * scale
+    q = p[:, :B] + sigma * torch.randn(batch, B, V, generator=g)
+    p, q = p.to(dtype), q.to(dtype)
+    d = workloads.sample_drafts(q, 1.0, 1.0, g)
+    return p.to(DEV), q.to(DEV), d.to(DEV)
+
+
+def _run_and_compare(p, q, d, T=1.0, top_p=1.0, seed=123, steps=(0,), flags=0, rows=None,
+                     request_base=0, tally=None):
+    tally = tally or Tally()
+    ph, qh, dh = host_logits(p), host_logits(q), d.cpu().numpy()
+    rows = list(range(p.shape[0])) if rows is None else rows
+    Th, tph = float(T), float(top_p)
+    for step in steps:
+        out = psispec_verify_linear(p, q, d, temperature=T, top_p=top_p, seed=seed, step=step,
+                                    flags=flags, request_base=request_base)
+        g = gpu_linear_numpy(out)
+        o = oracle_linear_requests(ph, qh, dh, rows, Th, tph, seed, step, flags, request_base)
+        compare_linear(tally, g, o, rows, p.shape[1] - 1, tph)
+    return tally
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("batch,B,V", [(1, 4, 32), (5, 3, 1000), (7, 8, 40013), (3, 1, 7),
+                                       (2, 64, 300), (4, 16, 4096)])
+def test_linear_small_and_ragged(dtype, batch, B, V):
+    p, q, d = _rand_linear(batch, B, V, dtype, seed=batch * 1000 + B * 10 + V % 97)
+    t = _run_and_compare(p, q, d, steps=range(6))
+    print(t)
+    t.check()
+
+
+@pytest.mark.parametrize("T,top_p", [(0.7, 1.0), (1.3, 1.0), (1.0, 0.9), (0.7, 0.95), (1.0, 0.5)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_linear_temperature_and_top_p(T, top_p, dtype):
+    batch, B, V = 6, 5, 5003
+    p, q, _ = _rand_linear(batch, B, V, dtype, seed=77)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    d = workloads.sample_drafts(q.cpu(), T, top_p, g).to(DEV)
+    t = _run_and_compare(p, q, d, T=T, top_p=top_p, steps=range(5))
+    print(t)
+    t.check()
+
+
+def test_linear_first_from_target_layout():
+    batch, B, V = 8, 6, 2048
+    p, q, d = _rand_linear(batch, B, V, torch.bfloat16, seed=3)
+    q[:, 0] = p[:, 0]
+    t = _run_and_compare(p, q, d, steps=range(8), flags=PSISPEC_FIRST_FROM_TARGET)
+    t.check()
+    out = psispec_verify_linear(p, q, d, seed=1, flags=PSISPEC_FIRST_FROM_TARGET)
+    acc = out["accept_len"].cpu().numpy()
+    assert (acc >= 1).all() and (acc <= B).all()  # 1 <= TPF = (k+1)/2 <= (B+1)/2
+
+
+def test_linear_request_base_and_steps():
+    p, q, d = _rand_linear(4, 4, 777, torch.float32, seed=4)
+    t = _run_and_compare(p, q, d, steps=(0, 5, 2**32 - 1), request_base=1000, seed=2**64 - 1)
+    t.check()
+
+
+def test_linear_full_accept_and_walkthrough_structure():
+    # p == q: every draft kept, the extra token comes from the block-end row
+    batch, B, V = 16, 4, 3001
+    p, _, _ = _rand_linear(batch, B, V, torch.float32, seed=8)
+    q = p[:, :B].contiguous()
+    g = torch.Generator(device="cpu").manual_seed(1)
+    d = workloads.sample_drafts(q.cpu(), 1.0, 1.0, g).to(DEV)
+    out = psispec_verify_linear(p, q, d, seed=3)
+    assert (out["accept_len"] == B).all()
+    t = _run_and_compare(p, q, d, seed=3)
+    t.check()
+    # the third draft has zero target probability: kept T1, T2, then a correction, rest discarded
+    q2 = p[:, :B].clone()
+    p2 = p.clone()
+    p2[torch.arange(batch), 2, d[:, 2].long()] = float("-inf")
+    out = psispec_verify_linear(p2, q2.contiguous(), d, seed=3)
+    assert (out["accept_len"] == 2).all()
+    tok = out["out_tokens"].cpu()
+    assert (tok[:, :2] == d[:, :2].cpu()).all() and (tok[:, 2] != d[:, 2].cpu()).all()
+    assert (tok[:, 3:] == -1).all()
+    t = _run_and_compare(p2, q2.contiguous(), d, seed=3)
+    t.check()
+
+
+def test_linear_status_bits():
+    batch, B, V = 6, 3, 500
+    p, q, d = _rand_linear(batch, B, V, torch.float32, seed=9)
+    d[1, 2] = V + 5       # bad token
+    d[2, 0] = -1
+    p[3, 1, 7] = float("nan")
+    q[4, 2, 9] = float("inf")
+    p[5, 3, :] = float("-inf")  # no finite logit in the block-end row
+    t = _run_and_compare(p, q, d, seed=4)
+    assert t.status_requests == 5
+    t.check()
+
+
+def test_linear_empty_batch():
+    p = torch.zeros(0, 5, 64, device=DEV)
+    q = torch.zeros(0, 4, 64, device=DEV)
+    d = torch.zeros(0, 4, dtype=torch.int32, device=DEV)
+    out = psispec_verify_linear(p, q, d)
+    assert out["accept_len"].numel() == 0
+
+
+def test_linear_deterministic_and_workspace_independent():
+    p, q, d = _rand_linear(9, 8, 20000, torch.bfloat16, seed=10)
+    a = psispec_verify_linear(p, q, d, seed=11, step=3)
+    ws = torch.full((64 << 20,), 0xAB, dtype=torch.uint8, device=DEV)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = psispec_verify_linear(p, q, d, seed=11, step=3, workspace=ws)
+    s.synchronize()
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k].cpu(), b[k].cpu()), k
+
+
+def test_c1_histogram_on_gpu():
+    """10,000 steps of the small fp32 workload on the GPU: committed-token frequencies against the
+    target rows and parity with the oracle on every step."""
+    from refdist import committed_histogram_check
+    inp = workloads.make_linear("c1", device="cpu", steps=10000)
+    p, q = inp.p.to(DEV), inp.q.to(DEV)
+    n = len(inp.drafts)
+    acc = np.zeros(n, np.int32)
+    toks = np.zeros((n, inp.preset.B + 1), np.int32)
+    tally = Tally()
+    ph, qh = host_logits(p), host_logits(q)
+    for s, dd in enumerate(inp.drafts):
+        out = psispec_verify_linear(p, q, dd.to(DEV), seed=inp.seed, step=s)
+        g = gpu_linear_numpy(out)
+        acc[s], toks[s] = g["accept_len"][0], g["out_tokens"][0]
+        if s % 10 == 0:
+            o = oracle.verify_linear(ph, qh, dd.numpy(), seed=inp.seed, step=s)
+            compare_linear(tally, g, o, [0], inp.preset.B, 1.0)
+    tally.check()
+    pvals, mean, want, se = committed_histogram_check(inp.p.numpy()[0], inp.q.numpy()[0], acc, toks)
+    assert min(pvals) > 1e-4, pvals
+    assert abs(mean - want) < 5 * se
+
+
+@pytest.mark.parametrize("name,nreq", [("c2", 64), ("ns", 24), ("c3", 12)])
+def test_full_size_linear(name, nreq):
+    inp = workloads.make_linear(name, device=DEV, steps=2)
+    pr = inp.preset
+    ph, qh = host_logits(inp.p), host_logits(inp.q)
+    rows = list(range(0, pr.batch, max(1, pr.batch // nreq)))[:nreq]
+    tally = Tally()
+    for step, d in enumerate(inp.drafts):
+        out = psispec_verify_linear(inp.p, inp.q, d, temperature=pr.T, top_p=pr.top_p,
+                                    seed=inp.seed, step=step)
+        g = gpu_linear_numpy(out)
+        o = oracle_linear_requests(ph, qh, d.cpu().numpy(), rows, pr.T, pr.top_p, inp.seed, step)
+        compare_linear(tally, g, o, rows, pr.B, pr.top_p)
+        assert (g["status"] == 0).all()
+    print(name, tally)
+    tally.check()
+
+
+def test_v262144_bf16():
+    p, q, d = _rand_linear(3, 4, 262144, torch.bfloat16, seed=12)
+    t = _run_and_compare(p, q, d, steps=range(2))
+    t.check()
+
+
+# ------------------------------------------------------------------------------------------------
+# tree
+# ------------------------------------------------------------------------------------------------
+def _rand_tree(batch, N, V, dtype, seed, k=3, depth=4, dup=False):
+    rng = np.random.default_rng(seed)
+    parent = np.full((batch, N), -1, np.int32)
+    tokens = np.zeros((batch, N), np.int32)
+    for r in range(batch):
+        kids = {-1: 0}
+        dep = {-1: 0}
+        for j in range(N):
+            cands = [v for v in range(-1, j) if kids.get(v, 0) < k and dep[v] < depth]
+            v = int(rng.choice(cands))
+            parent[r, j] = v
+            kids[v] = kids.get(v, 0) + 1
+            kids[j] = 0
+            dep[j] = dep[v] + 1
+            tokens[r, j] = rng.integers(0, V)
+            if dup and j > 0 and parent[r, j - 1] == v and rng.random() < 0.3:
+                tokens[r, j] = tokens[r, j - 1]
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    p = (torch.randn(batch, N + 1, V, generator=g) * 2.0)
+    # make the node tokens likely so walks go deep
+    for r in range(batch):
+        for j in range(N):
+            p[r, parent[r, j] + 1, tokens[r, j]] += 3.0
+    p = p.to(dtype)
+    return p.to(DEV), parent, tokens
+
+
+def _tree_compare(p, parent, tokens, max_depth, T=1.0, top_p=1.0, seed=5, steps=(0,), rows=None):
+    tally = Tally()
+    ph = host_logits(p)
+    rows = list(range(p.shape[0])) if rows is None else rows
+    par_d = torch.from_numpy(parent).to(DEV)
+    tok_d = torch.from_numpy(tokens).to(DEV)
+    for step in steps:
+        out = psispec_verify_tree(p, par_d, tok_d, max_depth, temperature=T, top_p=top_p, seed=seed,
+                                  step=step)
+        torch.cuda.synchronize()
+        g = {k: v.cpu().numpy() for k, v in out.items()}
+        o = oracle_tree_requests(ph, parent, tokens, rows, max_depth, float(T), float(top_p), seed,
+                                 step)
+        compare_tree(tally, g, o, rows, float(top_p))
+    return tally
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("batch,N,V", [(4, 10, 64), (3, 32, 5003), (2, 1, 100), (5, 60, 999)])
+def test_tree_small(dtype, batch, N, V):
+    p, parent, tokens = _rand_tree(batch, N, V, dtype, seed=N + V, dup=True)
+    t = _tree_compare(p, parent, tokens, 8, steps=range(6))
+    print(t)
+    t.check()
+
+
+@pytest.mark.parametrize("T,top_p", [(0.7, 1.0), (1.0, 0.9)])
+def test_tree_temperature_top_p(T, top_p):
+    p, parent, tokens = _rand_tree(4, 20, 3000, torch.float32, seed=21)
+    t = _tree_compare(p, parent, tokens, 8, T=T, top_p=top_p, steps=range(4))
+    t.check()
+
+
+def test_tree_bad_parent_status():
+    p, parent, tokens = _rand_tree(3, 6, 50, torch.float32, seed=22)
+    parent[1, 3] = 5  # parent after child
+    t = _tree_compare(p, parent, tokens, 8)
+    assert t.status_requests >= 1
+    t.check()
+
+
+def test_chain_tree_equals_linear_one_hot():
+    batch, B, V = 4, 5, 777
+    p, _, d = _rand_linear(batch, B, V, torch.float32, seed=23)
+    q = torch.full((batch, B, V), float("-inf"), device=DEV)
+    q.scatter_(2, d.long().unsqueeze(-1), 0.0)
+    parent = torch.arange(-1, B - 1, dtype=torch.int32, device=DEV).repeat(batch, 1).contiguous()
+    lin = psispec_verify_linear(p, q, d, seed=9)
+    tr = psispec_verify_tree(p, parent, d, B, seed=9)
+    assert torch.equal(lin["ratios"], tr["node_ratios"])
+
+
+@pytest.mark.parametrize("name", ["c4", "c4b"])
+def test_full_size_tree(name):
+    inp = workloads.make_tree(name, device=DEV)
+    pr = inp.preset
+    t = _tree_compare(inp.p, inp.parent.cpu().numpy(), inp.node_tokens.cpu().numpy(), pr.depth,
+                      T=pr.T, top_p=pr.top_p, seed=inp.seed, steps=range(3))
+    print(name, t)
+    t.check()
