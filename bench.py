@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the Psi-Spec linear verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one psispec_verify_linear call over one batch of synthetic logits: the HBM pass over
+every p and q row, the nucleus pass when top-p is on, the accept test and first-rejection scan, and
+the fp64 final draw.  The timed workload is the batch-64, B=8, V=151,936 bf16 block (Zipf-boosted
+N(0, 3^2) target logits, draft noise sigma in {0.3, 1, 2} per request, T = 1); rotation sets that
+together exceed the 256 MB last-level cache are cycled so every step reads its rows from HBM, and
+each step has its own drafted tokens and Philox step.  Inputs are resident in HBM before timing.
+
+One JSON line is printed: verified rows/s (batch*B per step) as `value`, committed tokens/s, the
+roofline of the dominant kernel (the HBM pass, timed with HIP events on the library's stream), the
+oracle timed on the host cores as `cpu_baseline`, and the batch-256 B=8 shape as `target_shape`.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, datasheet
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2", choices=["c2", "ns", "c3"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-target", action="store_true", help="skip the batch-256 target shape")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for counter scaling)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def run_workload(name, steps, warmup, torch, pkg, workloads):
+    """Time `steps` verify calls; returns a dict of measurements."""
+    preset = workloads.PRESETS[name]
+    R = preset.rotations
+    per_rot = (steps + warmup + R - 1) // R + 1
+    t0 = time.time()
+    sets = [workloads.make_linear(preset, device="cuda", rotation=i, steps=per_rot) for i in range(R)]
+    torch.cuda.synchronize()
+    log(f"{name}: generated {R} rotation sets in {time.time() - t0:.1f}s")
+    b, B, V = preset.batch, preset.B, preset.V
+    dev = sets[0].p.device
+    ws = torch.empty(pkg.linear_workspace_bytes(b, B, V, pkg.PSISPEC_BF16), dtype=torch.uint8,
+                     device=dev)
+    n_total = steps + warmup
+    acc_all = torch.zeros(n_total, b, dtype=torch.int32, device=dev)
+    outs = [dict(accept_len=acc_all[s],
+                 out_tokens=torch.empty(b, B + 1, dtype=torch.int32, device=dev),
+                 ratios=torch.empty(b, B, dtype=torch.float32, device=dev),
+                 accept_mask=torch.empty(b, dtype=torch.int64, device=dev),
+                 status=torch.empty(b, dtype=torch.int32, device=dev)) for s in range(min(n_total, 8))]
+
+    def step(s, out):
+        inp = sets[s % R]
+        d = inp.drafts[s // R]
+        o = dict(outs[s % len(outs)])
+        o["accept_len"] = acc_all[s]
+        pkg.psispec_verify_linear(inp.p, inp.q, d, temperature=preset.T, top_p=preset.top_p,
+                                  seed=inp.seed, step=s, workspace=ws, out=o)
+
+    for s in range(warmup):
+        step(s, None)
+    torch.cuda.synchronize()
+    # phase A: the timed region
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for s in range(warmup, warmup + steps):
+        step(s, None)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1)
+    committed = int((acc_all[warmup:warmup + steps].to(torch.int64) + 1).sum().item())
+    # phase B: same steps again with HIP events around every library kernel
+    pkg.timing_enable(True)
+    for s in range(warmup, warmup + steps):
+        step(s, None)
+    kern = pkg.timing_read()
+    pkg.timing_enable(False)
+    torch.cuda.synchronize()
+    elem = 2 if preset.dtype == torch.bfloat16 else 4
+    alg = workloads.algorithmic_bytes_linear(b, B, V, elem)
+    row_bytes = b * (2 * B + 1) * V * elem
+    res = dict(name=name, preset=preset, ms_total=ms, wall_s=wall, steps=steps,
+               ms_per_step=ms / steps, rows_per_s=steps * b * B / (ms / 1e3),
+               committed_per_s=committed / (ms / 1e3), alg_bytes=alg, row_bytes=row_bytes,
+               kernels={k: dict(avg_us=1e3 * v[0] / max(1, v[1]), launches=v[1])
+                        for k, v in kern.items()},
+               mean_committed=committed / (steps * b))
+    res["hbm_gbs_step"] = alg / (res["ms_per_step"] / 1e3) / 1e9
+    rs = res["kernels"].get("rowstats")
+    if rs:
+        res["rowstats_gbs"] = row_bytes / (rs["avg_us"] / 1e6) / 1e9
+    host = dict(p=sets[0].p, q=sets[0].q, d=sets[0].drafts[0], seed=sets[0].seed)
+    del sets
+    torch.cuda.empty_cache()
+    return res, host
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernel
+    source; else None."""
+    import hashlib
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc", "rows.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if kv.get("rows_hip_sha256_16") != sha:
+        return None
+    try:
+        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(host, preset, seconds):
+    """The oracle as it stands, single-threaded on this host, on the first requests of rotation
+    set 0 (step 0), for about `seconds` of work."""
+    import numpy as np
+    import oracle
+    import torch
+
+    p = host["p"].detach().cpu()
+    q = host["q"].detach().cpu()
+    if p.dtype == torch.bfloat16:
+        ph = p.view(torch.int16).numpy().view(np.uint16)
+        qh = q.view(torch.int16).numpy().view(np.uint16)
+    else:
+        ph, qh = p.numpy(), q.numpy()
+    d = host["d"].cpu().numpy()
+    B = preset.B
+    done = 0
+    t0 = time.perf_counter()
+    while done < preset.batch and time.perf_counter() - t0 < seconds:
+        oracle.verify_linear(ph[done:done + 1], qh[done:done + 1], d[done:done + 1], T=preset.T,
+                             top_p=preset.top_p, seed=host["seed"], step=0, request_base=done)
+        done += 1
+    el = time.perf_counter() - t0
+    return dict(value=done * B / el, unit="rows/s", cores=1, kind="oracle",
+                sample=f"{done} of {preset.batch} requests (x {B} verified rows) of rotation set 0, "
+                       f"step 0, one thread, {el:.1f} s")
+
+
+def copy_calibration(torch):
+    n = 512 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requests would shard by request_base with no exchange).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import lossless_draft_verification_spec_amd as pkg
+    from lossless_draft_verification_spec_amd import workloads
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    pkg.lib()
+    res, host = run_workload(args.workload, args.steps, args.warmup, torch, pkg, workloads)
+    pr = res["preset"]
+    log(f"{args.workload}: {res['ms_per_step'] * 1e3:.1f} us/step, kernels {res['kernels']}")
+    target = None
+    if not args.no_target and args.workload != "ns":
+        tres, _ = run_workload("ns", args.steps, args.warmup, torch, pkg, workloads)
+        rs = tres["kernels"].get("rowstats", {})
+        target = dict(workload="ns: linear verify batch=256 B=8 V=151936 bf16, generated as c2",
+                      rows_per_s=round(tres["rows_per_s"], 1),
+                      committed_tokens_per_s=round(tres["committed_per_s"], 1),
+                      ms_per_step=round(tres["ms_per_step"], 4),
+                      hbm_gbs_step=round(tres["hbm_gbs_step"], 1),
+                      rowstats_avg_us=round(rs.get("avg_us", 0.0), 2),
+                      rowstats_gbs=round(tres.get("rowstats_gbs", 0.0), 1),
+                      rowstats_frac_of_peak=round(tres.get("rowstats_gbs", 0.0) / HBM_PEAK_GBS, 4),
+                      kernels_avg_us={k: round(v["avg_us"], 2) for k, v in tres["kernels"].items()})
+        log(f"ns: {tres['ms_per_step'] * 1e3:.1f} us/step, kernels {tres['kernels']}")
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(host, pr, args.cpu_seconds)
+    rs = res["kernels"]["rowstats"]
+    achieved = res["row_bytes"] / (rs["avg_us"] / 1e6) / 1e9
+    traffic = read_traffic("rowstats", args.workload)
+    line = {
+        "metric": "verified rows/s + committed tokens/s, HBM GB/s as % of peak (B=8, V=151936)",
+        "value": round(res["rows_per_s"], 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: linear verify batch={pr.batch} B={pr.B} "
+                               f"V={pr.V} bf16 logits, T={pr.T}, top_p={pr.top_p}",
+                   "batch": pr.batch, "B": pr.B, "V": pr.V, "input_dtype": "bf16",
+                   "parallelism": "single GPU", "rotation_sets": pr.rotations},
+        "committed_tokens_per_s": round(res["committed_per_s"], 1),
+        "mean_committed_per_request": round(res["mean_committed"], 4),
+        "hbm_gbs_step": round(res["hbm_gbs_step"], 1),
+        "hbm_frac_step": round(res["hbm_gbs_step"] / HBM_PEAK_GBS, 4),
+        "kernels_avg_us": {k: round(v["avg_us"], 2) for k, v in res["kernels"].items()},
+        "roofline": {"bound": "hbm", "kernel": "k_rowstats", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": res["row_bytes"],
+                     "avg_launch_us": round(rs["avg_us"], 2)},
+        "cpu_baseline": cpu,
+        "target_shape": target,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

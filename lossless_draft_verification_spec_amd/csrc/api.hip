@@ -24,7 +24,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Plan {
   int nchunk, chunk_elems;          // main pass split of a row
   int nchunk_draw, chunk_elems_draw, nsub;
-  size_t off_part, off_rowstat, off_topp, off_desc, off_excl, off_esum, off_subsum, off_sublast;
+  size_t off_part, off_rowstat, off_topp, off_desc, off_excl, off_esum, off_suba, off_subn,
+      off_subsum, off_suboff, off_upool, off_ucount;
   size_t total;
 };
 
@@ -59,10 +60,18 @@ Plan make_plan(int64_t rows, int batch, int V, size_t es, int excl_stride) {
   off = align_up(off + sizeof(int32_t) * (size_t)batch * (size_t)excl_stride);
   pl.off_esum = off;
   off = align_up(off + sizeof(double2) * (size_t)batch * pl.nchunk_draw);
+  pl.off_suba = off;
+  off = align_up(off + sizeof(double2) * (size_t)batch * pl.nsub);
+  pl.off_subn = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)batch * pl.nsub);
   pl.off_subsum = off;
   off = align_up(off + sizeof(double) * (size_t)batch * pl.nsub);
-  pl.off_sublast = off;
+  pl.off_suboff = off;
   off = align_up(off + sizeof(int32_t) * (size_t)batch * pl.nsub);
+  pl.off_upool = off;
+  off = align_up(off + sizeof(double2) * (size_t)batch * kUncPool);
+  pl.off_ucount = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)batch);
   pl.total = off + kAlign;
   return pl;
 }
@@ -114,15 +123,16 @@ hipEvent_t take_event(Timing& t) {
     return e;
   }
   hipEvent_t e = nullptr;
-  hipEventCreate(&e);
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
 }
 
 void drain(Timing& t) {
   for (auto& tl : t.pending) {
-    hipEventSynchronize(tl.stop);
     float ms = 0.f;
-    hipEventElapsedTime(&ms, tl.start, tl.stop);
+    if (hipEventSynchronize(tl.stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, tl.start, tl.stop) != hipSuccess)
+      ms = 0.f;
     size_t i = 0;
     for (; i < t.names.size(); ++i)
       if (t.names[i] == tl.name) break;
@@ -146,7 +156,7 @@ void timing_begin(const char* name, hipStream_t stream) {
   std::lock_guard<std::mutex> g(t.mu);
   if (!t.on) return;
   hipEvent_t e = take_event(t);
-  hipEventRecord(e, stream);
+  if (!e || hipEventRecord(e, stream) != hipSuccess) return;
   t.open.emplace_back(name, e);
 }
 
@@ -157,8 +167,8 @@ void timing_end(const char* name, hipStream_t stream) {
   for (size_t i = t.open.size(); i-- > 0;) {
     if (t.open[i].first == name) {
       hipEvent_t e = take_event(t);
-      hipEventRecord(e, stream);
-      t.pending.push_back(TimedLaunch{name, t.open[i].second, e});
+      if (e && hipEventRecord(e, stream) == hipSuccess)
+        t.pending.push_back(TimedLaunch{name, t.open[i].second, e});
       t.open.erase(t.open.begin() + (long)i);
       break;
     }
@@ -275,6 +285,7 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
   la.topp = topp;
   la.rowstat = rowstat;
   la.desc = desc;
+  la.ucount = carve<int32_t>(workspace, pl.off_ucount);
   la.accept_len = accept_len;
   la.out_tokens = out_tokens;
   la.ratios = ratios;
@@ -300,7 +311,11 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
   da.excl_stride = 0;
   da.esum = carve<double2>(workspace, pl.off_esum);
   da.subsum = carve<double>(workspace, pl.off_subsum);
-  da.sublast = carve<int32_t>(workspace, pl.off_sublast);
+  da.suba = carve<double2>(workspace, pl.off_suba);
+  da.subn = carve<int32_t>(workspace, pl.off_subn);
+  da.suboff = carve<int32_t>(workspace, pl.off_suboff);
+  da.upool = carve<double2>(workspace, pl.off_upool);
+  da.ucount = carve<int32_t>(workspace, pl.off_ucount);
   da.out_tokens = out_tokens;
   da.status = status;
   if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
@@ -362,6 +377,7 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
   ta.topp = topp;
   ta.rowstat = rowstat;
   ta.desc = desc;
+  ta.ucount = carve<int32_t>(workspace, pl.off_ucount);
   ta.excl = excl;
   ta.accept_len = accept_len;
   ta.accept_nodes = accept_nodes;
@@ -388,7 +404,11 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
   da.excl_stride = N;
   da.esum = carve<double2>(workspace, pl.off_esum);
   da.subsum = carve<double>(workspace, pl.off_subsum);
-  da.sublast = carve<int32_t>(workspace, pl.off_sublast);
+  da.suba = carve<double2>(workspace, pl.off_suba);
+  da.subn = carve<int32_t>(workspace, pl.off_subn);
+  da.suboff = carve<int32_t>(workspace, pl.off_suboff);
+  da.upool = carve<double2>(workspace, pl.off_upool);
+  da.ucount = carve<int32_t>(workspace, pl.off_ucount);
   da.out_tokens = out_tokens;
   da.status = status;
   if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;

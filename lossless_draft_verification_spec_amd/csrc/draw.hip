@@ -8,47 +8,77 @@
 // with u' the Philox uniform of (request, position, draw).
 //
 // The draw decides an integer from floating point, so it is computed in fp64 end to end
-// (normalisers, weights and prefix sums): three kernels, all with fixed-order reductions.
-//   k_draw_norm:    per (request, chunk) partial sums of exp((l - lmax) / T) over the kept tokens
-//                   of the stopping p row (and q row);
-//   k_draw_weights: per (request, sub-chunk of 1024 tokens) residual mass and last positive token;
-//   k_draw_select:  per request, locate the sub-chunk holding u' S, then a block prefix scan over
-//                   its 1024 weights.
+// (normalisers, weights and prefix sums) with a table-driven fp64 exp; all reductions run in a
+// fixed order.  Two kernels:
+//   k_draw_pass:   one fp64 pass over the stopping row(s), one wave per sub-chunk of 1024 tokens,
+//                  16 consecutive tokens per lane.  Without a q row (bonus draw, tree draw) the
+//                  weights need no normaliser: w = exp((l - lmax) / T) over the kept, not removed
+//                  tokens, and the pass stores each sub-chunk's mass.  With a q row the sign of
+//                  p'(x) - q'(x) = (e_p(x) - rho e_q(x)) / E_p, rho = E_p / E_q, is decided with
+//                  the ratio of the normalisers from the HBM pass (relative error below ~1e-6);
+//                  tokens within a 1e-5 band of the sign change are uncertain: each wave packs the
+//                  exact (e_p, e_q) of its sub-chunk's uncertain tokens, in token order, into a
+//                  segment of a per-request pool.  The pass stores per sub-chunk the sums A_p, A_q
+//                  of e_p, e_q over the positive tokens and the segment, and per chunk the partial
+//                  normalisers E_p, E_q.
+//   k_draw_select: per request, the exact E_p, E_q give rho; each sub-chunk's mass is
+//                  (A_p - rho A_q) / E_p plus the residual weights of its uncertain tokens (added
+//                  in token order); it is recomputed token by token only when the pool overflowed
+//                  or rho strays from the HBM-pass ratio by more than a quarter of the band (which
+//                  voids the classification); a block scan over the
+//                  masses locates u' S, then a block scan over that sub-chunk's 1024 weights
+//                  picks the token.
 #include "launch.h"
 
 namespace psispec {
 namespace {
 
-template <typename T>
-__device__ inline double term(const T* row, int x, float lmax, float thr, double inv_T) {
-  const float l = to_f32(row[x]);
-  if (!(l >= thr)) return 0.0;
-  return exp(((double)l - (double)lmax) * inv_T);
+constexpr int kPerLane = kSub / 64;  // tokens per lane in k_draw_weights (16)
+
+// Load n consecutive logits starting at x0 (x0 a multiple of n); tokens past V read as -inf.
+// Whole 16-byte vectors when the row allows it, else element by element.
+template <typename T, int n>
+__device__ inline void load_run(const T* row, int x0, int V, bool vec_ok, float (&f)[n]) {
+  constexpr int E = 16 / (int)sizeof(T);
+  if constexpr (n % E == 0) {
+    if (vec_ok && x0 + n <= V) {
+      const u32x4* vp = reinterpret_cast<const u32x4*>(row + x0);
+#pragma unroll
+      for (int v = 0; v < n / E; ++v) {
+        const u32x4 w = vp[v];
+        if constexpr (sizeof(T) == 2) {
+          f[8 * v + 0] = __uint_as_float(w.x << 16);
+          f[8 * v + 1] = __uint_as_float(w.x & 0xffff0000u);
+          f[8 * v + 2] = __uint_as_float(w.y << 16);
+          f[8 * v + 3] = __uint_as_float(w.y & 0xffff0000u);
+          f[8 * v + 4] = __uint_as_float(w.z << 16);
+          f[8 * v + 5] = __uint_as_float(w.z & 0xffff0000u);
+          f[8 * v + 6] = __uint_as_float(w.w << 16);
+          f[8 * v + 7] = __uint_as_float(w.w & 0xffff0000u);
+        } else {
+          f[4 * v + 0] = __uint_as_float(w.x);
+          f[4 * v + 1] = __uint_as_float(w.y);
+          f[4 * v + 2] = __uint_as_float(w.z);
+          f[4 * v + 3] = __uint_as_float(w.w);
+        }
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < n; ++e) f[e] = (x0 + e < V) ? to_f32(row[x0 + e]) : -__builtin_huge_valf();
 }
 
-// fixed-order block sum of one double per thread (wave shuffles, then waves in order)
-__device__ inline double block_sum(double v, double* scratch) {
+__device__ inline double wave_sum(double v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[wave] = v;
-  __syncthreads();
-  double s = 0.0;
-  for (int w = 0; w < kThreads / 64; ++w) s += scratch[w];
-  return s;
+  return v;
 }
 
-__device__ inline int block_max_int(int v, int* scratch) {
+__device__ inline int wave_max(int v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[wave] = v;
-  __syncthreads();
-  int m = scratch[0];
-  for (int w = 1; w < kThreads / 64; ++w) m = max(m, scratch[w]);
-  return m;
+  return v;
 }
 
 struct RowView {
@@ -69,225 +99,378 @@ __device__ inline RowView row_view(const DrawArgs& a, const DrawDesc& d) {
   return v;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_draw_norm(DrawArgs a) {
-  const int r = blockIdx.x / a.nchunk_draw;
-  const int c = blockIdx.x - r * a.nchunk_draw;
-  const DrawDesc d = a.desc[r];
-  const RowView v = row_view(a, d);
-  const T* prow = row_ptr<T>(a.rs, d.prow);
-  const T* qrow = d.qrow >= 0 ? row_ptr<T>(a.rs, d.qrow) : nullptr;
-  const int start = c * a.chunk_elems_draw;
-  const int end = min(a.V, start + a.chunk_elems_draw);
-  double ep = 0.0, eq = 0.0;
-  for (int x = start + threadIdx.x; x < end; x += kThreads) {
-    ep += term(prow, x, v.lmax_p, v.thr_p, a.inv_T);
-    if (qrow) eq += term(qrow, x, v.lmax_q, v.thr_q, a.inv_T);
-  }
-  __shared__ double scratch[kThreads / 64];
-  ep = block_sum(ep, scratch);
-  eq = block_sum(eq, scratch);
-  if (threadIdx.x == 0) a.esum[(int64_t)r * a.nchunk_draw + c] = make_double2(ep, eq);
+// exp((l - lmax) / T) for a kept token, 0 outside the nucleus (and for l = -inf)
+__device__ inline double term(float l, float lmax, float thr, double inv_T, const double* tbl) {
+  if (!(l >= thr)) return 0.0;
+  return exp_tang(((double)l - (double)lmax) * inv_T, tbl);
 }
 
-// Residual weight of token x: max(0, p'(x) - q'(x)), or p'(x) without a q row; removed tokens 0.
-template <typename T>
-__device__ inline double weight(const T* prow, const T* qrow, int x, const RowView& v, double Ep,
-                                double Eq, double inv_T, const int* excl, int nexcl) {
+constexpr double kBand = 1e-5;  // relative band of uncertain residual signs
+
+__device__ inline bool excluded(int x, const int* excl, int nexcl) {
   for (int i = 0; i < nexcl; ++i)
-    if (excl[i] == x) return 0.0;
-  const double pp = term(prow, x, v.lmax_p, v.thr_p, inv_T) / Ep;
-  if (!qrow) return pp;
-  const double qq = term(qrow, x, v.lmax_q, v.thr_q, inv_T) / Eq;
-  const double w = pp - qq;
-  return w > 0.0 ? w : 0.0;
+    if (excl[i] == x) return true;
+  return false;
 }
 
-__device__ inline void normalisers(const DrawArgs& a, int r, double& Ep, double& Eq) {
-  Ep = 0.0;
-  Eq = 0.0;
-  for (int k = 0; k < a.nchunk_draw; ++k) {
-    const double2 e = a.esum[(int64_t)r * a.nchunk_draw + k];
-    Ep += e.x;
-    Eq += e.y;
+// ratio of the normalisers E_p / E_q as estimated by the HBM pass (sum over the kept tokens)
+__device__ inline double rho_estimate(const DrawArgs& a, const DrawDesc& d) {
+  double ep = a.rowstat[d.prow].Z, eq = a.rowstat[d.qrow].Z;
+  if (a.use_topp) {
+    ep *= a.topp[d.prow].M;
+    eq *= a.topp[d.qrow].M;
   }
+  return ep / eq;
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_draw_weights(DrawArgs a) {
+__global__ __launch_bounds__(kThreads) void k_draw_pass(DrawArgs a, int vec_ok) {
+  __shared__ double tbl[64];
+  __shared__ int s_excl[1024];
+  __shared__ double2 s_part[kThreads / 64];
+  exp_table_fill(tbl);
   const int r = blockIdx.x / a.nchunk_draw;
   const int c = blockIdx.x - r * a.nchunk_draw;
   const DrawDesc d = a.desc[r];
   const RowView v = row_view(a, d);
   const T* prow = row_ptr<T>(a.rs, d.prow);
-  const T* qrow = d.qrow >= 0 ? row_ptr<T>(a.rs, d.qrow) : nullptr;
-  __shared__ int s_excl[1024];
-  __shared__ double scratch[kThreads / 64];
-  __shared__ int iscratch[kThreads / 64];
-  const int nexcl = min(d.nexcl, 1024);
-  for (int i = threadIdx.x; i < nexcl; i += kThreads) s_excl[i] = a.excl[(int64_t)r * a.excl_stride + i];
+  const bool has_q = d.qrow >= 0;
+  const T* qrow = has_q ? row_ptr<T>(a.rs, d.qrow) : nullptr;
+  const int nexcl = has_q ? 0 : min(d.nexcl, 1024);
+  for (int i = threadIdx.x; i < nexcl; i += kThreads)
+    s_excl[i] = a.excl[(int64_t)r * a.excl_stride + i];
+  const double rho = has_q ? rho_estimate(a, d) : 0.0;
   __syncthreads();
-  double Ep, Eq;
-  normalisers(a, r, Ep, Eq);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub_per_chunk = a.chunk_elems_draw / kSub;
-  for (int j = 0; j < sub_per_chunk; ++j) {
+  double Ep = 0.0, Eq = 0.0;
+  for (int j = wave; j < sub_per_chunk; j += kThreads / 64) {
     const int sub = c * sub_per_chunk + j;
     if (sub >= a.nsub) break;
-    const int base = sub * kSub + threadIdx.x * 4;
-    double acc = 0.0;
-    int last = -1;
+    const int x0 = sub * kSub + lane * kPerLane;
+    float fp[kPerLane], fq[kPerLane];
+    load_run<T, kPerLane>(prow, x0, a.V, vec_ok, fp);
+    double Ap = 0.0, Aq = 0.0;
+    int unc = 0;
+    uint32_t umask = 0;
+    if (has_q) {
+      load_run<T, kPerLane>(qrow, x0, a.V, vec_ok, fq);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int x = base + e;
-      if (x < a.V) {
-        const double w = weight(prow, qrow, x, v, Ep, Eq, a.inv_T, s_excl, nexcl);
-        acc += w;
-        if (w > 0.0) last = x;
+      for (int e = 0; e < kPerLane; ++e) {
+        const double ep = term(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl);
+        const double eq = term(fq[e], v.lmax_q, v.thr_q, a.inv_T, tbl);
+        Ep += ep;
+        Eq += eq;
+        const double diff = ep - rho * eq, band = kBand * (ep + rho * eq);
+        if (diff > band) {
+          Ap += ep;
+          Aq += eq;
+        } else if (diff >= -band && ep > 0.0) {
+          ++unc;
+          umask |= 1u << e;
+        }
+      }
+      // pack this sub-chunk's uncertain tokens, in token order, into one pool segment
+      int before = unc;  // inclusive prefix over lanes, then made exclusive
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(before, off, 64);
+        if (lane >= off) before += y;
+      }
+      const int total = __shfl(before, 63, 64);
+      before -= unc;
+      int seg = -1;
+      if (total > 0) {
+        if (lane == 0) seg = atomicAdd(a.ucount + r, total);
+        seg = __shfl(seg, 0, 64);
+        if (seg + total > kUncPool) seg = -1;  // pool full: this sub-chunk is summed token by token
+        if (seg >= 0 && umask) {
+          double2* dst = a.upool + (int64_t)r * kUncPool + seg + before;
+          int i = 0;
+#pragma unroll
+          for (int e = 0; e < kPerLane; ++e) {
+            if (umask & (1u << e)) {
+              dst[i++] = make_double2(term(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl),
+                                      term(fq[e], v.lmax_q, v.thr_q, a.inv_T, tbl));
+            }
+          }
+        }
+      }
+      if (lane == 0) a.suboff[(int64_t)r * a.nsub + sub] = seg;
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e) {
+        double ep = term(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl);
+        if (nexcl && excluded(x0 + e, s_excl, nexcl)) ep = 0.0;
+        Ap += ep;
       }
     }
-    const double S = block_sum(acc, scratch);
-    const int L = block_max_int(last, iscratch);
-    if (threadIdx.x == 0) {
-      a.subsum[(int64_t)r * a.nsub + sub] = S;
-      a.sublast[(int64_t)r * a.nsub + sub] = L;
+    Ap = wave_sum(Ap);
+    Aq = wave_sum(Aq);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) unc += __shfl_xor(unc, off, 64);
+    if (lane == 0) {
+      a.suba[(int64_t)r * a.nsub + sub] = make_double2(Ap, Aq);
+      a.subn[(int64_t)r * a.nsub + sub] = unc;
     }
   }
+  if (!has_q) return;
+  Ep = wave_sum(Ep);
+  Eq = wave_sum(Eq);
+  if (lane == 0) s_part[wave] = make_double2(Ep, Eq);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double sp = 0.0, sq = 0.0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      sp += s_part[w].x;
+      sq += s_part[w].y;
+    }
+    a.esum[(int64_t)r * a.nchunk_draw + c] = make_double2(sp, sq);
+  }
+}
+
+// Fixed-order scan of one double per thread across the block.  Returns the exclusive prefix in
+// *lo and the inclusive prefix in *hi with hi of thread t bit-identical to lo of thread t+1, so
+// the intervals [lo, hi) tile [0, total) exactly; returns the block total.
+__device__ inline double block_scan(double x, double* s_wave, double* lo, double* hi) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  double excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = 0.0;
+  __syncthreads();
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  double off_w = 0.0;
+  for (int k = 0; k < wave; ++k) off_w += s_wave[k];
+  double tot = off_w;
+  for (int k = wave; k < kThreads / 64; ++k) tot += s_wave[k];
+  *lo = off_w + excl;
+  *hi = off_w + incl;
+  return tot;
+}
+
+// Weights of the 4 consecutive tokens x0..x0+3 (one thread's share of a sub-chunk).
+//   mode 0: residual max(0, e_p rEp - e_q rEq);  mode 1: e_p with removed tokens;  mode 2: e_p.
+template <typename T>
+__device__ inline void weights4(const T* prow, const T* qrow, int x0, int V, const RowView& v,
+                                int mode, double rEp, double rEq, double inv_T, const double* tbl,
+                                const int* excl, int nexcl, double (&w)[4]) {
+  float fp[4], fq[4];
+  load_run<T, 4>(prow, x0, V, false, fp);
+  if (mode == 0) load_run<T, 4>(qrow, x0, V, false, fq);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const double ep = term(fp[e], v.lmax_p, v.thr_p, inv_T, tbl);
+    if (mode == 0) {
+      const double x = ep * rEp - term(fq[e], v.lmax_q, v.thr_q, inv_T, tbl) * rEq;
+      w[e] = x > 0.0 ? x : 0.0;
+    } else if (mode == 1) {
+      w[e] = (nexcl && excluded(x0 + e, excl, nexcl)) ? 0.0 : ep;
+    } else {
+      w[e] = ep;
+    }
+  }
+}
+
+template <typename T>
+__device__ inline double subchunk_mass(const T* prow, const T* qrow, int sub, int V,
+                                       const RowView& v, int mode, double rEp, double rEq,
+                                       double inv_T, const double* tbl, const int* excl, int nexcl,
+                                       double* s_wave) {
+  double w[4];
+  weights4<T>(prow, qrow, sub * kSub + threadIdx.x * 4, V, v, mode, rEp, rEq, inv_T, tbl, excl,
+              nexcl, w);
+  double lo, hi;
+  return block_scan(w[0] + w[1] + w[2] + w[3], s_wave, &lo, &hi);
 }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_draw_select(DrawArgs a) {
-  const int r = blockIdx.x;
-  const DrawDesc d = a.desc[r];
+  __shared__ double tbl[64];
   __shared__ int s_excl[1024];
   __shared__ double s_wave[kThreads / 64];
-  __shared__ double scratch[kThreads / 64];
-  __shared__ int iscratch[kThreads / 64];
-  __shared__ int s_sub, s_fallback;
-  __shared__ double s_base, s_v;
-  int st = d.st;
+  __shared__ int s_pick[kThreads / 64];
+  __shared__ int s_last[kThreads / 64];
+  __shared__ int s_sub, s_flagged, s_list[1024];
+  __shared__ double s_base;
+  exp_table_fill(tbl);
+  const int r = blockIdx.x;
+  const DrawDesc d = a.desc[r];
   if (d.out_idx < 0) {
-    if (threadIdx.x == 0 && a.status) a.status[r] = st;
+    if (threadIdx.x == 0 && a.status) a.status[r] = d.st;
     return;
   }
+  int st = d.st;
   const RowView v = row_view(a, d);
   const T* prow = row_ptr<T>(a.rs, d.prow);
-  const T* qrow = d.qrow >= 0 ? row_ptr<T>(a.rs, d.qrow) : nullptr;
-  const int nexcl = min(d.nexcl, 1024);
-  for (int i = threadIdx.x; i < nexcl; i += kThreads) s_excl[i] = a.excl[(int64_t)r * a.excl_stride + i];
-  double Ep, Eq;
-  normalisers(a, r, Ep, Eq);
-  const double* subsum = a.subsum + (int64_t)r * a.nsub;
-  const int32_t* sublast = a.sublast + (int64_t)r * a.nsub;
-  const double u = philox_uniform(a.seed, a.request_base + (uint32_t)r, (uint32_t)d.pos,
-                                  kPurposeDraw, a.step);
-  if (threadIdx.x == 0) {
-    double S = 0.0;
-    for (int j = 0; j < a.nsub; ++j) S += subsum[j];
-    s_fallback = !(S > 0.0);
-    s_v = u * S;
+  const bool has_q = d.qrow >= 0;
+  const T* qrow = has_q ? row_ptr<T>(a.rs, d.qrow) : nullptr;
+  const int nexcl = has_q ? 0 : min(d.nexcl, 1024);
+  for (int i = threadIdx.x; i < nexcl; i += kThreads)
+    s_excl[i] = a.excl[(int64_t)r * a.excl_stride + i];
+  if (threadIdx.x == 0) s_flagged = 0;
+  double rEp = 1.0, rEq = 0.0, rho = 0.0;
+  bool band_ok = true;
+  if (has_q) {
+    double Ep = 0.0, Eq = 0.0;
+    for (int k = 0; k < a.nchunk_draw; ++k) {
+      const double2 e = a.esum[(int64_t)r * a.nchunk_draw + k];
+      Ep += e.x;
+      Eq += e.y;
+    }
+    rEp = 1.0 / Ep;
+    rEq = 1.0 / Eq;
+    rho = Ep / Eq;
+    band_ok = fabs(rho / rho_estimate(a, d) - 1.0) <= 0.25 * kBand;
+  }
+  const int mode = has_q ? 0 : 1;
+  double* mass = a.subsum + (int64_t)r * a.nsub;
+  const double2* suba = a.suba + (int64_t)r * a.nsub;
+  const int32_t* subn = a.subn + (int64_t)r * a.nsub;
+  __syncthreads();
+
+  // 1. mass of every sub-chunk: the positive-token sums plus its uncertain tokens (their pool
+  //    segment is in token order, so the sum order is fixed); token-by-token sums only for
+  //    sub-chunks whose segment did not fit and when the classification is void
+  const double2* pool = a.upool + (int64_t)r * kUncPool;
+  const int32_t* suboff = a.suboff + (int64_t)r * a.nsub;
+  for (int j = threadIdx.x; j < a.nsub; j += kThreads) {
+    const double2 A = suba[j];
+    if (!has_q) {
+      mass[j] = A.x;
+      continue;
+    }
+    const int n = subn[j];
+    const int seg = n > 0 ? suboff[j] : 0;
+    if (band_ok && seg >= 0) {
+      double m = (A.x - rho * A.y) * rEp;
+      m = m > 0.0 ? m : 0.0;
+      for (int i = 0; i < n; ++i) {
+        const double2 t = pool[seg + i];
+        const double w = t.x * rEp - t.y * rEq;
+        if (w > 0.0) m += w;
+      }
+      mass[j] = m;
+    } else {
+      const int slot = atomicAdd(&s_flagged, 1);
+      if (slot < 1024) s_list[slot] = j;
+    }
   }
   __syncthreads();
-  if (s_fallback) {
-    // Zero residual mass (not reachable in exact arithmetic): draw from the target row instead.
-    st |= PSISPEC_ST_RESID_ZERO;
-    qrow = nullptr;
+  const int nflag = s_flagged;
+  if (nflag > 1024) {
+    for (int j = 0; j < a.nsub; ++j) {
+      const double m = subchunk_mass<T>(prow, qrow, j, a.V, v, mode, rEp, rEq, a.inv_T, tbl, s_excl,
+                                        nexcl, s_wave);
+      if (threadIdx.x == 0) mass[j] = m;
+    }
+  } else {
+    for (int i = 0; i < nflag; ++i) {
+      const int j = s_list[i];
+      const double m = subchunk_mass<T>(prow, qrow, j, a.V, v, mode, rEp, rEq, a.inv_T, tbl, s_excl,
+                                        nexcl, s_wave);
+      if (threadIdx.x == 0) mass[j] = m;
+    }
   }
-  // Sub-chunk sums for the fallback are recomputed here; the normal path reuses k_draw_weights'.
-  if (threadIdx.x == 0 && !s_fallback) {
-    const double vv = s_v;
-    double C = 0.0;
-    int j = 0;
-    for (; j < a.nsub; ++j) {
-      if (C + subsum[j] > vv) break;
-      C += subsum[j];
+  __syncthreads();
+
+  // 2. locate u' S among the sub-chunks: each thread owns a contiguous run of them
+  const double u = philox_uniform(a.seed, a.request_base + (uint32_t)r, (uint32_t)d.pos,
+                                  kPurposeDraw, a.step);
+  const int per = (a.nsub + kThreads - 1) / kThreads;
+  const int j0 = min(a.nsub, threadIdx.x * per), j1 = min(a.nsub, j0 + per);
+  double mine = 0.0;
+  for (int j = j0; j < j1; ++j) mine += mass[j];
+  double lo, hi;
+  double S = block_scan(mine, s_wave, &lo, &hi);
+  int wmode = mode;
+  if (!(S > 0.0)) {
+    // Zero residual mass (not reachable in exact arithmetic): draw from the target row itself.
+    st |= PSISPEC_ST_RESID_ZERO;
+    wmode = 2;
+    for (int j = 0; j < a.nsub; ++j) {
+      const double m = subchunk_mass<T>(prow, qrow, j, a.V, v, 2, 1.0, 0.0, a.inv_T, tbl, s_excl,
+                                        0, s_wave);
+      if (threadIdx.x == 0) mass[j] = m;
+    }
+    __syncthreads();
+    mine = 0.0;
+    for (int j = j0; j < j1; ++j) mine += mass[j];
+    S = block_scan(mine, s_wave, &lo, &hi);
+  }
+  if (threadIdx.x == 0) {
+    s_sub = a.nsub;
+    s_base = 0.0;
+  }
+  __syncthreads();
+  double vv = u * S;
+  if (lo <= vv && vv < hi) {  // exactly one thread owns vv
+    double C = lo;
+    int j = j0;
+    for (; j < j1; ++j) {
+      if (C + mass[j] > vv) break;
+      C += mass[j];
+    }
+    if (j == j1) {  // rounding: the run ends before vv; its last sub-chunk
+      --j;
+      C -= mass[j];
     }
     s_sub = j;
     s_base = C;
   }
-  if (s_fallback) {
-    // S over the p row, then the sub-chunk walk, both by the whole block in fixed order
-    double S = 0.0;
-    for (int sub = 0; sub < a.nsub; ++sub) {
-      const int x0 = sub * kSub + threadIdx.x * 4;
-      double acc = 0.0;
-      for (int e = 0; e < 4; ++e)
-        if (x0 + e < a.V) acc += weight(prow, qrow, x0 + e, v, Ep, Eq, a.inv_T, s_excl, 0);
-      S += block_sum(acc, scratch);
-    }
-    const double vv = u * S;
-    double C = 0.0;
-    int j = 0;
-    for (; j < a.nsub; ++j) {
-      const int x0 = j * kSub + threadIdx.x * 4;
-      double acc = 0.0;
-      for (int e = 0; e < 4; ++e)
-        if (x0 + e < a.V) acc += weight(prow, qrow, x0 + e, v, Ep, Eq, a.inv_T, s_excl, 0);
-      const double Sj = block_sum(acc, scratch);
-      if (C + Sj > vv) break;
-      C += Sj;
-    }
+  __syncthreads();
+  if (s_sub == a.nsub) {
+    // u' S rounded to S: the last token of positive weight of the row (last sub-chunk with mass)
     if (threadIdx.x == 0) {
+      int j = a.nsub - 1;
+      while (j > 0 && !(mass[j] > 0.0)) --j;
       s_sub = j;
-      s_base = C;
-      s_v = vv;
     }
+    vv = __builtin_huge_val();
+    __syncthreads();
+  }
+  const int sub = s_sub;
+
+  // 3. the token inside the sub-chunk: block scan of its 1024 weights
+  const int x0 = sub * kSub + threadIdx.x * 4;
+  double w[4];
+  weights4<T>(prow, qrow, x0, a.V, v, wmode, rEp, rEq, a.inv_T, tbl, s_excl, nexcl, w);
+  int lastpos = -1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (w[e] > 0.0) lastpos = x0 + e;
+  double l0, h0;
+  block_scan(w[0] + w[1] + w[2] + w[3], s_wave, &l0, &h0);
+  double C = s_base + l0;
+  int tokv = 0x7fffffff;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    C += w[e];
+    if (w[e] > 0.0 && C > vv && tokv == 0x7fffffff) tokv = x0 + e;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    tokv = min(tokv, __shfl_xor(tokv, off, 64));
+    lastpos = max(lastpos, __shfl_xor(lastpos, off, 64));
   }
   __syncthreads();
-  const int sub = s_sub;
-  const int use_excl = s_fallback ? 0 : nexcl;
-  int tokv = 0x7fffffff;
-  int lastpos = -1;
-  if (sub < a.nsub) {
-    // weights of this thread's 4 consecutive tokens and their running sums
-    const int x0 = sub * kSub + threadIdx.x * 4;
-    double w[4];
-    double run = 0.0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w[e] = (x0 + e < a.V) ? weight(prow, qrow, x0 + e, v, Ep, Eq, a.inv_T, s_excl, use_excl) : 0.0;
-      run += w[e];
-      if (w[e] > 0.0) lastpos = x0 + e;
-    }
-    // exclusive scan of the per-thread totals: inclusive wave scan, then wave offsets in order
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    double incl = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    if (lane == 63) s_wave[wave] = incl;
-    __syncthreads();
-    double off_w = 0.0;
-    for (int k = 0; k < wave; ++k) off_w += s_wave[k];
-    double C = s_base + off_w + (incl - run);
-    const double vv = s_v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      C += w[e];
-      if (w[e] > 0.0 && C > vv && tokv == 0x7fffffff) tokv = x0 + e;
-    }
-  } else {
-    __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    s_pick[threadIdx.x >> 6] = tokv;
+    s_last[threadIdx.x >> 6] = lastpos;
   }
-  // first token past v in the sub-chunk (min over threads)
-  int tmin = tokv;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) tmin = min(tmin, __shfl_xor(tmin, off, 64));
-  __shared__ int s_min[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) s_min[threadIdx.x >> 6] = tmin;
-  const int lastsub = block_max_int(lastpos, iscratch);
+  __syncthreads();
   if (threadIdx.x == 0) {
-    int token = 0x7fffffff;
-    for (int k = 0; k < kThreads / 64; ++k) token = min(token, s_min[k]);
-    if (token == 0x7fffffff) {
-      // rounding put u' S at or past the end of the chosen interval: last positive token there,
-      // else the last positive token of the row
-      token = lastsub;
-      if (token < 0 && !s_fallback)
-        for (int j = a.nsub - 1; j >= 0 && token < 0; --j) token = sublast[j];
-      if (token < 0) token = 0;
+    int token = 0x7fffffff, last = -1;
+    for (int k = 0; k < kThreads / 64; ++k) {
+      token = min(token, s_pick[k]);
+      last = max(last, s_last[k]);
     }
+    if (token == 0x7fffffff) token = last >= 0 ? last : 0;  // rounding at the sub-chunk's end
     a.out_tokens[d.out_idx] = token;
     if (a.status) a.status[r] = st;
   }
@@ -298,21 +481,16 @@ __global__ __launch_bounds__(kThreads) void k_draw_select(DrawArgs a) {
 hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)a.batch * a.nchunk_draw);
-  timing_begin("draw_norm", stream);
+  const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
+  const int vec_ok = ((size_t)a.V * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
+                     ((uintptr_t)a.rs.q % 16) == 0;
+  timing_begin("draw_pass", stream);
   if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL(k_draw_norm<bf16_t>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_draw_pass<bf16_t>, dim3(grid), dim3(kThreads), 0, stream, a, vec_ok);
   else
-    hipLaunchKernelGGL(k_draw_norm<float>, dim3(grid), dim3(kThreads), 0, stream, a);
-  timing_end("draw_norm", stream);
+    hipLaunchKernelGGL(k_draw_pass<float>, dim3(grid), dim3(kThreads), 0, stream, a, vec_ok);
+  timing_end("draw_pass", stream);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  timing_begin("draw_weights", stream);
-  if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL(k_draw_weights<bf16_t>, dim3(grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_draw_weights<float>, dim3(grid), dim3(kThreads), 0, stream, a);
-  timing_end("draw_weights", stream);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   timing_begin("draw_select", stream);
   if (dtype == PSISPEC_BF16)

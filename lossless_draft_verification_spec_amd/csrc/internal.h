@@ -15,6 +15,7 @@ namespace psispec {
 
 constexpr int kThreads = 256;       // workgroup size of the streaming kernels (4 wave64)
 constexpr int kSub = 1024;          // tokens per sub-chunk of the fp64 residual prefix sums
+constexpr int kUncPool = 8192;     // uncertain-sign residual tokens kept per request
 constexpr float kNegBig = -3.40282346638528859812e+38f;  // running-max floor (finite: -inf - floor = -inf)
 
 enum : uint32_t { kPurposeAccept = 0, kPurposeDraw = 1 };
@@ -119,6 +120,36 @@ __device__ inline float key_to_float(uint32_t k) {
 __device__ inline float key16_to_float(uint32_t k) {
   const uint32_t b = (k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu);
   return __uint_as_float(b << 16);
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp64 exp by Tang's table-driven method (P. T. P. Tang, "Table-driven implementation of the
+// exponential function in IEEE floating-point arithmetic", ACM TOMS 15(2), 1989), with 64 table
+// entries: x = (64 m + j) ln2/64 + r, |r| <= ln2/128, exp(x) = 2^m * 2^(j/64) * exp(r), exp(r) - 1 by
+// its degree-5 Taylor polynomial (truncation below 3.5e-17 relative).  tbl[j] = 2^(j/64) lives in
+// LDS (filled by exp_table_fill).  Inputs are <= 0 here (logit minus row maximum); below -745 the
+// result underflows to 0.
+// ---------------------------------------------------------------------------------------------
+__device__ inline void exp_table_fill(double* tbl) {
+  for (int j = threadIdx.x; j < 64; j += blockDim.x) tbl[j] = exp2((double)j / 64.0);
+}
+
+__device__ inline double exp_tang(double x, const double* tbl) {
+  if (!(x > -745.0)) return 0.0;
+  const double kInvL = 92.33248261689366;     // 64 / ln 2
+  const double kL1 = 0.010830424696249145;    // ln 2 / 64 rounded to double
+  const double kL2 = 3.623510646634843e-19;   // ln 2 / 64 - kL1
+  const double kf = rint(x * kInvL);
+  const int k = (int)kf;
+  double r = fma(-kf, kL1, x);
+  r = fma(-kf, kL2, r);
+  double t = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+  t = fma(r, t, 1.0 / 6.0);
+  t = fma(r, t, 0.5);
+  t = fma(r, t, 1.0);
+  const double p = r * t;  // exp(r) - 1
+  const double tj = tbl[k & 63];
+  return ldexp(fma(tj, p, tj), k >> 6);
 }
 
 // online softmax accumulation: (m, s) with s = sum exp2((x - m) * c)

@@ -33,6 +33,7 @@ struct LinearArgs {
   const ToppStat* topp;
   RowStat* rowstat;
   DrawDesc* desc;
+  int32_t* ucount;
   int32_t* accept_len;
   int32_t* out_tokens;
   float* ratios;
@@ -55,6 +56,7 @@ struct TreeArgs {
   const ToppStat* topp;
   RowStat* rowstat;
   DrawDesc* desc;
+  int32_t* ucount;
   int32_t* excl;      // [batch][N] excluded tokens of the stopping node
   int32_t* accept_len;
   int32_t* accept_nodes;
@@ -76,9 +78,13 @@ struct DrawArgs {
   const DrawDesc* desc;
   const int32_t* excl;
   int excl_stride;
-  double2* esum;      // [batch][nchunk_draw] partial normalisers (p, q)
-  double* subsum;     // [batch][nsub] residual mass per sub-chunk
-  int32_t* sublast;   // [batch][nsub] last token with positive residual weight per sub-chunk
+  double2* esum;      // [batch][nchunk_draw] partial normalisers (E_p, E_q)
+  double2* suba;      // [batch][nsub] per sub-chunk sums of e_p, e_q over positive tokens
+  int32_t* subn;      // [batch][nsub] uncertain-sign tokens per sub-chunk
+  int32_t* suboff;    // [batch][nsub] pool offset of the sub-chunk's uncertain tokens, -1 = none kept
+  double2* upool;     // [batch][kUncPool] exact (e_p, e_q) of uncertain-sign tokens
+  int32_t* ucount;    // [batch] pool entries handed out (zeroed by the decide kernels)
+  double* subsum;     // [batch][nsub] sub-chunk masses (written by the select)
   int32_t* out_tokens;
   int32_t* status;
 };

@@ -115,6 +115,7 @@ __global__ __launch_bounds__(64) void k_decide_linear(LinearArgs a) {
     dd.nexcl = 0;
     dd.out_idx = (int32_t)((int64_t)r * Bp1 + k);
     a.desc[r] = dd;
+    a.ucount[r] = 0;
   }
 }
 
