@@ -34,7 +34,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=["c2", "ns", "c3"])
+    ap.add_argument("--workload", default="c2", choices=["c2", "ns", "c3", "c5"])
+    ap.add_argument("--no-lmhead", action="store_true", help="skip the fused LM-head measurement")
+    ap.add_argument("--lmhead-steps", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-target", action="store_true", help="skip the batch-256 target shape")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -117,6 +119,65 @@ def run_workload(name, steps, warmup, torch, pkg, workloads):
     return res, host
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, datasheet
+
+
+def run_lmhead(steps, warmup, torch, pkg, workloads):
+    """Time psispec_lmhead_verify on the batch-128, B=8, H=4096, V=151936, rank-16 LoRA workload."""
+    preset = workloads.PRESETS["c5"]
+    t0 = time.time()
+    inp = workloads.make_lmhead(preset, device="cuda", steps=min(steps + warmup, 8))
+    torch.cuda.synchronize()
+    log(f"c5: generated inputs in {time.time() - t0:.1f}s")
+    b, B, H, V, r = preset.batch, preset.B, preset.H, preset.V, preset.r
+    ws = torch.empty(pkg.lmhead_workspace_bytes(b, B, H, V, r, True), dtype=torch.uint8,
+                     device="cuda")
+    out = dict(accept_len=torch.empty(b, dtype=torch.int32, device="cuda"),
+               out_tokens=torch.empty(b, B + 1, dtype=torch.int32, device="cuda"),
+               ratios=torch.empty(b, B, dtype=torch.float32, device="cuda"),
+               accept_mask=torch.empty(b, dtype=torch.int64, device="cuda"),
+               status=torch.empty(b, dtype=torch.int32, device="cuda"))
+    acc = torch.zeros(b, dtype=torch.int64, device="cuda")
+
+    def step(s):
+        pkg.psispec_lmhead_verify(inp.h_ar, inp.h_draft, inp.w_t, inp.drafts[s % len(inp.drafts)],
+                                  inp.a_t, inp.b_t, preset.lora_scale, temperature=preset.T,
+                                  seed=inp.seed, step=s, workspace=ws, out=out)
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    committed = 0
+    for s in range(warmup, warmup + steps):
+        step(s)
+        acc += out["accept_len"].to(torch.int64) + 1
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    committed = int(acc.sum().item())
+    pkg.timing_enable(True)
+    for s in range(warmup, warmup + steps):
+        step(s)
+    kern = pkg.timing_read()
+    pkg.timing_enable(False)
+    flops = workloads.lmhead_flops(b, B, H, V, r)
+    g = kern.get("lmhead_gemm", (0.0, 1))
+    gemm_us = 1e3 * g[0] / max(1, g[1])
+    achieved = flops / (gemm_us / 1e6) / 1e12
+    return dict(workload=f"c5: LM head + linear verify, batch={b} B={B} H={H} V={V} LoRA rank {r}, "
+                         f"bf16 MFMA (fp32 accumulate)",
+                ms_per_step=round(ms / steps, 4),
+                rows_per_s=round(steps * b * B / (ms / 1e3), 1),
+                committed_tokens_per_s=round(committed / (ms / 1e3), 1),
+                kernels_avg_us={k: round(1e3 * v[0] / max(1, v[1]), 2) for k, v in kern.items()},
+                roofline={"bound": "mfma", "kernel": "k_lmhead_gemm", "achieved": round(achieved, 1),
+                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "flops_per_launch": flops, "avg_launch_us": round(gemm_us, 2)})
+
+
 def read_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter summary, if it matches the current kernel
     source; else None."""
@@ -195,6 +256,9 @@ def main():
         copy_calibration(torch)
         return
     pkg.lib()
+    if args.workload == "c5":
+        print(json.dumps(run_lmhead(args.lmhead_steps, 3, torch, pkg, workloads)), flush=True)
+        return
     res, host = run_workload(args.workload, args.steps, args.warmup, torch, pkg, workloads)
     pr = res["preset"]
     log(f"{args.workload}: {res['ms_per_step'] * 1e3:.1f} us/step, kernels {res['kernels']}")
@@ -212,6 +276,10 @@ def main():
                       rowstats_frac_of_peak=round(tres.get("rowstats_gbs", 0.0) / HBM_PEAK_GBS, 4),
                       kernels_avg_us={k: round(v["avg_us"], 2) for k, v in tres["kernels"].items()})
         log(f"ns: {tres['ms_per_step'] * 1e3:.1f} us/step, kernels {tres['kernels']}")
+    lmhead = None
+    if not args.no_lmhead:
+        lmhead = run_lmhead(args.lmhead_steps, 3, torch, pkg, workloads)
+        log(f"c5: {lmhead['ms_per_step'] * 1e3:.1f} us/step, kernels {lmhead['kernels_avg_us']}")
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(host, pr, args.cpu_seconds)
@@ -246,6 +314,7 @@ def main():
                      "avg_launch_us": round(rs["avg_us"], 2)},
         "cpu_baseline": cpu,
         "target_shape": target,
+        "lmhead": lmhead,
     }
     print(json.dumps(line), flush=True)
 

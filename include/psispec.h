@@ -141,6 +141,39 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
                                    int32_t* status, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/*
+ * LM head + linear verify ([lanes] §"헤드냐, LoRA냐": the draft path is the frozen AR weights plus a
+ * low-rank LoRA delta; [alphalab] walkthrough steps 2-3: the draft rows go through the LoRA path, the
+ * AR path scores the block).  Computes, on the bf16 matrix cores with fp32 accumulation,
+ *   p logits (AR rows)    = h_ar . W
+ *   q logits (draft rows) = h_draft . W + lora_scale (h_draft . A) . B
+ * and runs psispec_verify_linear on them (same sampling, outputs, statuses and Philox keys).
+ *
+ *   h_ar      bf16 [batch][B+1][H]  final hidden states of the AR rows (row B = block end)
+ *   h_draft   bf16 [batch][B][H]    final hidden states of the draft rows
+ *   w_t       bf16 [V][H]           W[H][V] stored one vocabulary row at a time
+ *   lora_a_t  bf16 [r][H]           A[H][r] stored one rank row at a time; NULL when r = 0
+ *   lora_b_t  bf16 [V][r]           B[r][V] stored one vocabulary row at a time; NULL when r = 0
+ *   H         multiple of 64;  0 <= r <= 64;  B 1..64
+ *   logits    fp32 [batch*(2B+1)][V] or NULL: where the logits are written (rows 0..batch(B+1)-1
+ *             the AR rows request-major, then the draft rows); NULL keeps them in the workspace
+ *             (size from psispec_lmhead_verify_workspace with logits_in_workspace = 1)
+ * h_ar, h_draft, w_t, lora_a_t and logits must be 16-byte aligned (PSISPEC_EINVAL otherwise).  All
+ * inputs are read-only and caller-owned; the call is asynchronous on `stream`.
+ * The product h_draft . A is formed in fp64 and enters the matrix product as a bf16 pair
+ * (hi + lo, relative error 2^-17).
+ */
+size_t psispec_lmhead_verify_workspace(int32_t batch, int32_t B, int32_t H, int32_t V, int32_t r,
+                                       int32_t logits_in_workspace);
+
+psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, const void* w_t,
+                                     const void* lora_a_t, const void* lora_b_t, float lora_scale,
+                                     int32_t batch, int32_t B, int32_t H, int32_t V, int32_t r,
+                                     const int32_t* draft_tokens, const psispec_sampling* s,
+                                     int32_t* accept_len, int32_t* out_tokens, float* ratios,
+                                     uint64_t* accept_mask, int32_t* status, float* logits,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for a return code (static string). */
 const char* psispec_strerror(psispec_status code);
 

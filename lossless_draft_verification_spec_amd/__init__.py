@@ -20,8 +20,9 @@ PSISPEC_FIRST_FROM_TARGET = 1
 ST_NONFINITE, ST_BAD_TOKEN, ST_Q_ZERO, ST_RESID_ZERO, ST_BAD_PARENT = 1, 2, 4, 8, 16
 
 EXPORTS = ("psispec_verify_linear_workspace", "psispec_verify_linear",
-           "psispec_verify_tree_workspace", "psispec_verify_tree", "psispec_strerror",
-           "psispec_timing_enable", "psispec_timing_read")
+           "psispec_verify_tree_workspace", "psispec_verify_tree", "psispec_lmhead_verify_workspace",
+           "psispec_lmhead_verify", "psispec_strerror", "psispec_timing_enable",
+           "psispec_timing_read")
 
 
 class PsispecError(RuntimeError):
@@ -56,6 +57,11 @@ def lib():
         L.psispec_verify_tree.argtypes = [P, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P,
                                           sz, P]
         L.psispec_verify_tree.restype = i32
+        L.psispec_lmhead_verify_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.psispec_lmhead_verify_workspace.restype = sz
+        L.psispec_lmhead_verify.argtypes = ([P, P, P, P, P, ctypes.c_float, i32, i32, i32, i32, i32,
+                                             P, P, P, P, P, P, P, P, P, sz, P])
+        L.psispec_lmhead_verify.restype = i32
         L.psispec_strerror.argtypes = [i32]
         L.psispec_strerror.restype = ctypes.c_char_p
         L.psispec_timing_enable.argtypes = [i32]
@@ -189,6 +195,70 @@ def psispec_verify_tree(p_logits: torch.Tensor, parent: torch.Tensor, node_token
         _ptr(out["out_tokens"]), _ptr(out.get("node_ratios")), _ptr(out.get("status")),
         _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "psispec_verify_tree")
+    return out
+
+
+def lmhead_workspace_bytes(batch, B, H, V, r, logits_in_workspace=True) -> int:
+    return int(lib().psispec_lmhead_verify_workspace(batch, B, H, V, r, 1 if logits_in_workspace else 0))
+
+
+def psispec_lmhead_verify(h_ar: torch.Tensor, h_draft: torch.Tensor, w_t: torch.Tensor,
+                          draft_tokens: torch.Tensor, lora_a_t: torch.Tensor | None = None,
+                          lora_b_t: torch.Tensor | None = None, lora_scale: float = 1.0,
+                          temperature: float = 1.0, top_p: float = 1.0, seed: int = 0, step: int = 0,
+                          request_base: int = 0, flags: int = 0, logits: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None, out: dict | None = None,
+                          stream=None) -> dict:
+    """LM head + linear verify.  h_ar [batch][B+1][H], h_draft [batch][B][H], w_t [V][H] (the
+    weight stored one vocabulary row at a time), lora_a_t [r][H], lora_b_t [V][r], all bf16 on one
+    GPU; draft_tokens int32 [batch][B].  `logits`, if given, is an fp32 [batch*(2B+1)][V] tensor
+    that receives the logits (AR rows first).  Returns the outputs of psispec_verify_linear."""
+    if h_ar.dim() != 3 or h_draft.dim() != 3 or w_t.dim() != 2:
+        raise PsispecError("h_ar [batch][B+1][H], h_draft [batch][B][H], w_t [V][H]")
+    batch, Bp1, H = h_ar.shape
+    B = Bp1 - 1
+    V = w_t.shape[0]
+    if tuple(h_draft.shape) != (batch, B, H) or w_t.shape[1] != H:
+        raise PsispecError("h_draft must be [batch][B][H] and w_t [V][H]")
+    for name, t in (("h_ar", h_ar), ("h_draft", h_draft), ("w_t", w_t)):
+        if t.dtype != torch.bfloat16:
+            raise PsispecError(f"{name} must be bfloat16")
+        _dev(t, name)
+    r = 0
+    if lora_a_t is not None and lora_a_t.numel():
+        r = lora_a_t.shape[0]
+        if tuple(lora_a_t.shape) != (r, H) or lora_b_t is None or tuple(lora_b_t.shape) != (V, r):
+            raise PsispecError("lora_a_t must be [r][H] and lora_b_t [V][r]")
+        _dev(lora_a_t, "lora_a_t")
+        _dev(lora_b_t, "lora_b_t")
+    else:
+        lora_a_t = lora_b_t = None
+    if tuple(draft_tokens.shape) != (batch, B) or draft_tokens.dtype != torch.int32:
+        raise PsispecError("draft_tokens must be int32 [batch][B]")
+    _dev(draft_tokens, "draft_tokens")
+    dev = h_ar.device
+    if logits is not None:
+        if tuple(logits.shape) != (batch * (2 * B + 1), V) or logits.dtype != torch.float32:
+            raise PsispecError("logits must be float32 [batch*(2B+1)][V]")
+        _dev(logits, "logits")
+    if out is None:
+        out = dict(accept_len=torch.empty(batch, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty(batch, B + 1, dtype=torch.int32, device=dev),
+                   ratios=torch.empty(batch, B, dtype=torch.float32, device=dev),
+                   accept_mask=torch.empty(batch, dtype=torch.int64, device=dev),
+                   status=torch.empty(batch, dtype=torch.int32, device=dev))
+    need = lmhead_workspace_bytes(batch, B, H, V, r, logits is None)
+    if need == 0:
+        raise PsispecError("unsupported sizes (H a multiple of 64, r <= 64, B 1..64)")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = _sampling(temperature, top_p, seed, step, request_base, flags)
+    rc = lib().psispec_lmhead_verify(
+        _ptr(h_ar), _ptr(h_draft), _ptr(w_t), _ptr(lora_a_t), _ptr(lora_b_t), float(lora_scale),
+        batch, B, H, V, r, _ptr(draft_tokens), ctypes.byref(s), _ptr(out["accept_len"]),
+        _ptr(out["out_tokens"]), _ptr(out.get("ratios")), _ptr(out.get("accept_mask")),
+        _ptr(out.get("status")), _ptr(logits), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "psispec_lmhead_verify")
     return out
 
 

@@ -25,13 +25,13 @@ struct Plan {
   int nchunk, chunk_elems;          // main pass split of a row
   int nchunk_draw, chunk_elems_draw, nsub;
   size_t off_part, off_rowstat, off_topp, off_desc, off_excl, off_esum, off_suba, off_subn,
-      off_subsum, off_suboff, off_upool, off_ucount;
+      off_subsum, off_suboff, off_upool, off_ucount, off_extra;
   size_t total;
 };
 
 // Row split of the HBM pass: chunks of about 32 KiB so that even a few hundred rows give
 // thousands of workgroups; chunk starts stay 16-byte aligned (multiples of 64 elements).
-Plan make_plan(int64_t rows, int batch, int V, size_t es, int excl_stride) {
+Plan make_plan(int64_t rows, int batch, int V, size_t es, int excl_stride, int fixed_nchunk = 0) {
   Plan pl{};
   const size_t row_bytes = (size_t)V * es;
   int nchunk = (int)((row_bytes + 32767) / 32768);
@@ -40,6 +40,10 @@ Plan make_plan(int64_t rows, int batch, int V, size_t es, int excl_stride) {
   ce = (ce + 63) / 64 * 64;
   pl.nchunk = (V + ce - 1) / ce;
   pl.chunk_elems = ce;
+  if (fixed_nchunk > 0) {  // row pairs produced elsewhere (the LM-head epilogue), one per column tile
+    pl.nchunk = fixed_nchunk;
+    pl.chunk_elems = 0;
+  }
   pl.nsub = (V + kSub - 1) / kSub;
   int nd = batch > 0 ? (2048 + batch - 1) / batch : 1;
   if (nd > pl.nsub) nd = pl.nsub;
@@ -72,7 +76,8 @@ Plan make_plan(int64_t rows, int batch, int V, size_t es, int excl_stride) {
   off = align_up(off + sizeof(double2) * (size_t)batch * kUncPool);
   pl.off_ucount = off;
   off = align_up(off + sizeof(int32_t) * (size_t)batch);
-  pl.total = off + kAlign;
+  pl.total = off;
+  pl.off_extra = off;
   return pl;
 }
 
@@ -226,14 +231,14 @@ size_t psispec_verify_linear_workspace(int32_t batch, int32_t B, int32_t V, psis
   if (batch < 0 || B < 1 || B > 64 || V < 1) return 0;
   if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return 0;
   const int64_t rows = (int64_t)batch * (2 * B + 1);
-  return make_plan(rows, batch, V, elem_size(dtype), 0).total;
+  return make_plan(rows, batch, V, elem_size(dtype), 0).total + kAlign;
 }
 
 size_t psispec_verify_tree_workspace(int32_t batch, int32_t N, int32_t V, psispec_dtype dtype) {
   if (batch < 0 || N < 1 || N > 1024 || V < 1) return 0;
   if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return 0;
   const int64_t rows = (int64_t)batch * (N + 1);
-  return make_plan(rows, batch, V, elem_size(dtype), N).total;
+  return make_plan(rows, batch, V, elem_size(dtype), N).total + kAlign;
 }
 
 psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits, psispec_dtype dtype,
@@ -412,6 +417,161 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
   da.out_tokens = out_tokens;
   da.status = status;
   if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
+  return PSISPEC_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// LM head + linear verify
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+struct LMPlan {
+  Plan pl;
+  size_t off_logits, off_taug, off_baug, total;
+  int ntiles, mtiles, kx;
+};
+
+LMPlan make_lm_plan(int batch, int B, int H, int V, int r, bool own_logits) {
+  LMPlan lp{};
+  const int nP = batch * (B + 1), nQ = batch * B, M = nP + nQ;
+  lp.ntiles = (V + lmhead_tile_n() - 1) / lmhead_tile_n();
+  lp.mtiles = (M + 255) / 256;
+  lp.pl = make_plan((int64_t)M, batch, V, 4, 0, lp.ntiles);
+  size_t off = lp.pl.total;
+  lp.off_logits = off;
+  if (own_logits) off = align_up(off + sizeof(float) * (size_t)M * (size_t)V);
+  lp.kx = r > 0 ? (2 * r + 63) / 64 * 64 : 0;
+  lp.off_taug = off;
+  off = align_up(off + sizeof(uint16_t) * (size_t)M * (size_t)lp.kx);
+  lp.off_baug = off;
+  off = align_up(off + sizeof(uint16_t) * (size_t)V * (size_t)lp.kx);
+  lp.total = off + kAlign;
+  (void)H;
+  return lp;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t psispec_lmhead_verify_workspace(int32_t batch, int32_t B, int32_t H, int32_t V, int32_t r,
+                                       int32_t logits_in_workspace) {
+  if (batch < 0 || B < 1 || B > 64 || V < 1 || H < 64 || H % 64 || r < 0 || r > 64) return 0;
+  return make_lm_plan(batch, B, H, V, r, logits_in_workspace != 0).total;
+}
+
+psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, const void* w_t,
+                                     const void* lora_a_t, const void* lora_b_t, float lora_scale,
+                                     int32_t batch, int32_t B, int32_t H, int32_t V, int32_t r,
+                                     const int32_t* draft_tokens, const psispec_sampling* s,
+                                     int32_t* accept_len, int32_t* out_tokens, float* ratios,
+                                     uint64_t* accept_mask, int32_t* status, float* logits,
+                                     void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  if (batch < 0 || B < 1 || B > 64 || V < 1 || H < 64 || H % 64 || r < 0 || r > 64)
+    return PSISPEC_EINVAL;
+  if (!sampling_ok(s) || !isfinite(lora_scale)) return PSISPEC_EINVAL;
+  if (batch == 0) return PSISPEC_OK;
+  if (!h_ar || !h_draft || !w_t || !draft_tokens || !accept_len || !out_tokens) return PSISPEC_EINVAL;
+  if (r > 0 && (!lora_a_t || !lora_b_t)) return PSISPEC_EINVAL;
+  if (((uintptr_t)h_ar | (uintptr_t)h_draft | (uintptr_t)w_t | (uintptr_t)lora_a_t |
+       (uintptr_t)logits) % 16)
+    return PSISPEC_EINVAL;
+  const LMPlan lp = make_lm_plan(batch, B, H, V, r, logits == nullptr);
+  if (!workspace || workspace_bytes < lp.total || ((uintptr_t)workspace % kAlign) != 0)
+    return PSISPEC_EWORKSPACE;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const double T = s->temperature;
+  const float c = (float)(1.4426950408889634074 / T);
+  const bool use_topp = s->top_p < 1.0;
+  const int nP = batch * (B + 1), nQ = batch * B, M = nP + nQ;
+  float* L = logits ? logits : carve<float>(workspace, lp.off_logits);
+  const Plan& pl = lp.pl;
+  float2* part = carve<float2>(workspace, pl.off_part);
+
+  LMHeadArgs ha{};
+  ha.h_ar = static_cast<const uint16_t*>(h_ar);
+  ha.h_dr = static_cast<const uint16_t*>(h_draft);
+  ha.w_t = static_cast<const uint16_t*>(w_t);
+  ha.lora_at = static_cast<const uint16_t*>(lora_a_t);
+  ha.lora_bt = static_cast<const uint16_t*>(lora_b_t);
+  ha.taug = carve<uint16_t>(workspace, lp.off_taug);
+  ha.baug = carve<uint16_t>(workspace, lp.off_baug);
+  ha.kx = lp.kx;
+  ha.lora_scale = lora_scale;
+  ha.nP = nP;
+  ha.nQ = nQ;
+  ha.M = M;
+  ha.N = V;
+  ha.K = H;
+  ha.r = r;
+  ha.mtiles = lp.mtiles;
+  ha.ntiles = lp.ntiles;
+  ha.c = c;
+  ha.logits = L;
+  ha.part = part;
+  if (launch_lmhead(ha, stream) != hipSuccess) return PSISPEC_EHIP;
+
+  // the verify itself, on the fp32 logits, with the epilogue's row pairs (one per column tile)
+  RowSet rs{L, L + (int64_t)nP * V, nP, nQ, V, B, (s->flags & PSISPEC_FIRST_FROM_TARGET) ? 1 : 0};
+  RowStat* rowstat = carve<RowStat>(workspace, pl.off_rowstat);
+  ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
+  DrawDesc* desc = carve<DrawDesc>(workspace, pl.off_desc);
+  if (use_topp &&
+      launch_topp(rs, PSISPEC_F32, pl.nchunk, c, s->top_p, part, topp, stream) != hipSuccess)
+    return PSISPEC_EHIP;
+  LinearArgs la{};
+  la.rs = rs;
+  la.draft = draft_tokens;
+  la.batch = batch;
+  la.B = B;
+  la.V = V;
+  la.nchunk = pl.nchunk;
+  la.c = c;
+  la.inv_T = 1.0 / T;
+  la.use_topp = use_topp;
+  la.seed = s->seed;
+  la.step = s->step;
+  la.request_base = s->request_base;
+  la.flags = s->flags;
+  la.part = part;
+  la.topp = topp;
+  la.rowstat = rowstat;
+  la.desc = desc;
+  la.ucount = carve<int32_t>(workspace, pl.off_ucount);
+  la.accept_len = accept_len;
+  la.out_tokens = out_tokens;
+  la.ratios = ratios;
+  la.accept_mask = accept_mask;
+  if (launch_decide_linear(la, PSISPEC_F32, stream) != hipSuccess) return PSISPEC_EHIP;
+  DrawArgs da{};
+  da.rs = rs;
+  da.batch = batch;
+  da.V = V;
+  da.nchunk_draw = pl.nchunk_draw;
+  da.chunk_elems_draw = pl.chunk_elems_draw;
+  da.nsub = pl.nsub;
+  da.inv_T = 1.0 / T;
+  da.use_topp = use_topp;
+  da.seed = s->seed;
+  da.step = s->step;
+  da.request_base = s->request_base;
+  da.rowstat = rowstat;
+  da.topp = topp;
+  da.desc = desc;
+  da.excl = nullptr;
+  da.excl_stride = 0;
+  da.esum = carve<double2>(workspace, pl.off_esum);
+  da.suba = carve<double2>(workspace, pl.off_suba);
+  da.subn = carve<int32_t>(workspace, pl.off_subn);
+  da.suboff = carve<int32_t>(workspace, pl.off_suboff);
+  da.upool = carve<double2>(workspace, pl.off_upool);
+  da.ucount = carve<int32_t>(workspace, pl.off_ucount);
+  da.subsum = carve<double>(workspace, pl.off_subsum);
+  da.out_tokens = out_tokens;
+  da.status = status;
+  if (launch_draw(da, PSISPEC_F32, stream) != hipSuccess) return PSISPEC_EHIP;
   return PSISPEC_OK;
 }
 

@@ -90,4 +90,24 @@ struct DrawArgs {
 };
 hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t stream);
 
+// lmhead.hip -- LM head on MFMA feeding the linear verify
+struct LMHeadArgs {
+  const uint16_t* h_ar;     // bf16 [nP][K]
+  const uint16_t* h_dr;     // bf16 [nQ][K]
+  const uint16_t* w_t;      // bf16 [N][K]
+  const uint16_t* lora_at;  // bf16 [r][K] or null
+  const uint16_t* lora_bt;  // bf16 [N][r] or null
+  uint16_t* taug;           // bf16 [M][kx] scratch: zeros (AR rows), [t_hi | t_lo | 0] (draft rows)
+  uint16_t* baug;           // bf16 [N][kx] scratch: [B_t | B_t | 0]
+  float lora_scale;
+  int nP, nQ, M, N, K, r;
+  int kx;                   // extra contraction columns (2r rounded up to 64; 0 without LoRA)
+  int mtiles, ntiles;
+  float c;                  // log2(e) / T for the epilogue's row pairs
+  float* logits;            // fp32 [M][N]
+  float2* part;             // [M][ntiles] online (max, sum exp) pairs
+};
+int lmhead_tile_n();
+hipError_t launch_lmhead(const LMHeadArgs& a, hipStream_t stream);
+
 }  // namespace psispec

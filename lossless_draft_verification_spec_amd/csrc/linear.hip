@@ -32,27 +32,59 @@ __global__ __launch_bounds__(64) void k_decide_linear(LinearArgs a) {
   __shared__ double s_Z[2 * kMaxB + 1];
   __shared__ int s_st[2 * kMaxB + 1];
 
-  // 1. finish the row statistics (rows 0..B of p, then rows 0..B-1 of q)
-  for (int j = t; j < 2 * B + 1; j += 64) {
-    const int64_t row = j <= B ? prow0 + j : qrow0 + (j - Bp1);
-    if (j > B && first_from_target && j == Bp1) {
-      s_lmax[j] = 0.f;
-      s_Z[j] = 1.0;
-      s_st[j] = 0;
-      continue;
+  // 1. finish the row statistics (rows 0..B of p, then rows 0..B-1 of q).  Few chunks: one lane
+  //    per row; many (LM-head column tiles): the wave reduces each row's chunks in a fixed order.
+  if (a.nchunk <= 16) {
+    for (int j = t; j < 2 * B + 1; j += 64) {
+      const int64_t row = j <= B ? prow0 + j : qrow0 + (j - Bp1);
+      if (j > B && first_from_target && j == Bp1) {
+        s_lmax[j] = 0.f;
+        s_Z[j] = 1.0;
+        s_st[j] = 0;
+        continue;
+      }
+      float lmax = kNegBig;
+      for (int k = 0; k < a.nchunk; ++k) lmax = fmaxf(lmax, a.part[row * a.nchunk + k].x);
+      double Z = 0.0;
+      for (int k = 0; k < a.nchunk; ++k) {
+        const float2 pk = a.part[row * a.nchunk + k];
+        Z += (double)pk.y * exp2((double)(pk.x - lmax) * (double)a.c);
+      }
+      const int st = row_status(lmax, Z);
+      s_lmax[j] = lmax;
+      s_Z[j] = Z;
+      s_st[j] = st;
+      a.rowstat[row] = RowStat{lmax, st, Z};
     }
-    float lmax = kNegBig;
-    for (int k = 0; k < a.nchunk; ++k) lmax = fmaxf(lmax, a.part[row * a.nchunk + k].x);
-    double Z = 0.0;
-    for (int k = 0; k < a.nchunk; ++k) {
-      const float2 pk = a.part[row * a.nchunk + k];
-      Z += (double)pk.y * exp2((double)(pk.x - lmax) * (double)a.c);
+  } else {
+    for (int j = 0; j < 2 * B + 1; ++j) {
+      const int64_t row = j <= B ? prow0 + j : qrow0 + (j - Bp1);
+      if (j > B && first_from_target && j == Bp1) {
+        if (t == 0) {
+          s_lmax[j] = 0.f;
+          s_Z[j] = 1.0;
+          s_st[j] = 0;
+        }
+        continue;
+      }
+      const float2* pr = a.part + row * a.nchunk;
+      float lmax = kNegBig;
+      for (int k = t; k < a.nchunk; k += 64) lmax = fmaxf(lmax, pr[k].x);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, 64));
+      double Z = 0.0;
+      for (int k = t; k < a.nchunk; k += 64)
+        Z += (double)pr[k].y * exp2((double)(pr[k].x - lmax) * (double)a.c);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) Z += __shfl_xor(Z, off, 64);
+      if (t == 0) {
+        const int st = row_status(lmax, Z);
+        s_lmax[j] = lmax;
+        s_Z[j] = Z;
+        s_st[j] = st;
+        a.rowstat[row] = RowStat{lmax, st, Z};
+      }
     }
-    const int st = row_status(lmax, Z);
-    s_lmax[j] = lmax;
-    s_Z[j] = Z;
-    s_st[j] = st;
-    a.rowstat[row] = RowStat{lmax, st, Z};
   }
   __syncthreads();
 

@@ -253,9 +253,9 @@ class LMHeadInputs:
     preset: LMHeadPreset
     h_ar: torch.Tensor     # bf16 [batch][B+1][H]
     h_draft: torch.Tensor  # bf16 [batch][B][H]
-    W: torch.Tensor        # bf16 [H][V]
-    A: torch.Tensor        # bf16 [H][r]
-    Bl: torch.Tensor       # bf16 [r][V]
+    w_t: torch.Tensor      # bf16 [V][H]: the LM-head weight W[H][V] stored one token row at a time
+    a_t: torch.Tensor      # bf16 [r][H]: LoRA A[H][r] stored the same way
+    b_t: torch.Tensor      # bf16 [V][r]: LoRA B[r][V] stored the same way
     seed: int
     drafts: list = field(default_factory=list)
 
@@ -263,25 +263,29 @@ class LMHeadInputs:
 def make_lmhead(preset: LMHeadPreset | str, device="cpu", rotation: int = 0, steps: int | None = None,
                 batch=None, B=None, H=None, V=None, r=None) -> LMHeadInputs:
     """Hidden states ~ N(0,1), W ~ N(0, 0.02^2), LoRA A, B ~ N(0, 0.01^2), all bf16 (independent
-    draws for the AR and draft rows).  Drafts are drawn from the draft logits computed here with a
-    plain fp32 torch matmul (input generation only)."""
+    draws for the AR and the draft rows).  The weights are generated in the usual output-major
+    storage (one row per output feature).  Drafts are drawn from the draft logits computed here with
+    a plain fp32 torch matmul (input generation only)."""
     if isinstance(preset, str):
         preset = PRESETS[preset]
     preset = replace(preset, batch=batch or preset.batch, B=B or preset.B, H=H or preset.H,
-                     V=V or preset.V, r=r or preset.r)
+                     V=V or preset.V, r=preset.r if r is None else r)
     b, B, H, V, rr = preset.batch, preset.B, preset.H, preset.V, preset.r
     g = _gen(device, preset.seed, rotation, 0x1AE)
     h_ar = torch.randn(b, B + 1, H, generator=g, device=device).to(torch.bfloat16)
     h_dr = torch.randn(b, B, H, generator=g, device=device).to(torch.bfloat16)
-    W = (torch.randn(H, V, generator=g, device=device) * 0.02).to(torch.bfloat16)
-    A = (torch.randn(H, rr, generator=g, device=device) * 0.01).to(torch.bfloat16)
-    Bl = (torch.randn(rr, V, generator=g, device=device) * 0.01).to(torch.bfloat16)
+    w_t = (torch.randn(V, H, generator=g, device=device) * 0.02).to(torch.bfloat16)
+    a_t = (torch.randn(max(rr, 1), H, generator=g, device=device) * 0.01).to(torch.bfloat16)[:rr]
+    b_t = (torch.randn(V, max(rr, 1), generator=g, device=device) * 0.01).to(torch.bfloat16)[:, :rr]
     seed = (preset.seed * 1000003 + rotation) & (2**64 - 1)
-    inp = LMHeadInputs(preset, h_ar, h_dr, W, A, Bl, seed)
+    inp = LMHeadInputs(preset, h_ar.contiguous(), h_dr.contiguous(), w_t.contiguous(),
+                       a_t.contiguous(), b_t.contiguous(), seed)
     n = steps if steps is not None else 1
     if n:
         hd = h_dr.float().reshape(b * B, H)
-        ql = hd @ W.float() + preset.lora_scale * ((hd @ A.float()) @ Bl.float())
+        ql = hd @ w_t.float().t()
+        if rr:
+            ql += preset.lora_scale * ((hd @ a_t.float().t()) @ b_t.float().t())
         ql = ql.view(b, B, V)
         for s in range(n):
             gs = _gen(device, preset.seed, s, 0xD7AF7)

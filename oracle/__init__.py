@@ -185,3 +185,18 @@ def lmhead_logits(h, W, A=None, Bl=None, scale=1.0):
     if rc != 0:
         raise ValueError(f"oracle lmhead_logits rejected its arguments (code {rc})")
     return out
+
+
+def lmhead_logits_rows(h, w_t, a_t=None, b_t=None, scale=1.0):
+    """fp64 logits of bf16 hidden rows h[M][H] (uint16 bit patterns) against weights stored one output
+    row at a time: w_t[V][H] (W = w_t^T), LoRA a_t[r][H] (A = a_t^T), b_t[V][r] (B = b_t^T).
+    The same arithmetic as lmhead_logits, with numpy's fp64 matmul as the product (for full-size
+    rows, where the plain loops would take minutes)."""
+    def val(x):
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    hv = val(h)
+    out = hv @ val(w_t).T
+    if a_t is not None and np.asarray(a_t).size:
+        out += scale * ((hv @ val(a_t).T) @ val(b_t).T)
+    return out

@@ -21,3 +21,17 @@ def test_lmhead_logits_match_numpy(orc, M, H, V, r):
     assert np.allclose(lora, hv @ Wv + (hv @ Av) @ Bv, rtol=1e-13, atol=1e-15)
     half = orc.lmhead_logits(h, W, A, Bl, scale=0.5)
     assert np.allclose(half - base, 0.5 * (lora - base), rtol=1e-12, atol=1e-15)
+
+
+def test_lmhead_rows_helper_matches_plain_oracle(orc):
+    """The numpy-product helper used at full size agrees with the plain loops (weights stored one
+    output row at a time)."""
+    rng = np.random.default_rng(7)
+    M, H, V, r = 4, 96, 53, 3
+    h = bf16_round(rng.standard_normal((M, H)))
+    W = bf16_round(rng.standard_normal((H, V)) * 0.02)
+    A = bf16_round(rng.standard_normal((H, r)) * 0.01)
+    Bl = bf16_round(rng.standard_normal((r, V)) * 0.01)
+    plain = orc.lmhead_logits(h, W, A, Bl, scale=1.0)
+    helper = orc.lmhead_logits_rows(h, W.T.copy(), A.T.copy(), Bl.T.copy(), 1.0)
+    assert np.allclose(plain, helper, rtol=1e-13, atol=1e-15)
