@@ -154,7 +154,7 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
  *   w_t       bf16 [V][H]           W[H][V] stored one vocabulary row at a time
  *   lora_a_t  bf16 [r][H]           A[H][r] stored one rank row at a time; NULL when r = 0
  *   lora_b_t  bf16 [V][r]           B[r][V] stored one vocabulary row at a time; NULL when r = 0
- *   H         multiple of 64;  0 <= r <= 64;  B 1..64
+ *   H         multiple of 64, at most 2^20;  0 <= r <= 64;  B 1..64
  *   logits    fp32 [batch*(2B+1)][V] or NULL: where the logits are written (rows 0..batch(B+1)-1
  *             the AR rows request-major, then the draft rows); NULL keeps them in the workspace
  *             (size from psispec_lmhead_verify_workspace with logits_in_workspace = 1)

@@ -429,7 +429,7 @@ namespace {
 
 struct LMPlan {
   Plan pl;
-  size_t off_logits, off_taug, off_baug, total;
+  size_t off_logits, off_aaug, off_baug, total;
   int ntiles, mtiles, kx;
 };
 
@@ -443,12 +443,11 @@ LMPlan make_lm_plan(int batch, int B, int H, int V, int r, bool own_logits) {
   lp.off_logits = off;
   if (own_logits) off = align_up(off + sizeof(float) * (size_t)M * (size_t)V);
   lp.kx = r > 0 ? (2 * r + 63) / 64 * 64 : 0;
-  lp.off_taug = off;
-  off = align_up(off + sizeof(uint16_t) * (size_t)M * (size_t)lp.kx);
+  lp.off_aaug = off;
+  off = align_up(off + sizeof(uint16_t) * (size_t)M * (size_t)(H + lp.kx));
   lp.off_baug = off;
   off = align_up(off + sizeof(uint16_t) * (size_t)V * (size_t)lp.kx);
   lp.total = off + kAlign;
-  (void)H;
   return lp;
 }
 
@@ -458,7 +457,8 @@ extern "C" {
 
 size_t psispec_lmhead_verify_workspace(int32_t batch, int32_t B, int32_t H, int32_t V, int32_t r,
                                        int32_t logits_in_workspace) {
-  if (batch < 0 || B < 1 || B > 64 || V < 1 || H < 64 || H % 64 || r < 0 || r > 64) return 0;
+  if (batch < 0 || B < 1 || B > 64 || V < 1 || H < 64 || H % 64 || H > (1 << 20) || r < 0 || r > 64)
+    return 0;
   return make_lm_plan(batch, B, H, V, r, logits_in_workspace != 0).total;
 }
 
@@ -469,7 +469,7 @@ psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, cons
                                      int32_t* accept_len, int32_t* out_tokens, float* ratios,
                                      uint64_t* accept_mask, int32_t* status, float* logits,
                                      void* workspace, size_t workspace_bytes, void* stream_ptr) {
-  if (batch < 0 || B < 1 || B > 64 || V < 1 || H < 64 || H % 64 || r < 0 || r > 64)
+  if (batch < 0 || B < 1 || B > 64 || V < 1 || H < 64 || H % 64 || H > (1 << 20) || r < 0 || r > 64)
     return PSISPEC_EINVAL;
   if (!sampling_ok(s) || !isfinite(lora_scale)) return PSISPEC_EINVAL;
   if (batch == 0) return PSISPEC_OK;
@@ -496,7 +496,7 @@ psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, cons
   ha.w_t = static_cast<const uint16_t*>(w_t);
   ha.lora_at = static_cast<const uint16_t*>(lora_a_t);
   ha.lora_bt = static_cast<const uint16_t*>(lora_b_t);
-  ha.taug = carve<uint16_t>(workspace, lp.off_taug);
+  ha.aaug = carve<uint16_t>(workspace, lp.off_aaug);
   ha.baug = carve<uint16_t>(workspace, lp.off_baug);
   ha.kx = lp.kx;
   ha.lora_scale = lora_scale;

@@ -97,7 +97,7 @@ struct LMHeadArgs {
   const uint16_t* w_t;      // bf16 [N][K]
   const uint16_t* lora_at;  // bf16 [r][K] or null
   const uint16_t* lora_bt;  // bf16 [N][r] or null
-  uint16_t* taug;           // bf16 [M][kx] scratch: zeros (AR rows), [t_hi | t_lo | 0] (draft rows)
+  uint16_t* aaug;           // bf16 [M][K+kx] scratch: h row, then zeros (AR) / [t_hi | t_lo | 0] (draft)
   uint16_t* baug;           // bf16 [N][kx] scratch: [B_t | B_t | 0]
   float lora_scale;
   int nP, nQ, M, N, K, r;

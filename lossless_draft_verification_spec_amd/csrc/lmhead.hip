@@ -28,34 +28,41 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LROW = BK + 8;  // bf16 elements per LDS row (16-byte pad: conflict-free 16-byte reads)
-constexpr int A_STAGE = BM * LROW, B_STAGE = BN * LROW;
+constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
+constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per LDS stage: A tile then B tile (32 KB)
+constexpr int kDma = BM * BK * 2 / 1024 / 4;  // 1 KB direct-to-LDS blocks per wave per operand
 constexpr int kXcd = 8;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer resource: 32-bit data, no swizzle
 
 __device__ inline uint16_t bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// Extra contraction columns of row m (grid over all M rows): zeros for the AR rows (m < nP); for
-// draft row i = m - nP, t_j = s sum_h h_dr[i][h] A_t[j][h] (fp64 sum) stored as bf16 t_hi (columns
-// 0..r-1) and t_lo = t - t_hi (columns r..2r-1), zero up to kx.
-__global__ __launch_bounds__(kThreads) void k_lora_aug_rows(const uint16_t* __restrict__ hd,
-                                                            const uint16_t* __restrict__ at, int nP,
-                                                            int K, int r, int kx, float scale,
-                                                            uint16_t* __restrict__ taug) {
+// Row m of the augmented A operand (grid over all M rows), KX = K + kx columns: the hidden state
+// (h_ar row m for m < nP, h_dr row m - nP after), then the extra contraction columns: zeros for the
+// AR rows; for draft row i = m - nP, t_j = s sum_h h_dr[i][h] A_t[j][h] (fp64 sum) stored as bf16
+// t_hi (columns K..K+r-1) and t_lo = t - t_hi (columns K+r..K+2r-1), zero up to KX.
+__global__ __launch_bounds__(kThreads) void k_build_a(const uint16_t* __restrict__ har,
+                                                      const uint16_t* __restrict__ hd,
+                                                      const uint16_t* __restrict__ at, int nP,
+                                                      int K, int r, int kx, float scale,
+                                                      uint16_t* __restrict__ aaug) {
   const int m = blockIdx.x;
-  uint16_t* out = taug + (int64_t)m * kx;
+  const int KX = K + kx;
+  uint16_t* row = aaug + (int64_t)m * KX;
+  const uint16_t* x = m < nP ? har + (int64_t)m * K : hd + (int64_t)(m - nP) * K;
+  const int nc = K >> 3;  // K is a multiple of 64: whole 16-byte chunks
+  for (int c = threadIdx.x; c < nc; c += kThreads)
+    *reinterpret_cast<u32x4*>(row + 8 * c) = *reinterpret_cast<const u32x4*>(x + 8 * c);
+  uint16_t* out = row + K;
   if (m < nP) {
     for (int j = threadIdx.x; j < kx; j += kThreads) out[j] = 0;
     return;
   }
-  const uint16_t* x = hd + (int64_t)(m - nP) * K;
   for (int j = threadIdx.x + 2 * r; j < kx; j += kThreads) out[j] = 0;
-  // all ranks in one pass over h: each thread owns 8-element chunks of h (K is a multiple of 64)
-  // and keeps up to 16 fp64 partial sums per round
-  const int nc = K >> 3;
+  // all ranks in one pass over h: each thread owns 8-element chunks of h and keeps up to 16 fp64
+  // partial sums per round
   for (int j0 = 0; j0 < r; j0 += 16) {
     const int nj = min(16, r - j0);
     double acc[16];
@@ -130,8 +137,14 @@ __global__ __launch_bounds__(kThreads) void k_lora_aug_cols(const uint16_t* __re
   *reinterpret_cast<u32x4*>(baug + (int64_t)n * kx + j0) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory operations are in
+// flight, leaving the LDS and export counters unconstrained.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(LMHeadArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (A_STAGE + B_STAGE)];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NSTAGE * STAGE];
   // XCD-aware tile order: workgroup ids are dealt round-robin to the 8 XCDs; give each XCD a
   // contiguous range of tiles, M tiles fastest, so the XCD's workgroups share W column blocks.
   const int ntile = a.mtiles * a.ntiles;
@@ -140,57 +153,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(LMHeadArgs a) {
   if (tile >= ntile) return;
   const int tm = tile % a.mtiles, tn = tile / a.mtiles;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: LDS bases go to M0
   const int wm = wave >> 1, wn = wave & 1;
   const int K = a.K;
 
-  // global -> register staging: 8 A and 8 B 16-byte chunks per thread per K step; rows past the
-  // end are clamped (loaded, never stored).  Steps past K read the LoRA columns (kx of them): row m
-  // of taug (zeros for the AR rows) and row n of baug.  Row pointers are fixed per thread, so the
-  // loop only adds the step offset (kt is uniform: the two phases are a scalar branch).
-  const uint16_t* pa[8];
-  const uint16_t* pb[8];
-  int ma[8], nb[8];
-  const int kc = (t & 7) * 8;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ma[i] = min(m0 + (t >> 3) + 32 * i, a.M - 1);
-    nb[i] = min(n0 + (t >> 3) + 32 * i, a.N - 1);
-    pa[i] = (ma[i] < a.nP ? a.h_ar + (int64_t)ma[i] * K : a.h_dr + (int64_t)(ma[i] - a.nP) * K) + kc;
-    pb[i] = a.w_t + (int64_t)nb[i] * K + kc;
-  }
+  // Operands stream HBM -> LDS with 16-byte direct-to-LDS buffer loads, NSTAGE-1 K steps ahead of
+  // the MFMAs.  Each load instruction fills one 1 KB block: 16 rows of 32 bf16, lane l writing row
+  // l/4, 16-byte slot l%4.  Slot s of row r holds the row's K chunk s ^ f(r), f(r) = r2 | (r1^r3)<<1
+  // (r_k = bit k of r): the 16-byte fragment reads then hit distinct banks both within each group
+  // of 8 rows on 32 banks and within each group of 16 rows on 64 banks.  The buffer resources
+  // cover only this tile's valid rows: rows past M or N, and the steps past the end (a zero-length
+  // resource), land as zeros.  A is the augmented [M][K + kx] matrix; B is W_t for the first K/32
+  // steps and the augmented LoRA columns [N][kx] after.
+  const int KX = K + a.kx;
+  const int rows_a = min(BM, a.M - m0), rows_b = min(BN, a.N - n0);
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.aaug + (int64_t)m0 * KX), (short)0, rows_a * KX * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.w_t + (int64_t)n0 * K), (short)0, rows_b * K * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.baug + (int64_t)n0 * a.kx), (short)0, rows_b * a.kx * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_0 =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.w_t, (short)0, 0, kRsrcWord3);
+  const int drow = wave * kDma * 16 + (lane >> 2);  // + 16 i
+  const int gch = (lane & 3) ^ (((lane >> 4) & 1) | ((((lane >> 3) ^ (lane >> 5)) & 1) << 1));
+  const int va = drow * KX * 2 + 16 * gch;
+  const int vw = drow * K * 2 + 16 * gch;
+  const int vx = drow * a.kx * 2 + 16 * gch;
   const int KT = K / BK, KTX = KT + a.kx / BK;
-  u32x4 ra[8], rb[8];
-  auto gload = [&](int kt) {
-    if (kt < KT) {
-      const int ko = kt * BK;
+  auto dma = [&](int kt) {
+    uint16_t* As = smem + (kt % NSTAGE) * STAGE + wave * kDma * 512;
+    uint16_t* Bs = As + BM * BK;
+    const bool live = kt < KTX, main = kt < KT;
+    const __amdgpu_buffer_rsrc_t ra = live ? rs_a : rs_0;
+    const __amdgpu_buffer_rsrc_t rb = live ? (main ? rs_w : rs_x) : rs_0;
+    const int oa = va + kt * (BK * 2);
+    const int ob = main ? vw + kt * (BK * 2) : vx + (kt - KT) * (BK * 2);
+    const int sa = 16 * KX * 2, sb = 16 * (main ? K : a.kx) * 2;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + ko);
-        rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + ko);
-      }
-    } else {
-      const int ko = (kt - KT) * BK + kc;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ra[i] = *reinterpret_cast<const u32x4*>(a.taug + (int64_t)ma[i] * a.kx + ko);
-        rb[i] = *reinterpret_cast<const u32x4*>(a.baug + (int64_t)nb[i] * a.kx + ko);
-      }
+    for (int i = 0; i < kDma; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(As + i * 512), 16, oa + i * sa, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(Bs + i * 512), 16, ob + i * sb, 0, 0, 0);
     }
   };
-  const int lofs = (t >> 3) * LROW + kc;  // + 32*i*LROW
-  auto lstore = [&](int buf) {
-    uint16_t* As = smem + buf * (A_STAGE + B_STAGE);
-    uint16_t* Bs = As + A_STAGE;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<u32x4*>(As + lofs + 32 * i * LROW) = ra[i];
-      *reinterpret_cast<u32x4*>(Bs + lofs + 32 * i * LROW) = rb[i];
-    }
-  };
-  gload(0);
-  lstore(0);
-  __syncthreads();
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -200,40 +206,65 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(LMHeadArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int frag = (lane & 31) * LROW + 8 * (lane >> 5);
-  for (int kt = 0; kt < KTX; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KTX) gload(kt + 1);
-    const uint16_t* As = smem + buf * (A_STAGE + B_STAGE) + (wm * 128) * LROW + frag;
-    const uint16_t* Bs = smem + buf * (A_STAGE + B_STAGE) + A_STAGE + (wn * 128) * LROW + frag;
-    // fragments of substep ks+1 are read from LDS while the 16 MFMAs of substep ks run
-    bf16x8 fa[2][4], fb[2][4];
+  // fragment of MFMA row/column l%32, K chunk 2 ks + l/32 (8 bf16), through the slot swizzle
+  const int xr = ((lane >> 2) & 1) | ((((lane >> 1) ^ (lane >> 3)) & 1) << 1);
+  const int fofs0 = (lane & 31) * BK + 8 * ((lane >> 5) ^ xr);
+  const int fofs1 = (lane & 31) * BK + 8 * ((2 + (lane >> 5)) ^ xr);
+  bf16x8 fa[2][4], fb[2][4];
+  auto fread = [&](int kt, int ks, bf16x8(&ra)[4], bf16x8(&rb)[4]) {
+    const uint16_t* As = smem + (kt % NSTAGE) * STAGE + (wm * 128) * BK + (ks ? fofs1 : fofs0);
+    const uint16_t* Bs = As + BM * BK + (wn - wm) * 128 * BK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      fa[0][i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * LROW);
-      fb[0][i] = *reinterpret_cast<const bf16x8*>(Bs + i * 32 * LROW);
+      ra[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * BK);
+      rb[i] = *reinterpret_cast<const bf16x8*>(Bs + i * 32 * BK);
+    }
+  };
+  auto mfma16 = [&](const bf16x8(&ra)[4], const bf16x8(&rb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i], rb[j], acc[i][j], 0, 0, 0);
+  };
+
+#pragma unroll
+  for (int k = 0; k < NSTAGE - 1; ++k) dma(k);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSTAGE - 2) * 2 * kDma));  // step 0 landed
+  __builtin_amdgcn_s_barrier();
+  fread(0, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < KTX; ++kt) {
+    // One barrier per step.  Past it, step kt+1 has landed for every wave (each waited for its own
+    // loads of it) and every wave is done with step kt-1, whose stage the loads of step
+    // kt+NSTAGE-1 then overwrite.  Everything else in the step is free to overlap the MFMAs.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSTAGE - 3) * 2 * kDma));
+    __builtin_amdgcn_s_barrier();
+    fread(kt, 1, fa[1], fb[1]);
+    dma(kt + NSTAGE - 1);
+    mfma16(fa[0], fb[0]);
+    fread(kt + 1, 0, fa[0], fb[0]);
+    mfma16(fa[1], fb[1]);
+    // issue order: one fragment read after each of the first 8 MFMAs, one DMA load after each of
+    // the next 8, then the reads of step kt+1 between the first 8 MFMAs of substep 1
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < BK / 16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          fa[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * LROW + (ks + 1) * 16);
-          fb[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(Bs + i * 32 * LROW + (ks + 1) * 16);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the reads of ks+1 ahead of the MFMAs of ks
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (direct-to-LDS)
     }
-    if (kt + 1 < KTX) lstore(buf ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the zero-filling tail loads also write LDS
+  __syncthreads();
 
   // ---- epilogue -------------------------------------------------------------------------------
   // Element (i, j, v) of this lane sits at row m0 + wm*128 + i*32 + 8*(v/4) + 4*(lane/32) + v%4,
@@ -300,14 +331,16 @@ int lmhead_tile_n() { return BN; }
 
 hipError_t launch_lmhead(const LMHeadArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
+  timing_begin("build_a", stream);
+  hipLaunchKernelGGL(k_build_a, dim3((unsigned)a.M), dim3(kThreads), 0, stream, a.h_ar, a.h_dr,
+                     a.lora_at, a.nP, a.K, a.r, a.kx, a.lora_scale, a.aaug);
   if (a.kx > 0) {
-    timing_begin("lora_aug", stream);
-    hipLaunchKernelGGL(k_lora_aug_rows, dim3((unsigned)a.M), dim3(kThreads), 0, stream, a.h_dr,
-                       a.lora_at, a.nP, a.K, a.r, a.kx, a.lora_scale, a.taug);
     const int64_t n = (int64_t)a.N * (a.kx >> 3);
     hipLaunchKernelGGL(k_lora_aug_cols, dim3((unsigned)((n + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, stream, a.lora_bt, a.N, a.r, a.kx, a.baug);
-    timing_end("lora_aug", stream);
+  }
+  timing_end("build_a", stream);
+  {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
