@@ -45,11 +45,8 @@ Plan make_plan(int64_t rows, int batch, int V, size_t es, int excl_stride, int f
     pl.chunk_elems = 0;
   }
   pl.nsub = (V + kSub - 1) / kSub;
-  int nd = batch > 0 ? (2048 + batch - 1) / batch : 1;
-  if (nd > pl.nsub) nd = pl.nsub;
-  if (nd < 1) nd = 1;
-  const int sub_per = (pl.nsub + nd - 1) / nd;
-  pl.chunk_elems_draw = sub_per * kSub;
+  // draw pass: one 1024-token sub-chunk per wave of a block
+  pl.chunk_elems_draw = (kThreads / 64) * kSub;
   pl.nchunk_draw = (V + pl.chunk_elems_draw - 1) / pl.chunk_elems_draw;
   size_t off = 0;
   pl.off_part = off;

@@ -1,0 +1,121 @@
+// rows.h -- device code of the HBM row pass, shared by the row-pass kernel and the fused verify.
+//
+// A workgroup streams one chunk of one row with 16-byte loads and keeps an online
+// (max, sum of exp) pair per lane; the pair of each (row, chunk) goes to the workspace and is
+// combined in a fixed order by the consumers, so results do not depend on scheduling.
+#pragma once
+
+#include "internal.h"
+
+namespace psispec {
+namespace {
+
+template <typename T>
+struct Elems;
+template <>
+struct Elems<bf16_t> {
+  static constexpr int kPerVec = 8;
+  __device__ static void unpack(const u32x4& v, float (&f)[8]) {
+    f[0] = __uint_as_float(v.x << 16);
+    f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16);
+    f[3] = __uint_as_float(v.y & 0xffff0000u);
+    f[4] = __uint_as_float(v.z << 16);
+    f[5] = __uint_as_float(v.z & 0xffff0000u);
+    f[6] = __uint_as_float(v.w << 16);
+    f[7] = __uint_as_float(v.w & 0xffff0000u);
+  }
+};
+template <>
+struct Elems<float> {
+  static constexpr int kPerVec = 4;
+  __device__ static void unpack(const u32x4& v, float (&f)[4]) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+};
+
+// Fold n values into the online pair (m, s), s = sum exp2((x - m) * c).  m starts at a finite floor
+// so that -inf entries contribute exp2(-inf) = 0 and NaN/+inf entries turn s into NaN.
+template <int n>
+__device__ inline void fold(const float (&f)[n], float& m, float& s, float c) {
+  float vm = f[0];
+#pragma unroll
+  for (int j = 1; j < n; ++j) vm = fmaxf(vm, f[j]);
+  if (vm > m) {
+    s *= __builtin_amdgcn_exp2f((m - vm) * c);
+    m = vm;
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < n; ++j) acc += __builtin_amdgcn_exp2f((f[j] - m) * c);
+  s += acc;
+}
+
+__device__ inline void block_reduce_pair(float& m, float& s, float c) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, 64);
+    const float s2 = __shfl_xor(s, off, 64);
+    os_combine(m, s, m2, s2, c);
+  }
+  __shared__ float sm[kThreads / 64], ss[kThreads / 64];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm[wave] = m;
+    ss[wave] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = sm[0];
+    s = ss[0];
+    for (int w = 1; w < kThreads / 64; ++w) os_combine(m, s, sm[w], ss[w], c);
+  }
+}
+
+// One chunk of one row: the block's online pair (max, sum exp2((x - max) c)) over logits
+// [chunk * chunk_elems, min(V, (chunk + 1) * chunk_elems)), written by thread 0 to *out.  Called by
+// every thread of a kThreads block (it contains block barriers).
+template <typename T, int kUnroll>
+__device__ inline void rowstats_task(const RowSet& rs, int64_t row, int chunk, int chunk_elems,
+                                     float c, float2* out, int vec_ok) {
+  const T* rp = row_ptr<T>(rs, row);
+  const int start = chunk * chunk_elems;
+  const int end = min(rs.V, start + chunk_elems);
+  float m = kNegBig, s = 0.f;
+  int tail = start;
+  if (vec_ok) {
+    constexpr int E = Elems<T>::kPerVec;
+    const int nvec = (end - start) / E;
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rp + start);
+    int i = threadIdx.x;
+    for (; i + (kUnroll - 1) * kThreads < nvec; i += kUnroll * kThreads) {
+      u32x4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(vp + i + u * kThreads);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float f[E];
+        Elems<T>::unpack(v[u], f);
+        fold(f, m, s, c);
+      }
+    }
+    for (; i < nvec; i += kThreads) {
+      float f[E];
+      Elems<T>::unpack(vp[i], f);
+      fold(f, m, s, c);
+    }
+    tail = start + nvec * E;
+  }
+  for (int x = tail + threadIdx.x; x < end; x += kThreads) {
+    const float f[1] = {to_f32(rp[x])};
+    fold(f, m, s, c);
+  }
+  block_reduce_pair(m, s, c);
+  if (threadIdx.x == 0) *out = make_float2(m, s);
+}
+
+}  // namespace
+}  // namespace psispec

@@ -7,74 +7,10 @@
 // (max, sum of exp) pair per lane; the pair of each (row, chunk) goes to the workspace and is
 // combined in a fixed order by the consumers, so results do not depend on scheduling.
 #include "launch.h"
+#include "rows.h"
 
 namespace psispec {
 namespace {
-
-template <typename T>
-struct Elems;
-template <>
-struct Elems<bf16_t> {
-  static constexpr int kPerVec = 8;
-  __device__ static void unpack(const u32x4& v, float (&f)[8]) {
-    f[0] = __uint_as_float(v.x << 16);
-    f[1] = __uint_as_float(v.x & 0xffff0000u);
-    f[2] = __uint_as_float(v.y << 16);
-    f[3] = __uint_as_float(v.y & 0xffff0000u);
-    f[4] = __uint_as_float(v.z << 16);
-    f[5] = __uint_as_float(v.z & 0xffff0000u);
-    f[6] = __uint_as_float(v.w << 16);
-    f[7] = __uint_as_float(v.w & 0xffff0000u);
-  }
-};
-template <>
-struct Elems<float> {
-  static constexpr int kPerVec = 4;
-  __device__ static void unpack(const u32x4& v, float (&f)[4]) {
-    f[0] = __uint_as_float(v.x);
-    f[1] = __uint_as_float(v.y);
-    f[2] = __uint_as_float(v.z);
-    f[3] = __uint_as_float(v.w);
-  }
-};
-
-// Fold n values into the online pair (m, s), s = sum exp2((x - m) * c).  m starts at a finite floor
-// so that -inf entries contribute exp2(-inf) = 0 and NaN/+inf entries turn s into NaN.
-template <int n>
-__device__ inline void fold(const float (&f)[n], float& m, float& s, float c) {
-  float vm = f[0];
-#pragma unroll
-  for (int j = 1; j < n; ++j) vm = fmaxf(vm, f[j]);
-  if (vm > m) {
-    s *= __builtin_amdgcn_exp2f((m - vm) * c);
-    m = vm;
-  }
-  float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < n; ++j) acc += __builtin_amdgcn_exp2f((f[j] - m) * c);
-  s += acc;
-}
-
-__device__ inline void block_reduce_pair(float& m, float& s, float c) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float m2 = __shfl_xor(m, off, 64);
-    const float s2 = __shfl_xor(s, off, 64);
-    os_combine(m, s, m2, s2, c);
-  }
-  __shared__ float sm[kThreads / 64], ss[kThreads / 64];
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    sm[wave] = m;
-    ss[wave] = s;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    m = sm[0];
-    s = ss[0];
-    for (int w = 1; w < kThreads / 64; ++w) os_combine(m, s, sm[w], ss[w], c);
-  }
-}
 
 template <typename T, int kUnroll>
 __global__ __launch_bounds__(kThreads) void k_rowstats(RowSet rs, int nchunk, int chunk_elems,
@@ -84,40 +20,7 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(RowSet rs, int nchunk, in
   const int64_t row = task / nchunk;
   const int chunk = (int)(task - row * nchunk);
   if (row_skipped(rs, row)) return;
-  const T* rp = row_ptr<T>(rs, row);
-  const int start = chunk * chunk_elems;
-  const int end = min(rs.V, start + chunk_elems);
-  float m = kNegBig, s = 0.f;
-  int tail = start;
-  if (vec_ok) {
-    constexpr int E = Elems<T>::kPerVec;
-    const int nvec = (end - start) / E;
-    const u32x4* vp = reinterpret_cast<const u32x4*>(rp + start);
-    int i = threadIdx.x;
-    for (; i + (kUnroll - 1) * kThreads < nvec; i += kUnroll * kThreads) {
-      u32x4 v[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(vp + i + u * kThreads);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        float f[E];
-        Elems<T>::unpack(v[u], f);
-        fold(f, m, s, c);
-      }
-    }
-    for (; i < nvec; i += kThreads) {
-      float f[E];
-      Elems<T>::unpack(vp[i], f);
-      fold(f, m, s, c);
-    }
-    tail = start + nvec * E;
-  }
-  for (int x = tail + threadIdx.x; x < end; x += kThreads) {
-    const float f[1] = {to_f32(rp[x])};
-    fold(f, m, s, c);
-  }
-  block_reduce_pair(m, s, c);
-  if (threadIdx.x == 0) part[task] = make_float2(m, s);
+  rowstats_task<T, kUnroll>(rs, row, chunk, chunk_elems, c, part + task, vec_ok);
 }
 
 // ---------------------------------------------------------------------------------------------
