@@ -29,12 +29,13 @@ struct Plan {
   size_t total;
 };
 
-// Row split of the HBM pass: chunks of about 32 KiB so that even a few hundred rows give
-// thousands of workgroups; chunk starts stay 16-byte aligned (multiples of 64 elements).
+// Row split of the HBM pass: chunks of about 64 KiB (a workgroup keeps 32 KiB of 16-byte loads in
+// flight, two rounds per chunk), still thousands of workgroups for a few hundred rows; chunk
+// starts stay 16-byte aligned (multiples of 64 elements).
 Plan make_plan(int64_t rows, int batch, int V, size_t es, int excl_stride, int fixed_nchunk = 0) {
   Plan pl{};
   const size_t row_bytes = (size_t)V * es;
-  int nchunk = (int)((row_bytes + 32767) / 32768);
+  int nchunk = (int)((row_bytes + 65535) / 65536);
   if (nchunk < 1) nchunk = 1;
   int ce = (V + nchunk - 1) / nchunk;
   ce = (ce + 63) / 64 * 64;

@@ -123,10 +123,10 @@ hipError_t launch_rowstats(const RowSet& rs, psispec_dtype dtype, int nchunk, in
                      ((uintptr_t)rs.q % 16) == 0 && (chunk_elems % 8) == 0;
   timing_begin("rowstats", stream);
   if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL((k_rowstats<bf16_t, 4>), dim3((unsigned)tasks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((k_rowstats<bf16_t, 8>), dim3((unsigned)tasks), dim3(kThreads), 0, stream,
                        rs, nchunk, chunk_elems, c, part, vec_ok);
   else
-    hipLaunchKernelGGL((k_rowstats<float, 4>), dim3((unsigned)tasks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((k_rowstats<float, 8>), dim3((unsigned)tasks), dim3(kThreads), 0, stream,
                        rs, nchunk, chunk_elems, c, part, vec_ok);
   timing_end("rowstats", stream);
   return hipGetLastError();
