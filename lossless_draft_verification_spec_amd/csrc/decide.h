@@ -7,6 +7,7 @@ namespace psispec {
 namespace {
 
 constexpr int kMaxB = 64;
+constexpr int kStageChunks = 16;  // row pairs per row staged in LDS (more: the wave-reduce path)
 
 __device__ inline int row_status(float lmax, double Z) {
   const bool ok = (lmax > kNegBig) && (lmax < __builtin_huge_valf()) && (Z > 0.0) && (Z < 1e300);
@@ -26,12 +27,20 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
   __shared__ float s_lmax[2 * kMaxB + 1];
   __shared__ double s_Z[2 * kMaxB + 1];
   __shared__ int s_st[2 * kMaxB + 1];
+  __shared__ float2 s_pair[(2 * kMaxB + 1) * kStageChunks];
 
   // 1. finish the row statistics (rows 0..B of p, then rows 0..B-1 of q).  Few chunks: one lane
   //    per row; many (LM-head column tiles): the wave reduces each row's chunks in a fixed order.
   if (t >= 64) {
     // other waves of a larger block only join the barrier
-  } else if (a.nchunk <= 16) {
+  } else if (a.nchunk <= kStageChunks) {
+    // the request's pairs: p rows then q rows, each a contiguous run of the workspace, loaded by
+    // the whole wave in one round
+    const int np = Bp1 * a.nchunk, nq = B * a.nchunk;
+    for (int i = t; i < np + nq; i += 64)
+      s_pair[i] = i < np ? a.part[prow0 * a.nchunk + i] : a.part[qrow0 * a.nchunk + (i - np)];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     for (int j = t; j < 2 * B + 1; j += 64) {
       const int64_t row = j <= B ? prow0 + j : qrow0 + (j - Bp1);
       if (j > B && first_from_target && j == Bp1) {
@@ -40,11 +49,12 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
         s_st[j] = 0;
         continue;
       }
+      const float2* pr = s_pair + j * a.nchunk;
       float lmax = kNegBig;
-      for (int k = 0; k < a.nchunk; ++k) lmax = fmaxf(lmax, a.part[row * a.nchunk + k].x);
+      for (int k = 0; k < a.nchunk; ++k) lmax = fmaxf(lmax, pr[k].x);
       double Z = 0.0;
       for (int k = 0; k < a.nchunk; ++k) {
-        const float2 pk = a.part[row * a.nchunk + k];
+        const float2 pk = pr[k];
         Z += (double)pk.y * exp2((double)(pk.x - lmax) * (double)a.c);
       }
       const int st = row_status(lmax, Z);

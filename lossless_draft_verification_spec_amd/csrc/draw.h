@@ -79,6 +79,8 @@ __device__ inline double term(float l, float lmax, float thr, double inv_T, cons
 }
 
 constexpr double kBand = 1e-5;  // relative band of uncertain residual signs
+constexpr int kEsLds = 512;     // chunk normaliser pairs staged in LDS by the select
+constexpr int kMassLds = 2048;  // sub-chunk masses kept in LDS by the select (V <= 2M tokens)
 
 __device__ inline bool excluded(int x, const int* excl, int nexcl) {
   for (int i = 0; i < nexcl; ++i)
@@ -269,6 +271,8 @@ __device__ inline void draw_select_request(const DrawArgs& a, int r) {
   __shared__ int s_last[kThreads / 64];
   __shared__ int s_sub, s_flagged, s_list[1024];
   __shared__ double s_base;
+  __shared__ double2 s_es[kEsLds];
+  __shared__ double s_mass[kMassLds];
   exp_table_fill(tbl);
   const DrawDesc d = a.desc[r];
   if (d.out_idx < 0) {
@@ -287,9 +291,16 @@ __device__ inline void draw_select_request(const DrawArgs& a, int r) {
   double rEp = 1.0, rEq = 0.0, rho = 0.0;
   bool band_ok = true;
   if (has_q) {
+    // the chunks' partial normalisers, loaded in parallel and summed in chunk order
+    const double2* es = a.esum + (int64_t)r * a.nchunk_draw;
+    const bool in_lds = a.nchunk_draw <= kEsLds;
+    if (in_lds) {
+      for (int k = threadIdx.x; k < a.nchunk_draw; k += kThreads) s_es[k] = es[k];
+      __syncthreads();
+    }
     double Ep = 0.0, Eq = 0.0;
     for (int k = 0; k < a.nchunk_draw; ++k) {
-      const double2 e = a.esum[(int64_t)r * a.nchunk_draw + k];
+      const double2 e = in_lds ? s_es[k] : es[k];
       Ep += e.x;
       Eq += e.y;
     }
@@ -299,7 +310,8 @@ __device__ inline void draw_select_request(const DrawArgs& a, int r) {
     band_ok = fabs(rho / rho_estimate(a, d) - 1.0) <= 0.25 * kBand;
   }
   const int mode = has_q ? 0 : 1;
-  double* mass = a.subsum + (int64_t)r * a.nsub;
+  // sub-chunk masses: in LDS up to kMassLds sub-chunks, else in the workspace
+  double* mass = a.nsub <= kMassLds ? s_mass : a.subsum + (int64_t)r * a.nsub;
   const double2* suba = a.suba + (int64_t)r * a.nsub;
   const int32_t* subn = a.subn + (int64_t)r * a.nsub;
   __syncthreads();
