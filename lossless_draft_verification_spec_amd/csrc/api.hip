@@ -435,7 +435,7 @@ LMPlan make_lm_plan(int batch, int B, int H, int V, int r, bool own_logits) {
   LMPlan lp{};
   const int nP = batch * (B + 1), nQ = batch * B, M = nP + nQ;
   lp.ntiles = (V + lmhead_tile_n() - 1) / lmhead_tile_n();
-  lp.mtiles = (M + 255) / 256;
+  lp.mtiles = (M + lmhead_tile_m() - 1) / lmhead_tile_m();
   lp.pl = make_plan((int64_t)M, batch, V, 4, 0, lp.ntiles);
   size_t off = lp.pl.total;
   lp.off_logits = off;

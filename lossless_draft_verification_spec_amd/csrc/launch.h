@@ -108,6 +108,7 @@ struct LMHeadArgs {
   float2* part;             // [M][ntiles] online (max, sum exp) pairs
 };
 int lmhead_tile_n();
+int lmhead_tile_m();
 hipError_t launch_lmhead(const LMHeadArgs& a, hipStream_t stream);
 
 }  // namespace psispec

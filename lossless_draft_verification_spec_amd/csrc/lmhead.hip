@@ -269,8 +269,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(LMHeadArgs a) {
   // ---- epilogue -------------------------------------------------------------------------------
   // Element (i, j, v) of this lane sits at row m0 + wm*128 + i*32 + 8*(v/4) + 4*(lane/32) + v%4,
   // column n0 + wn*128 + j*32 + lane%32.  One 64-row slice (i fixed) at a time goes through LDS:
-  // then 4 threads per row store 64 columns each with 16-byte writes and fold them into the row's
-  // online pair (max, sum exp) for this column tile.
+  // then 4 threads per row store 64 columns each with 16-byte writes and reduce them to the
+  // segment's (max, sum exp2((x - max) c)), combined over the row's 4 segments.
   constexpr int SROW = BN + 4;
   float* S = reinterpret_cast<float*>(smem);  // [64][SROW]
   const float c = a.c;
@@ -287,31 +287,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(LMHeadArgs a) {
     __syncthreads();
     const int m = m0 + (lr < 32 ? i * 32 + lr : 128 + i * 32 + (lr - 32));
     const int nbase = n0 + qq * 64;
+    const int nvalid = a.N - nbase;  // columns of this segment inside the row (may be <= 0)
     const float* src = S + lr * SROW + qq * 64;
-    float mx = kNegBig, sm = 0.f;
     float4 buf[16];
 #pragma unroll
+    for (int k = 0; k < 16; ++k) buf[k] = *reinterpret_cast<const float4*>(src + 4 * k);
+    float mx = kNegBig;  // finite floor: a segment past the row's end gives (floor, 0)
+#pragma unroll
     for (int k = 0; k < 16; ++k) {
-      buf[k] = *reinterpret_cast<const float4*>(src + 4 * k);
       const float x[4] = {buf[k].x, buf[k].y, buf[k].z, buf[k].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float xv = (nbase + 4 * k + e < a.N) ? x[e] : -__builtin_huge_valf();
-        if (xv > mx) {
-          sm *= exp2f((mx - xv) * c);
-          mx = xv;
-        }
-        sm += exp2f((xv - mx) * c);
-      }
+      for (int e = 0; e < 4; ++e)
+        if (4 * k + e < nvalid) mx = fmaxf(mx, x[e]);
+    }
+    float sm = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float x[4] = {buf[k].x, buf[k].y, buf[k].z, buf[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * k + e < nvalid) sm += __builtin_amdgcn_exp2f((x[e] - mx) * c);
     }
     if (m < a.M) {
       float* dst = a.logits + (int64_t)m * a.N + nbase;
-      if (nbase + 64 <= a.N && (a.N & 3) == 0) {
+      if (nvalid >= 64 && (a.N & 3) == 0) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) *reinterpret_cast<float4*>(dst + 4 * k) = buf[k];
       } else {
-        for (int k = 0; k < 64; ++k)
-          if (nbase + k < a.N) dst[k] = src[k];
+        for (int k = 0; k < min(64, nvalid); ++k) dst[k] = src[k];
       }
     }
 #pragma unroll
@@ -328,6 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(LMHeadArgs a) {
 }  // namespace
 
 int lmhead_tile_n() { return BN; }
+int lmhead_tile_m() { return BM; }
 
 hipError_t launch_lmhead(const LMHeadArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
