@@ -516,8 +516,11 @@ psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, cons
   RowStat* rowstat = carve<RowStat>(workspace, pl.off_rowstat);
   ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
   DrawDesc* desc = carve<DrawDesc>(workspace, pl.off_desc);
-  if (use_topp &&
-      launch_topp(rs, PSISPEC_F32, pl.nchunk, c, s->top_p, part, topp, stream) != hipSuccess)
+  // one pair per column tile: combine every row's pairs once, one wave per row
+  if (launch_combine_rows(rs, part, pl.nchunk, c, rowstat, stream) != hipSuccess)
+    return PSISPEC_EHIP;
+  if (use_topp && launch_topp(rs, PSISPEC_F32, pl.nchunk, c, s->top_p, part, topp, stream,
+                              rowstat) != hipSuccess)
     return PSISPEC_EHIP;
   LinearArgs la{};
   la.rs = rs;
@@ -536,6 +539,7 @@ psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, cons
   la.part = part;
   la.topp = topp;
   la.rowstat = rowstat;
+  la.rowstat_ready = 1;
   la.desc = desc;
   la.ucount = carve<int32_t>(workspace, pl.off_ucount);
   la.accept_len = accept_len;

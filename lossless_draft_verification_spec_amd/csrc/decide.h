@@ -14,6 +14,22 @@ __device__ inline int row_status(float lmax, double Z) {
   return ok ? 0 : PSISPEC_ST_NONFINITE;
 }
 
+// Statistics of one row from its per-chunk pairs, reduced by one wave64 in a fixed order: lane l
+// takes chunks l, l+64, ...; then a butterfly.  Every lane returns the row's (lmax, Z).
+__device__ inline void combine_row_wave(const float2* pr, int nchunk, float c, float& lmax,
+                                        double& Z) {
+  const int t = threadIdx.x & 63;
+  lmax = kNegBig;
+  for (int k = t; k < nchunk; k += 64) lmax = fmaxf(lmax, pr[k].x);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, 64));
+  Z = 0.0;
+  for (int k = t; k < nchunk; k += 64)
+    Z += (double)pr[k].y * exp2((double)(pr[k].x - lmax) * (double)c);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) Z += __shfl_xor(Z, off, 64);
+}
+
 // Accept test and first-rejection scan of request r (wave 0 of the calling block does the work;
 // every thread of the block must call it: it contains one block barrier).
 template <typename T>
@@ -33,6 +49,21 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
   //    per row; many (LM-head column tiles): the wave reduces each row's chunks in a fixed order.
   if (t >= 64) {
     // other waves of a larger block only join the barrier
+  } else if (a.rowstat_ready) {
+    // statistics already combined (one wave per row, by combine_row_wave)
+    for (int j = t; j < 2 * B + 1; j += 64) {
+      const int64_t row = j <= B ? prow0 + j : qrow0 + (j - Bp1);
+      if (j > B && first_from_target && j == Bp1) {
+        s_lmax[j] = 0.f;
+        s_Z[j] = 1.0;
+        s_st[j] = 0;
+        continue;
+      }
+      const RowStat rw = a.rowstat[row];
+      s_lmax[j] = rw.lmax;
+      s_Z[j] = rw.Z;
+      s_st[j] = rw.st;
+    }
   } else if (a.nchunk <= kStageChunks) {
     // the request's pairs: p rows then q rows, each a contiguous run of the workspace, loaded by
     // the whole wave in one round
@@ -74,16 +105,9 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
         }
         continue;
       }
-      const float2* pr = a.part + row * a.nchunk;
-      float lmax = kNegBig;
-      for (int k = t; k < a.nchunk; k += 64) lmax = fmaxf(lmax, pr[k].x);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, 64));
-      double Z = 0.0;
-      for (int k = t; k < a.nchunk; k += 64)
-        Z += (double)pr[k].y * exp2((double)(pr[k].x - lmax) * (double)a.c);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) Z += __shfl_xor(Z, off, 64);
+      float lmax;
+      double Z;
+      combine_row_wave(a.part + row * a.nchunk, a.nchunk, a.c, lmax, Z);
       if (t == 0) {
         const int st = row_status(lmax, Z);
         s_lmax[j] = lmax;

@@ -17,7 +17,8 @@ void timing_end(const char* name, hipStream_t stream);
 hipError_t launch_rowstats(const RowSet& rs, psispec_dtype dtype, int nchunk, int chunk_elems,
                            float c, float2* part, hipStream_t stream);
 hipError_t launch_topp(const RowSet& rs, psispec_dtype dtype, int nchunk, float c, double top_p,
-                       const float2* part, ToppStat* topp, hipStream_t stream);
+                       const float2* part, ToppStat* topp, hipStream_t stream,
+                       const RowStat* rowstat = nullptr);
 
 // linear.hip
 struct LinearArgs {
@@ -32,6 +33,7 @@ struct LinearArgs {
   const float2* part;
   const ToppStat* topp;
   RowStat* rowstat;
+  int rowstat_ready;  // rowstat already holds every row's statistics (launch_combine_rows)
   DrawDesc* desc;
   int32_t* ucount;
   int32_t* accept_len;
@@ -40,6 +42,9 @@ struct LinearArgs {
   uint64_t* accept_mask;
 };
 hipError_t launch_decide_linear(const LinearArgs& a, psispec_dtype dtype, hipStream_t stream);
+// Row statistics from many per-chunk pairs (the LM-head column tiles), one wave per row.
+hipError_t launch_combine_rows(const RowSet& rs, const float2* part, int nchunk, float c,
+                               RowStat* rowstat, hipStream_t stream);
 
 // tree.hip
 struct TreeArgs {

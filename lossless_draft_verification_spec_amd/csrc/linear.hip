@@ -18,7 +18,29 @@ __global__ __launch_bounds__(64) void k_decide_linear(LinearArgs a) {
   decide_linear_request<T>(a, blockIdx.x);
 }
 
+__global__ __launch_bounds__(64) void k_combine_rows(RowSet rs, const float2* __restrict__ part,
+                                                    int nchunk, float c,
+                                                    RowStat* __restrict__ rowstat) {
+  const int64_t row = blockIdx.x;
+  if (row_skipped(rs, row)) return;
+  float lmax;
+  double Z;
+  combine_row_wave(part + row * nchunk, nchunk, c, lmax, Z);
+  if (threadIdx.x == 0) rowstat[row] = RowStat{lmax, row_status(lmax, Z), Z};
+}
+
 }  // namespace
+
+hipError_t launch_combine_rows(const RowSet& rs, const float2* part, int nchunk, float c,
+                               RowStat* rowstat, hipStream_t stream) {
+  const int64_t rows = rs.nP + rs.nQ;
+  if (rows == 0) return hipSuccess;
+  timing_begin("combine_rows", stream);
+  hipLaunchKernelGGL(k_combine_rows, dim3((unsigned)rows), dim3(64), 0, stream, rs, part, nchunk, c,
+                     rowstat);
+  timing_end("combine_rows", stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_decide_linear(const LinearArgs& a, psispec_dtype dtype, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;

@@ -44,7 +44,8 @@ __device__ inline void row_stats_from_parts(const float2* part, int64_t row, int
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_topp(RowSet rs, int nchunk, float c, double top_p,
                                                    float pi_min, const float2* __restrict__ part,
-                                                   ToppStat* __restrict__ topp) {
+                                                   ToppStat* __restrict__ topp,
+                                                   const RowStat* __restrict__ pre) {
   constexpr bool kHalf = sizeof(T) == 2;
   constexpr int kKeyBits = kHalf ? 16 : 32;
   constexpr int kRounds = kKeyBits / 8;
@@ -53,7 +54,12 @@ __global__ __launch_bounds__(kThreads) void k_topp(RowSet rs, int nchunk, float 
   const T* rp = row_ptr<T>(rs, row);
   float lmax;
   double Z;
-  row_stats_from_parts(part, row, nchunk, c, lmax, Z);
+  if (pre) {  // statistics already combined
+    lmax = pre[row].lmax;
+    Z = pre[row].Z;
+  } else {
+    row_stats_from_parts(part, row, nchunk, c, lmax, Z);
+  }
   if (!(lmax > kNegBig) || !(lmax < __builtin_huge_valf()) || !(Z > 0.0) || !(Z < 1e300)) {
     if (threadIdx.x == 0) topp[row] = ToppStat{-__builtin_huge_valf(), 0, 1.0};
     return;
@@ -133,7 +139,8 @@ hipError_t launch_rowstats(const RowSet& rs, psispec_dtype dtype, int nchunk, in
 }
 
 hipError_t launch_topp(const RowSet& rs, psispec_dtype dtype, int nchunk, float c, double top_p,
-                       const float2* part, ToppStat* topp, hipStream_t stream) {
+                       const float2* part, ToppStat* topp, hipStream_t stream,
+                       const RowStat* rowstat) {
   const int64_t rows = rs.nP + rs.nQ;
   if (rows == 0) return hipSuccess;
   double pmin = (1.0 - top_p) / (4.0 * (double)rs.V);
@@ -141,10 +148,10 @@ hipError_t launch_topp(const RowSet& rs, psispec_dtype dtype, int nchunk, float 
   timing_begin("topp", stream);
   if (dtype == PSISPEC_BF16)
     hipLaunchKernelGGL(k_topp<bf16_t>, dim3((unsigned)rows), dim3(kThreads), 0, stream, rs, nchunk,
-                       c, top_p, (float)pmin, part, topp);
+                       c, top_p, (float)pmin, part, topp, rowstat);
   else
     hipLaunchKernelGGL(k_topp<float>, dim3((unsigned)rows), dim3(kThreads), 0, stream, rs, nchunk,
-                       c, top_p, (float)pmin, part, topp);
+                       c, top_p, (float)pmin, part, topp, rowstat);
   timing_end("topp", stream);
   return hipGetLastError();
 }
