@@ -178,10 +178,18 @@ def run_lmhead(steps, warmup, torch, pkg, workloads):
                           "flops_per_launch": flops, "avg_launch_us": round(gemm_us, 2)})
 
 
+def rowstats_source_sha():
+    """Hash of the sources the row-pass kernel is built from (kernel, device body, helpers)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("rows.hip", "rows.h", "internal.h"):
+        h.update(open(os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def read_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter summary, if it matches the current kernel
     source; else None."""
-    import hashlib
     path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
@@ -190,9 +198,7 @@ def read_traffic(kernel, workload):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc", "rows.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if kv.get("rows_hip_sha256_16") != sha:
+    if kv.get("source_sha256_16") != rowstats_source_sha():
         return None
     try:
         return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
