@@ -207,8 +207,8 @@ def read_traffic(kernel, workload):
 
 
 def cpu_baseline(host, preset, seconds):
-    """The oracle as it stands, single-threaded on this host, on the first requests of rotation
-    set 0 (step 0), for about `seconds` of work."""
+    """The oracle as it stands, single-threaded on this host, on the requests of rotation set 0,
+    step after step (Philox step 0, 1, ...), for about `seconds` of work."""
     import numpy as np
     import oracle
     import torch
@@ -224,14 +224,16 @@ def cpu_baseline(host, preset, seconds):
     B = preset.B
     done = 0
     t0 = time.perf_counter()
-    while done < preset.batch and time.perf_counter() - t0 < seconds:
-        oracle.verify_linear(ph[done:done + 1], qh[done:done + 1], d[done:done + 1], T=preset.T,
-                             top_p=preset.top_p, seed=host["seed"], step=0, request_base=done)
+    while time.perf_counter() - t0 < seconds:
+        r, step = done % preset.batch, done // preset.batch
+        oracle.verify_linear(ph[r:r + 1], qh[r:r + 1], d[r:r + 1], T=preset.T, top_p=preset.top_p,
+                             seed=host["seed"], step=step, request_base=r)
         done += 1
     el = time.perf_counter() - t0
     return dict(value=done * B / el, unit="rows/s", cores=1, kind="oracle",
-                sample=f"{done} of {preset.batch} requests (x {B} verified rows) of rotation set 0, "
-                       f"step 0, one thread, {el:.1f} s")
+                sample=f"{done} request verifies (x {B} verified rows): the {preset.batch} requests "
+                       f"of rotation set 0 over Philox steps 0..{(done - 1) // preset.batch}, "
+                       f"one thread, {el:.1f} s")
 
 
 def copy_calibration(torch):
