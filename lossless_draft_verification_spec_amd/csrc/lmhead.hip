@@ -269,8 +269,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(LMHeadArgs a) {
   // ---- epilogue -------------------------------------------------------------------------------
   // Element (i, j, v) of this lane sits at row m0 + wm*128 + i*32 + 8*(v/4) + 4*(lane/32) + v%4,
   // column n0 + wn*128 + j*32 + lane%32.  One 64-row slice (i fixed) at a time goes through LDS:
-  // then 4 threads per row store 64 columns each with 16-byte writes and reduce them to the
-  // segment's (max, sum exp2((x - max) c)), combined over the row's 4 segments.
+  // then 4 threads per row reduce 64 columns each to the segment's (max, sum exp2((x - max) c)),
+  // combined over the row's 4 segments, and each wave stores 16 of the slice's rows, one row of
+  // 256 columns per 1 KB coalesced instruction.
   constexpr int SROW = BN + 4;
   float* S = reinterpret_cast<float*>(smem);  // [64][SROW]
   const float c = a.c;
@@ -286,44 +287,56 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(LMHeadArgs a) {
       }
     __syncthreads();
     const int m = m0 + (lr < 32 ? i * 32 + lr : 128 + i * 32 + (lr - 32));
-    const int nbase = n0 + qq * 64;
-    const int nvalid = a.N - nbase;  // columns of this segment inside the row (may be <= 0)
+    const int nvalid = a.N - (n0 + qq * 64);  // columns of this segment inside the row (may be <= 0)
     const float* src = S + lr * SROW + qq * 64;
     float4 buf[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) buf[k] = *reinterpret_cast<const float4*>(src + 4 * k);
-    float mx = kNegBig;  // finite floor: a segment past the row's end gives (floor, 0)
+    // segment max and sum, four independent chains each (a finite floor: a segment past the row's
+    // end gives (floor, 0)); the chains are combined in a fixed order
+    float mq[4] = {kNegBig, kNegBig, kNegBig, kNegBig};
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const float x[4] = {buf[k].x, buf[k].y, buf[k].z, buf[k].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (4 * k + e < nvalid) mx = fmaxf(mx, x[e]);
+        if (4 * k + e < nvalid) mq[e] = fmaxf(mq[e], x[e]);
     }
-    float sm = 0.f;
+    const float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const float x[4] = {buf[k].x, buf[k].y, buf[k].z, buf[k].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (4 * k + e < nvalid) sm += __builtin_amdgcn_exp2f((x[e] - mx) * c);
+        if (4 * k + e < nvalid) sq[e] += __builtin_amdgcn_exp2f((x[e] - mx) * c);
     }
-    if (m < a.M) {
-      float* dst = a.logits + (int64_t)m * a.N + nbase;
-      if (nvalid >= 64 && (a.N & 3) == 0) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) *reinterpret_cast<float4*>(dst + 4 * k) = buf[k];
-      } else {
-        for (int k = 0; k < min(64, nvalid); ++k) dst[k] = src[k];
-      }
-    }
+    float sm = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+    float mxc = mx;
 #pragma unroll
     for (int off = 1; off <= 2; off <<= 1) {
-      const float m2 = __shfl_xor(mx, off, 64);
+      const float m2 = __shfl_xor(mxc, off, 64);
       const float s2 = __shfl_xor(sm, off, 64);
-      os_combine(mx, sm, m2, s2, c);
+      os_combine(mxc, sm, m2, s2, c);
     }
-    if (qq == 0 && m < a.M) a.part[(int64_t)m * a.ntiles + tn] = make_float2(mx, sm);
+    if (qq == 0 && m < a.M) a.part[(int64_t)m * a.ntiles + tn] = make_float2(mxc, sm);
+    // logits: one wave writes one row's 256 columns per instruction (16 rows per wave)
+    const int ncol = min(BN, a.N - n0);
+#pragma unroll 4
+    for (int q = 0; q < 16; ++q) {
+      const int sr = wave * 16 + q;  // slice row
+      const int mr = m0 + (sr < 32 ? i * 32 + sr : 128 + i * 32 + (sr - 32));
+      if (mr >= a.M) continue;
+      const float4 v4 = *reinterpret_cast<const float4*>(S + sr * SROW + 4 * lane);
+      float* dst = a.logits + (int64_t)mr * a.N + n0 + 4 * lane;
+      if (4 * lane + 4 <= ncol && (a.N & 3) == 0) {
+        *reinterpret_cast<float4*>(dst) = v4;
+      } else {
+        const float e4[4] = {v4.x, v4.y, v4.z, v4.w};
+        for (int e = 0; e < 4; ++e)
+          if (4 * lane + e < ncol) dst[e] = e4[e];
+      }
+    }
     __syncthreads();
   }
 }
