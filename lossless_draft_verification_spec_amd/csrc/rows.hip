@@ -45,7 +45,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void k_topp(RowSet rs, int nchunk, float c, double top_p,
                                                    float pi_min, const float2* __restrict__ part,
                                                    ToppStat* __restrict__ topp,
-                                                   const RowStat* __restrict__ pre) {
+                                                   const RowStat* __restrict__ pre, int vec_ok) {
   constexpr bool kHalf = sizeof(T) == 2;
   constexpr int kKeyBits = kHalf ? 16 : 32;
   constexpr int kRounds = kKeyBits / 8;
@@ -66,8 +66,15 @@ __global__ __launch_bounds__(kThreads) void k_topp(RowSet rs, int nchunk, float 
   }
   const float invZ = (float)(1.0 / Z);
   const double target = top_p * 0x1.0p56;
+  // Logits below l_cut cannot pass the pi >= pi_min test (pi = exp2((l - lmax) c) / Z): a
+  // comparison rejects them without an exp.  The cut sits a margin below the exact bound, so the
+  // exact test below still decides every token near it.
+  const float l_cut = pi_min > 0.f
+      ? (float)((double)lmax + (log2((double)pi_min) + log2(Z)) / (double)c - 1e-3 * (1.0 + fabs((double)lmax)))
+      : -__builtin_huge_valf();
 
-  __shared__ unsigned long long hist[256];
+  // one histogram per wave (the candidates' keys crowd into few bins), summed in wave order
+  __shared__ unsigned long long hist[kThreads / 64][256];
   __shared__ uint32_t s_prefix;
   __shared__ unsigned long long s_above, s_kept;
   if (threadIdx.x == 0) {
@@ -75,25 +82,42 @@ __global__ __launch_bounds__(kThreads) void k_topp(RowSet rs, int nchunk, float 
     s_above = 0;
     s_kept = 0;
   }
+  const int wave = threadIdx.x >> 6;
+  constexpr int E = 16 / (int)sizeof(T);
+  const int nvec = vec_ok ? rs.V / E : 0;
   for (int round = 0; round < kRounds; ++round) {
     const int shift = kKeyBits - 8 * (round + 1);
-    hist[threadIdx.x] = 0;
+    for (int w = 0; w < kThreads / 64; ++w) hist[w][threadIdx.x] = 0;
     __syncthreads();
     const uint32_t prefix = s_prefix;
-    for (int x = threadIdx.x; x < rs.V; x += kThreads) {
-      const T e = rp[x];
+    auto take = [&](T e) {
       const float l = to_f32(e);
+      if (!(l >= l_cut)) return;
       uint32_t key;
       if constexpr (kHalf) {
         key = order_key16(e.bits);
       } else {
         key = order_key(l);
       }
-      if (round > 0 && (key >> (shift + 8)) != (prefix >> (shift + 8))) continue;
+      if (round > 0 && (key >> (shift + 8)) != (prefix >> (shift + 8))) return;
       const float pi = __builtin_amdgcn_exp2f((l - lmax) * c) * invZ;
-      if (!(pi >= pi_min) || pi == 0.f) continue;
+      if (!(pi >= pi_min) || pi == 0.f) return;
       const unsigned long long w = (unsigned long long)((double)pi * 0x1.0p56);
-      atomicAdd(&hist[(key >> shift) & 255u], w);
+      atomicAdd(&hist[wave][(key >> shift) & 255u], w);
+    };
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rp);
+    for (int i = threadIdx.x; i < nvec; i += kThreads) {
+      const u32x4 v = __builtin_nontemporal_load(vp + i);
+      const T* ev = reinterpret_cast<const T*>(&v);
+#pragma unroll
+      for (int k = 0; k < E; ++k) take(ev[k]);
+    }
+    for (int x = nvec * E + threadIdx.x; x < rs.V; x += kThreads) take(rp[x]);
+    __syncthreads();
+    {
+      unsigned long long tot = 0;
+      for (int w = 0; w < kThreads / 64; ++w) tot += hist[w][threadIdx.x];
+      hist[0][threadIdx.x] = tot;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -101,13 +125,13 @@ __global__ __launch_bounds__(kThreads) void k_topp(RowSet rs, int nchunk, float 
       int b = 255;
       int lowest = -1;
       for (; b >= 0; --b) {
-        if (hist[b]) lowest = b;
-        if ((double)(run + hist[b]) >= target) break;
-        run += hist[b];
+        if (hist[0][b]) lowest = b;
+        if ((double)(run + hist[0][b]) >= target) break;
+        run += hist[0][b];
       }
       if (b < 0) b = lowest < 0 ? 0 : lowest;  // rounding left the mass short: lowest kept bin
       s_above = run;
-      s_kept = run + hist[b];
+      s_kept = run + hist[0][b];
       s_prefix = prefix | ((uint32_t)b << shift);
     }
     __syncthreads();
@@ -145,13 +169,16 @@ hipError_t launch_topp(const RowSet& rs, psispec_dtype dtype, int nchunk, float 
   if (rows == 0) return hipSuccess;
   double pmin = (1.0 - top_p) / (4.0 * (double)rs.V);
   if (pmin < 1e-30) pmin = 0.0;
+  const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
+  const int vec_ok = ((size_t)rs.V * es) % 16 == 0 && ((uintptr_t)rs.p % 16) == 0 &&
+                     ((uintptr_t)rs.q % 16) == 0;
   timing_begin("topp", stream);
   if (dtype == PSISPEC_BF16)
     hipLaunchKernelGGL(k_topp<bf16_t>, dim3((unsigned)rows), dim3(kThreads), 0, stream, rs, nchunk,
-                       c, top_p, (float)pmin, part, topp, rowstat);
+                       c, top_p, (float)pmin, part, topp, rowstat, vec_ok);
   else
     hipLaunchKernelGGL(k_topp<float>, dim3((unsigned)rows), dim3(kThreads), 0, stream, rs, nchunk,
-                       c, top_p, (float)pmin, part, topp, rowstat);
+                       c, top_p, (float)pmin, part, topp, rowstat, vec_ok);
   timing_end("topp", stream);
   return hipGetLastError();
 }
