@@ -34,11 +34,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=["c2", "ns", "c3", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c2", "ns", "c3", "c4", "c5"])
     ap.add_argument("--no-lmhead", action="store_true", help="skip the fused LM-head measurement")
     ap.add_argument("--lmhead-steps", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-target", action="store_true", help="skip the batch-256 target shape")
+    ap.add_argument("--no-tree", action="store_true", help="skip the tree verify measurement")
+    ap.add_argument("--tree-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for counter scaling)")
@@ -117,6 +119,63 @@ def run_workload(name, steps, warmup, torch, pkg, workloads):
     del sets
     torch.cuda.empty_cache()
     return res, host
+
+
+def run_tree(steps, warmup, torch, pkg, workloads, name="c4"):
+    """Time psispec_verify_tree on the 8-request, 32-node, V=151936 fp32 tree workload (rotation
+    sets exceeding the last-level cache); HBM roofline of the row pass over the N+1 node rows."""
+    preset = workloads.PRESETS[name]
+    R = preset.rotations
+    t0 = time.time()
+    sets = [workloads.make_tree(preset, device="cuda", rotation=i) for i in range(R)]
+    torch.cuda.synchronize()
+    log(f"{name}: generated {R} rotation sets in {time.time() - t0:.1f}s")
+    b, N, V = preset.batch, preset.N, preset.V
+    elem = 2 if preset.dtype == torch.bfloat16 else 4
+    dt = pkg.PSISPEC_BF16 if elem == 2 else pkg.PSISPEC_F32
+    ws = torch.empty(pkg.tree_workspace_bytes(b, N, V, dt), dtype=torch.uint8, device="cuda")
+    acc = torch.zeros(b, dtype=torch.int64, device="cuda")
+
+    def step(s):
+        inp = sets[s % R]
+        return pkg.psispec_verify_tree(inp.p, inp.parent, inp.node_tokens, preset.depth,
+                                       temperature=preset.T, top_p=preset.top_p, seed=inp.seed,
+                                       step=s, workspace=ws)
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for s in range(warmup, warmup + steps):
+        o = step(s)
+        acc += o["accept_len"].to(torch.int64) + 1
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    committed = int(acc.sum().item())
+    pkg.timing_enable(True)
+    for s in range(warmup, warmup + steps):
+        step(s)
+    kern = pkg.timing_read()
+    pkg.timing_enable(False)
+    row_bytes = b * (N + 1) * V * elem
+    rs = kern.get("rowstats", (0.0, 1))
+    rs_us = 1e3 * rs[0] / max(1, rs[1])
+    del sets
+    torch.cuda.empty_cache()
+    return dict(workload=f"{name}: tree verify batch={b} N={N} nodes depth<={preset.depth} V={V} "
+                         f"{'bf16' if elem == 2 else 'fp32'} logits, T={preset.T}",
+                ms_per_step=round(ms / steps, 4),
+                nodes_per_s=round(steps * b * N / (ms / 1e3), 1),
+                committed_tokens_per_s=round(committed / (ms / 1e3), 1),
+                mean_committed_per_request=round(committed / (steps * b), 4),
+                kernels_avg_us={k: round(1e3 * v[0] / max(1, v[1]), 2) for k, v in kern.items()},
+                roofline={"bound": "hbm", "kernel": "k_rowstats",
+                          "achieved": round(row_bytes / (rs_us / 1e6) / 1e9, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(row_bytes / (rs_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "bytes_per_launch": row_bytes, "avg_launch_us": round(rs_us, 2)})
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, datasheet
@@ -267,6 +326,9 @@ def main():
     if args.workload == "c5":
         print(json.dumps(run_lmhead(args.lmhead_steps, 3, torch, pkg, workloads)), flush=True)
         return
+    if args.workload == "c4":
+        print(json.dumps(run_tree(args.tree_steps, 5, torch, pkg, workloads)), flush=True)
+        return
     res, host = run_workload(args.workload, args.steps, args.warmup, torch, pkg, workloads)
     pr = res["preset"]
     log(f"{args.workload}: {res['ms_per_step'] * 1e3:.1f} us/step, kernels {res['kernels']}")
@@ -288,6 +350,10 @@ def main():
     if not args.no_lmhead:
         lmhead = run_lmhead(args.lmhead_steps, 3, torch, pkg, workloads)
         log(f"c5: {lmhead['ms_per_step'] * 1e3:.1f} us/step, kernels {lmhead['kernels_avg_us']}")
+    tree = None
+    if not args.no_tree:
+        tree = run_tree(args.tree_steps, 5, torch, pkg, workloads)
+        log(f"c4: {tree['ms_per_step'] * 1e3:.1f} us/step, kernels {tree['kernels_avg_us']}")
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(host, pr, args.cpu_seconds)
@@ -323,6 +389,7 @@ def main():
         "cpu_baseline": cpu,
         "target_shape": target,
         "lmhead": lmhead,
+        "tree": tree,
     }
     print(json.dumps(line), flush=True)
 

@@ -15,6 +15,7 @@ namespace psispec {
 namespace {
 
 constexpr int kMaxNodes = 1024;
+constexpr int kStagePairs = 4096;  // row pairs of a request staged in LDS (more: read in place)
 
 __device__ inline int row_status(float lmax, double Z) {
   const bool ok = (lmax > kNegBig) && (lmax < __builtin_huge_valf()) && (Z > 0.0) && (Z < 1e300);
@@ -44,18 +45,36 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
   __shared__ float s_lmax[kMaxNodes + 1];
   __shared__ double s_Z[kMaxNodes + 1];
   __shared__ double s_ratio[kMaxNodes];
-  __shared__ int s_depth[kMaxNodes];
   __shared__ int s_st;
+  __shared__ int32_t s_par[kMaxNodes], s_tok[kMaxNodes];
+  __shared__ double s_u[kMaxNodes];
+  __shared__ double s_pown[kMaxNodes];
+  __shared__ int s_first[kMaxNodes];
+  __shared__ float2 s_pair[kStagePairs];
 
-  // 1. row statistics of the root and node rows
+  // 0. the tree, every node's accept uniform (Philox of (request, c+1, accept)) and the row pairs,
+  //    loaded or computed by the whole wave up front: the serial steps below then read LDS only
+  for (int j = t; j < N; j += 64) {
+    s_par[j] = par[j];
+    s_tok[j] = tok[j];
+    s_u[j] = philox_uniform(a.seed, a.request_base + (uint32_t)r, (uint32_t)(j + 1), kPurposeAccept,
+                            a.step);
+  }
+  const bool staged = (int64_t)(N + 1) * a.nchunk <= kStagePairs;
+  if (staged)
+    for (int i = t; i < (N + 1) * a.nchunk; i += 64) s_pair[i] = a.part[row0 * a.nchunk + i];
+  __syncthreads();
+
+  // 1. row statistics of the root and node rows (pairs in chunk order)
   int st = 0;
   for (int j = t; j <= N; j += 64) {
     const int64_t row = row0 + j;
+    const float2* pr = staged ? s_pair + j * a.nchunk : a.part + row * a.nchunk;
     float lmax = kNegBig;
-    for (int k = 0; k < a.nchunk; ++k) lmax = fmaxf(lmax, a.part[row * a.nchunk + k].x);
+    for (int k = 0; k < a.nchunk; ++k) lmax = fmaxf(lmax, pr[k].x);
     double Z = 0.0;
     for (int k = 0; k < a.nchunk; ++k) {
-      const float2 pk = a.part[row * a.nchunk + k];
+      const float2 pk = pr[k];
       Z += (double)pk.y * exp2((double)(pk.x - lmax) * (double)a.c);
     }
     const int rs = row_status(lmax, Z);
@@ -64,51 +83,68 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
     s_Z[j] = Z;
     a.rowstat[row] = RowStat{lmax, rs, Z};
   }
-  // 2. structure: parents precede children, depth within max_depth (one lane, N is small)
-  if (t == 0) {
+  // 2. structure: parents precede children, depth within max_depth.  Each lane climbs its node's
+  //    parent chain (indices strictly decrease along a valid chain; a chain that meets an invalid
+  //    parent stops there, and that node's own lane flags it).
+  {
     int bad = 0;
-    for (int j = 0; j < N; ++j) {
-      const int pj = par[j];
+    for (int j = t; j < N; j += 64) {
+      const int pj = s_par[j];
       if (pj < -1 || pj >= j) {
         bad = 1;
-        s_depth[j] = 1;
         continue;
       }
-      s_depth[j] = pj < 0 ? 1 : s_depth[pj] + 1;
-      if (s_depth[j] > a.max_depth) bad = 1;
+      int d = 1, pnode = pj;
+      while (pnode >= 0 && d <= a.max_depth) {
+        const int q = s_par[pnode];
+        if (q < -1 || q >= pnode) break;
+        ++d;
+        pnode = q;
+      }
+      if (d > a.max_depth) bad = 1;
     }
-    s_st = bad ? PSISPEC_ST_BAD_PARENT : 0;
+    if (t < 64) {
+      const uint64_t bm = __ballot(bad);
+      if (t == 0) s_st = bm ? PSISPEC_ST_BAD_PARENT : 0;
+    }
   }
   __syncthreads();
 
-  // 3. data-parallel node ratios
+  // 3. data-parallel node ratios.  An earlier sibling s of node j has the same parent row, so the
+  //    probability it removes from j's residual is s's own probability p_own[s]: one gather per
+  //    node, all in parallel, then the sibling sums read LDS.
   for (int j = t; j < N; j += 64) {
-    const int v = par[j];
+    const int v = s_par[j], tj = s_tok[j];
+    s_pown[j] = (tj >= 0 && tj < V && v >= -1 && v < j)
+                    ? node_prob<T>(a, row0 + v + 1, s_lmax[v + 1], s_Z[v + 1], tj)
+                    : 0.0;
+  }
+  // first[s]: no earlier sibling of s carries s's token (each distinct removed token counts once)
+  for (int j = t; j < N; j += 64) {
+    const int v = s_par[j], tj = s_tok[j];
+    int first = 1;
+#pragma unroll 8
+    for (int s2 = 0; s2 < N; ++s2) first &= !(s2 < j && s_par[s2] == v && s_tok[s2] == tj);
+    s_first[j] = first;
+  }
+  __syncthreads();
+  for (int j = t; j < N; j += 64) {
+    const int v = s_par[j];
     double ratio = 0.0;
-    const int tj = tok[j];
+    const int tj = s_tok[j];
     if (tj < 0 || tj >= V) {
       st |= PSISPEC_ST_BAD_TOKEN;
     } else if (v >= -1 && v < j) {
-      const int64_t row = row0 + v + 1;
-      const float lmax = s_lmax[v + 1];
-      const double Z = s_Z[v + 1];
-      double res = node_prob<T>(a, row, lmax, Z, tj);
+      double res = s_pown[j];
       double R = 1.0;
-      for (int s = 0; s < j; ++s) {
-        if (par[s] != v) continue;
-        const int ts = tok[s];
-        if (ts < 0 || ts >= V) continue;
-        if (ts == tj) {
+#pragma unroll 8
+      for (int s = 0; s < N; ++s) {  // earlier siblings, in index order
+        const int ts = s_tok[s];
+        if (s >= j || s_par[s] != v || ts < 0 || ts >= V) continue;
+        if (ts == tj)
           res = 0.0;  // same token rejected earlier: already removed from the residual
-          continue;
-        }
-        bool seen = false;  // subtract each distinct removed token once
-        for (int s2 = 0; s2 < s; ++s2)
-          if (par[s2] == v && tok[s2] == ts) {
-            seen = true;
-            break;
-          }
-        if (!seen) R -= node_prob<T>(a, row, lmax, Z, ts);
+        else if (s_first[s])
+          R -= s_pown[s];
       }
       ratio = R > 0.0 ? fmin(1.0, res / R) : 0.0;
     }
@@ -119,35 +155,43 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
   for (int off = 32; off >= 1; off >>= 1) st |= __shfl_xor(st, off, 64);
   __syncthreads();
 
-  // 4. the walk (one lane)
+  // 4. the walk.  At each node the children are scanned in index order by the whole wave, 64 at a
+  //    time: a ballot finds the first accepted child; the valid tokens of the children rejected
+  //    before it are appended to the removed-token list in index order.
   const int Dp1 = a.max_depth + 1;
   int32_t* nodes = a.accept_nodes + (int64_t)r * a.max_depth;
   int32_t* out = a.out_tokens + (int64_t)r * Dp1;
   int32_t* excl = a.excl + (int64_t)r * N;
-  if (t == 0) {
+  int cur = -1, dep = 0, nexcl = 0;
+  if (t < 64) {
     st |= s_st;
-    int cur = -1, dep = 0, nexcl = 0;
     if (!(s_st & PSISPEC_ST_BAD_PARENT)) {
       for (;;) {
         int next = -1;
         nexcl = 0;
-        for (int c = 0; c < N; ++c) {
-          if (par[c] != cur) continue;
-          const double u = philox_uniform(a.seed, a.request_base + (uint32_t)r, (uint32_t)(c + 1),
-                                          kPurposeAccept, a.step);
-          if (u < s_ratio[c]) {
-            next = c;
-            break;
-          }
-          if (tok[c] >= 0 && tok[c] < V) excl[nexcl++] = tok[c];
+        for (int c0 = 0; c0 < N && next < 0; c0 += 64) {
+          const int c = c0 + t;
+          const bool child = c < N && s_par[c] == cur;
+          const uint64_t am = __ballot(child && s_u[c] < s_ratio[c]);
+          const int firstacc = am ? __builtin_ctzll(am) : 64;
+          const uint64_t before = firstacc == 64 ? ~0ull : ((1ull << firstacc) - 1ull);
+          const bool rej = child && t < firstacc && s_tok[c] >= 0 && s_tok[c] < V;
+          const uint64_t rm = __ballot(rej) & before;
+          if (rej) excl[nexcl + __builtin_popcountll(rm & ((1ull << t) - 1ull))] = s_tok[c];
+          nexcl += __builtin_popcountll(rm);
+          if (firstacc < 64) next = c0 + firstacc;
         }
         if (next < 0) break;
-        nodes[dep] = next;
-        out[dep] = tok[next];
+        if (t == 0) {
+          nodes[dep] = next;
+          out[dep] = s_tok[next];
+        }
         ++dep;
         cur = next;
       }
     }
+  }
+  if (t == 0) {
     for (int i = dep; i < a.max_depth; ++i) nodes[i] = -1;
     for (int i = dep; i < Dp1; ++i) out[i] = -1;
     a.accept_len[r] = dep;
