@@ -53,7 +53,7 @@ def _run(inp, rows, T=1.0, top_p=1.0, steps=(0,), tally=None, logit_tol=(2e-5, 1
 
 @pytest.mark.parametrize("batch,B,H,V,r", [(3, 4, 128, 1000, 16), (1, 1, 64, 300, 0),
                                            (20, 8, 192, 600, 8), (5, 2, 256, 777, 33),
-                                           (2, 3, 64, 513, 1)])
+                                           (2, 3, 64, 513, 1), (2, 2, 128, 700, 64)])
 def test_lmhead_small(batch, B, H, V, r):
     inp = workloads.make_lmhead("c5", device="cpu", steps=3, batch=batch, B=B, H=H, V=V, r=r)
     t = _run(inp, range(batch), steps=range(3))

@@ -244,6 +244,17 @@ def test_tree_small(dtype, batch, N, V):
     t.check()
 
 
+@pytest.mark.parametrize("k,depth,seed", [(200, 4, 31), (3, 64, 32)])
+def test_tree_max_nodes(k, depth, seed):
+    """N = 1024, the largest tree: a wide one (a node may have up to 200 children, so the walk's
+    child scan crosses 64-lane chunks) and a deep one (max_depth 64)."""
+    p, parent, tokens = _rand_tree(2, 1024, 300, torch.float32, seed=seed, k=k, depth=depth,
+                                   dup=True)
+    t = _tree_compare(p, parent, tokens, 64, steps=range(3))
+    print(t)
+    t.check()
+
+
 @pytest.mark.parametrize("T,top_p", [(0.7, 1.0), (1.0, 0.9)])
 def test_tree_temperature_top_p(T, top_p):
     p, parent, tokens = _rand_tree(4, 20, 3000, torch.float32, seed=21)
