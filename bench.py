@@ -12,7 +12,9 @@ each step has its own drafted tokens and Philox step.  Inputs are resident in HB
 
 One JSON line is printed: verified rows/s (batch*B per step) as `value`, committed tokens/s, the
 roofline of the dominant kernel (the HBM pass, timed with HIP events on the library's stream), the
-oracle timed on the host cores as `cpu_baseline`, and the batch-256 B=8 shape as `target_shape`.
+oracle timed on the host cores as `cpu_baseline`, the batch-256 B=8 shape as `target_shape`, the
+LM head + verify (batch 128, B=8, H=4096, rank-16 LoRA) with its MFMA roofline as `lmhead`, and the
+32-node tree verify as `tree`.  `--workload c3|c4|c5` prints the top-p, tree or LM-head line alone.
 """
 from __future__ import annotations
 
@@ -310,7 +312,7 @@ def copy_calibration(torch):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(requests would shard by request_base with no exchange).", file=sys.stderr)
         sys.exit(2)
     import torch
