@@ -121,6 +121,7 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
  *   q_logits     must be NULL (sampled-candidate trees are not implemented: PSISPEC_EUNSUPPORTED)
  *   parent       [batch][N] int32 parent node of node j, -1 = root, must be < j
  *   node_tokens  [batch][N] int32 token of node j
+ *   N            1..1024 nodes per request;  V >= 1;  batch >= 0 (0 launches nothing)
  *   max_depth    bound on the depth of any node (1..64)
  * Uniforms: node c's test at (request, c+1, accept); the final draw at (request, row, draw) where
  * row is the stopping node's row.
