@@ -29,13 +29,13 @@ struct Plan {
   size_t total;
 };
 
-// Row split of the HBM pass: chunks of about 64 KiB (a workgroup keeps 32 KiB of 16-byte loads in
-// flight, two rounds per chunk), still thousands of workgroups for a few hundred rows; chunk
+// Row split of the HBM pass: chunks of about 128 KiB (a workgroup keeps 32 KiB of 16-byte loads in
+// flight, about four rounds per chunk), still thousands of workgroups for a few hundred rows; chunk
 // starts stay 16-byte aligned (multiples of 64 elements).
 Plan make_plan(int64_t rows, int batch, int V, size_t es, int excl_stride, int fixed_nchunk = 0) {
   Plan pl{};
   const size_t row_bytes = (size_t)V * es;
-  int nchunk = (int)((row_bytes + 65535) / 65536);
+  int nchunk = (int)((row_bytes + 131071) / 131072);
   if (nchunk < 1) nchunk = 1;
   int ce = (V + nchunk - 1) / nchunk;
   ce = (ce + 63) / 64 * 64;
