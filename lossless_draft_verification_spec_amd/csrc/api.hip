@@ -30,12 +30,18 @@ struct Plan {
 };
 
 // Row split of the HBM pass: chunks of about 128 KiB (a workgroup keeps 32 KiB of 16-byte loads in
-// flight, about four rounds per chunk), still thousands of workgroups for a few hundred rows; chunk
-// starts stay 16-byte aligned (multiples of 64 elements).
+// flight, about four rounds per chunk); calls with few rows get smaller chunks (down to 16 KiB) so
+// that about 2048 workgroups (8 per CU) stream at once; chunk starts stay 16-byte aligned
+// (multiples of 64 elements).
 Plan make_plan(int64_t rows, int batch, int V, size_t es, int excl_stride, int fixed_nchunk = 0) {
   Plan pl{};
   const size_t row_bytes = (size_t)V * es;
   int nchunk = (int)((row_bytes + 131071) / 131072);
+  if (rows > 0) {
+    const int64_t want = (2048 + rows - 1) / rows;
+    const int64_t most = std::max<int64_t>(1, (int64_t)(row_bytes / 16384));
+    nchunk = (int)std::max<int64_t>(nchunk, std::min(want, most));
+  }
   if (nchunk < 1) nchunk = 1;
   int ce = (V + nchunk - 1) / nchunk;
   ce = (ce + 63) / 64 * 64;
