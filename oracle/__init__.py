@@ -59,6 +59,9 @@ def lib():
         L.psispec_oracle_verify_tree.argtypes = (
             [P, i32, P, P, i32, i32, i32, i32, dbl, dbl, u64, u32, u32, P, P] + [P] * 10)
         L.psispec_oracle_verify_tree.restype = i32
+        L.psispec_oracle_sample_drafts.argtypes = (
+            [P, ctypes.c_int64, P, i32, i32, i32, i32, dbl, dbl, u64, u32, u32, u32] + [P] * 5)
+        L.psispec_oracle_sample_drafts.restype = i32
         L.psispec_oracle_lmhead_logits.argtypes = [P, P, P, P, dbl, i32, i32, i32, i32, P]
         L.psispec_oracle_lmhead_logits.restype = i32
         _lib = L
@@ -132,6 +135,38 @@ def verify_linear(p, q, draft, T=1.0, top_p=1.0, seed=0, step=0, request_base=0,
         _ptr(out.get("resid_S")))
     if rc != 0:
         raise ValueError(f"oracle verify_linear rejected its arguments (code {rc})")
+    return out
+
+
+def sample_drafts(ar, q, B=None, T=1.0, top_p=1.0, seed=0, step=0, request_base=0, flags=0,
+                  u_draw=None):
+    """Drafted tokens [batch][B].  q[batch][B][V] (row 0 unread with FIRST_FROM_TARGET; None allowed
+    then when B == 1); ar (read only with FIRST_FROM_TARGET): [batch][V] or [batch][k][V], whose
+    request r starts its first row at element r * (k V)."""
+    q = None if q is None else np.ascontiguousarray(q)
+    ar = None if ar is None else np.ascontiguousarray(ar)
+    if q is not None:
+        batch, B, V = q.shape
+        code = _dtype_code(q)
+    else:
+        batch, V = ar.shape[0], ar.shape[-1]
+        B = 1 if B is None else B
+        code = _dtype_code(ar)
+    stride = 0
+    if ar is not None:
+        if ar.shape[0] != batch or ar.shape[-1] != V or (q is not None and ar.dtype != q.dtype):
+            raise ValueError("ar must be [batch][...][V] with the dtype of q")
+        stride = ar.size // max(batch, 1)
+    ud = None if u_draw is None else np.ascontiguousarray(u_draw, dtype=np.float64)
+    out = dict(tokens=np.zeros((batch, B), np.int32), status=np.zeros((batch, B), np.int32),
+               margin_sample=np.zeros((batch, B), np.float64),
+               margin_topp=np.zeros((batch, B), np.float64))
+    rc = lib().psispec_oracle_sample_drafts(
+        _ptr(ar), stride, _ptr(q), code, batch, B, V, float(T), float(top_p), seed & (2**64 - 1),
+        step, request_base, flags, _ptr(ud), _ptr(out["tokens"]), _ptr(out["status"]),
+        _ptr(out["margin_sample"]), _ptr(out["margin_topp"]))
+    if rc != 0:
+        raise ValueError(f"oracle sample_drafts rejected its arguments (code {rc})")
     return out
 
 

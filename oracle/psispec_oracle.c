@@ -327,6 +327,54 @@ int psispec_oracle_verify_linear(const void* p, const void* q, int dtype, const 
 }
 
 /* ------------------------------------------------------------------------------------------------
+ * Drafting ([alphalab] walkthrough steps 1-2: the AR path samples the first token of the block, the
+ * diffusion path proposes the remaining ones in parallel; [lanes] "Ψ-Spec이 한 스텝에서 하는 일": the
+ * same model drafts the block).  Each drafted token is one inverse-CDF draw from its row after the
+ * same temperature and nucleus transform the verify applies (the verify is lossless only when the
+ * drafts come from exactly the q' it divides by).  Row of position i: with FIRST_FROM_TARGET and
+ * i = 0 the AR row of the request (ar + r * ar_stride elements), else q row i of the request
+ * (q[batch][B][V]; row 0 is then not read).  The uniform is the Philox value at
+ * (request_base + r, i, DRAFT, step), or u_draw[r][i] when given.
+ * ---------------------------------------------------------------------------------------------- */
+int psispec_oracle_sample_drafts(const void* ar, int64_t ar_stride, const void* q, int dtype,
+                                 int batch, int B, int V, double T, double top_p, uint64_t seed,
+                                 uint32_t step, uint32_t request_base, uint32_t flags,
+                                 const double* u_draw, int32_t* tokens, int32_t* status,
+                                 double* margin_sample, double* margin_topp) {
+  if (!tokens || batch < 0 || B < 1 || B > 64 || V < 1) return ORC_EINVAL;
+  if (!(T > 0.0) || !isfinite(T) || !(top_p > 0.0) || !(top_p <= 1.0)) return ORC_EINVAL;
+  int first_from_target = (flags & ORC_FIRST_FROM_TARGET) != 0;
+  if (first_from_target && (!ar || ar_stride < V)) return ORC_EINVAL;
+  if (!q && !(first_from_target && B == 1)) return ORC_EINVAL;
+  size_t es = elem_size(dtype);
+  double* pi = (double*)malloc(sizeof(double) * (size_t)V);
+  for (int r = 0; r < batch; ++r) {
+    for (int i = 0; i < B; ++i) {
+      const char* row;
+      if (first_from_target && i == 0)
+        row = (const char*)ar + (size_t)r * (size_t)ar_stride * es;
+      else
+        row = (const char*)q + ((size_t)r * (size_t)B + (size_t)i) * (size_t)V * es;
+      double mt = INFINITY;
+      int st = psispec_oracle_row_probs(row, dtype, V, T, top_p, pi, &mt);
+      double S = 0.0;
+      for (int x = 0; x < V; ++x) S += pi[x];
+      double u = u_draw ? u_draw[(size_t)r * B + i]
+                        : psispec_oracle_uniform(seed, request_base + (uint32_t)r, (uint32_t)i,
+                                                 ORC_PURPOSE_DRAFT, step);
+      double ms = 0.0;
+      int c = inverse_cdf(pi, V, S, u, &ms);
+      tokens[(size_t)r * B + i] = c;
+      if (status) status[(size_t)r * B + i] = st;
+      if (margin_sample) margin_sample[(size_t)r * B + i] = ms;
+      if (margin_topp) margin_topp[(size_t)r * B + i] = mt;
+    }
+  }
+  free(pi);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------------------------------
  * Tree verify ([alphalab] "Linear 與 Tree sampler": several likely candidates per position, pruned to
  * a finite prefix tree that is verified at once).  The pages give no rule; we take the lossless rule
  * for candidates chosen deterministically (top-k): at node v with distribution pi_v, children are

@@ -69,6 +69,15 @@ int psispec_oracle_verify_linear(const void* p, const void* q, int dtype, const 
                                  double* margin_sample, double* margin_topp, double* resid_w,
                                  double* resid_S);
 
+/* Drafting: tokens[r][i] ~ p'(row) by inverse CDF with the Philox value at (request, i, DRAFT, step)
+ * (or u_draw[r][i]); row = AR row r (ar + r * ar_stride elements) for i = 0 with FIRST_FROM_TARGET,
+ * else q[r][i].  status/margins [batch][B], nullable. */
+int psispec_oracle_sample_drafts(const void* ar, int64_t ar_stride, const void* q, int dtype,
+                                 int batch, int B, int V, double T, double top_p, uint64_t seed,
+                                 uint32_t step, uint32_t request_base, uint32_t flags,
+                                 const double* u_draw, int32_t* tokens, int32_t* status,
+                                 double* margin_sample, double* margin_topp);
+
 int psispec_oracle_verify_tree(const void* p, int dtype, const int32_t* parent,
                                const int32_t* node_tokens, int batch, int N, int V, int max_depth,
                                double T, double top_p, uint64_t seed, uint32_t step,
