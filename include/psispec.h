@@ -21,7 +21,7 @@
  * q' are softmax(logits / temperature), optionally truncated to the tie-inclusive nucleus of mass
  * top_p and renormalised.  Uniforms come from Philox4x32-10 (Salmon et al., SC'11) with key = seed
  * and counter = (request_base + request, position, purpose, step); u = top 53 bits of
- * (word0 << 32 | word1) times 2^-53.  Purposes: 0 = accept test, 1 = final draw.
+ * (word0 << 32 | word1) times 2^-53.  Purposes: 0 = accept test, 1 = final draw, 2 = drafting.
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; rows are contiguous with V elements.
@@ -141,6 +141,38 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
                                    int32_t* accept_nodes, int32_t* out_tokens, float* node_ratios,
                                    int32_t* status, void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/*
+ * Drafting step ([alphalab] walkthrough steps 1-2: the AR path samples the first token of the
+ * block, the diffusion path proposes the others in parallel).  Draws d_0..d_{B-1} of every request,
+ * each from its row after the transform the verify applies (softmax(logits / temperature), then the
+ * nucleus of mass top_p, renormalised): the verify is lossless only for drafts drawn from exactly
+ * that q'.  Each draw is an inverse CDF by ascending token id, computed in fp64 like the verify's
+ * final draw, with the Philox uniform of (request_base + request, i, purpose 2 = draft, step).
+ *
+ *   ar_logits    AR rows, read only with PSISPEC_FIRST_FROM_TARGET (may be NULL otherwise): the row
+ *                of request r starts at element r * ar_stride; d_0 is drawn from it.  ar_stride >= V
+ *                ((B+1)*V reads row 0 of the verify's p_logits [batch][B+1][V]; V reads packed
+ *                [batch][V] rows)
+ *   q_logits     [batch][B][V] draft rows; d_i is drawn from row i.  With PSISPEC_FIRST_FROM_TARGET
+ *                row 0 is not read, and q_logits may be NULL when B = 1
+ *   dtype        element type of ar_logits and q_logits (PSISPEC_F32 or PSISPEC_BF16)
+ *   B            1..64;  V >= 1;  batch >= 0 (0 launches nothing)
+ *   s            host pointer to the sampling parameters (the verify's temperature and top_p)
+ * Outputs (device):
+ *   draft_tokens [batch][B] int32   in [0, V)
+ *   status       [batch][B] int32   PSISPEC_ST_NONFINITE when the row holds NaN/+Inf or no finite
+ *                                   logit (that token is then unspecified); nullable
+ * Rows that are 16-byte aligned with V * element size and ar_stride * element size multiples of 16
+ * are read with 16-byte loads; any other layout is read element by element.
+ */
+size_t psispec_sample_drafts_workspace(int32_t batch, int32_t B, int32_t V, psispec_dtype dtype);
+
+psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
+                                     const void* q_logits, psispec_dtype dtype, int32_t batch,
+                                     int32_t B, int32_t V, const psispec_sampling* s,
+                                     int32_t* draft_tokens, int32_t* status, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /*
  * LM head + linear verify ([lanes] §"헤드냐, LoRA냐": the draft path is the frozen AR weights plus a

@@ -21,8 +21,8 @@ ST_NONFINITE, ST_BAD_TOKEN, ST_Q_ZERO, ST_RESID_ZERO, ST_BAD_PARENT = 1, 2, 4, 8
 
 EXPORTS = ("psispec_verify_linear_workspace", "psispec_verify_linear",
            "psispec_verify_tree_workspace", "psispec_verify_tree", "psispec_lmhead_verify_workspace",
-           "psispec_lmhead_verify", "psispec_strerror", "psispec_timing_enable",
-           "psispec_timing_read")
+           "psispec_lmhead_verify", "psispec_sample_drafts_workspace", "psispec_sample_drafts",
+           "psispec_strerror", "psispec_timing_enable", "psispec_timing_read")
 
 
 class PsispecError(RuntimeError):
@@ -62,6 +62,11 @@ def lib():
         L.psispec_lmhead_verify.argtypes = ([P, P, P, P, P, ctypes.c_float, i32, i32, i32, i32, i32,
                                              P, P, P, P, P, P, P, P, P, sz, P])
         L.psispec_lmhead_verify.restype = i32
+        L.psispec_sample_drafts_workspace.argtypes = [i32, i32, i32, i32]
+        L.psispec_sample_drafts_workspace.restype = sz
+        L.psispec_sample_drafts.argtypes = [P, ctypes.c_int64, P, i32, i32, i32, i32, P, P, P, P, sz,
+                                            P]
+        L.psispec_sample_drafts.restype = i32
         L.psispec_strerror.argtypes = [i32]
         L.psispec_strerror.restype = ctypes.c_char_p
         L.psispec_timing_enable.argtypes = [i32]
@@ -259,6 +264,68 @@ def psispec_lmhead_verify(h_ar: torch.Tensor, h_draft: torch.Tensor, w_t: torch.
         _ptr(out["out_tokens"]), _ptr(out.get("ratios")), _ptr(out.get("accept_mask")),
         _ptr(out.get("status")), _ptr(logits), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "psispec_lmhead_verify")
+    return out
+
+
+def drafts_workspace_bytes(batch, B, V, dtype) -> int:
+    return int(lib().psispec_sample_drafts_workspace(batch, B, V, dtype))
+
+
+def psispec_sample_drafts(q_logits: torch.Tensor | None, ar_logits: torch.Tensor | None = None,
+                          B: int | None = None, temperature: float = 1.0, top_p: float = 1.0,
+                          seed: int = 0, step: int = 0, request_base: int = 0, flags: int = 0,
+                          workspace: torch.Tensor | None = None, out: dict | None = None,
+                          stream=None) -> dict:
+    """Drafting step.  q_logits [batch][B][V] (bf16 or fp32); with FIRST_FROM_TARGET, d_0 comes from
+    ar_logits: a [batch][V] tensor whose rows are contiguous (any row stride, e.g. p[:, 0, :]) or a
+    contiguous [batch][k][V] tensor (row 0 of each request is read).  q_logits may be None with
+    FIRST_FROM_TARGET when B == 1.  Returns draft_tokens [batch][B] int32 and status [batch][B]."""
+    fft = (flags & PSISPEC_FIRST_FROM_TARGET) != 0
+    ref = q_logits if q_logits is not None else ar_logits
+    if ref is None:
+        raise PsispecError("q_logits is required (or ar_logits with FIRST_FROM_TARGET and B == 1)")
+    if q_logits is not None:
+        if q_logits.dim() != 3:
+            raise PsispecError("q_logits must be [batch][B][V]")
+        batch, B, V = q_logits.shape
+        _dev(q_logits, "q_logits")
+    else:
+        if not fft or (B not in (None, 1)):
+            raise PsispecError("q_logits may be omitted only with FIRST_FROM_TARGET and B == 1")
+        batch, V, B = ar_logits.shape[0], ar_logits.shape[-1], 1
+    dt = _dtype_code(ref)
+    dev = ref.device
+    stride = 0
+    if fft:
+        if ar_logits is None:
+            raise PsispecError("FIRST_FROM_TARGET needs ar_logits")
+        if ar_logits.dtype != ref.dtype or ar_logits.shape[0] != batch or ar_logits.shape[-1] != V:
+            raise PsispecError("ar_logits must hold [batch] rows of V elements of q's dtype")
+        if not ar_logits.is_cuda or ar_logits.device != dev:
+            raise PsispecError(f"ar_logits must be on {dev}")
+        if ar_logits.dim() == 2:
+            if ar_logits.stride(1) != 1 or ar_logits.stride(0) < V:
+                raise PsispecError("ar_logits rows must be contiguous and not overlap")
+            stride = ar_logits.stride(0)
+        elif ar_logits.dim() == 3:
+            _dev(ar_logits, "ar_logits")
+            stride = ar_logits.shape[1] * V
+        else:
+            raise PsispecError("ar_logits must be [batch][V] or [batch][k][V]")
+    if out is None:
+        out = dict(draft_tokens=torch.empty(batch, B, dtype=torch.int32, device=dev),
+                   status=torch.empty(batch, B, dtype=torch.int32, device=dev))
+    need = drafts_workspace_bytes(batch, B, V, dt)
+    if need == 0:
+        raise PsispecError("unsupported sizes (B must be 1..64)")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = _sampling(temperature, top_p, seed, step, request_base, flags)
+    rc = lib().psispec_sample_drafts(
+        _ptr(ar_logits) if fft else None, stride, _ptr(q_logits), dt, batch, B, V, ctypes.byref(s),
+        _ptr(out["draft_tokens"]), _ptr(out.get("status")), _ptr(workspace), workspace.numel(),
+        _stream(stream))
+    _check(rc, "psispec_sample_drafts")
     return out
 
 

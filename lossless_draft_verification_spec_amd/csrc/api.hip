@@ -5,6 +5,7 @@
 //   topp      -- (top_p < 1) nucleus threshold and mass per row;
 //   decide    -- per request: ratios, accept bits, first rejection (linear) or the tree walk;
 //   draw      -- fp64 normalisers, residual sub-chunk sums, inverse-CDF select of the final token.
+#include <limits.h>
 #include <math.h>
 #include <string.h>
 
@@ -33,7 +34,10 @@ struct Plan {
 // flight, about four rounds per chunk); calls with few rows get smaller chunks (down to 16 KiB) so
 // that about 2048 workgroups (8 per CU) stream at once; chunk starts stay 16-byte aligned
 // (multiples of 64 elements).
-Plan make_plan(int64_t rows, int batch, int V, size_t es, int excl_stride, int fixed_nchunk = 0) {
+// rows: rows of the HBM pass; batch: draws (one per request, or one per drafted token); pool: the
+// draws have a q row (residual draws keep a pool of uncertain-sign tokens).
+Plan make_plan(int64_t rows, int64_t batch, int V, size_t es, int excl_stride, int fixed_nchunk = 0,
+               bool pool = true) {
   Plan pl{};
   const size_t row_bytes = (size_t)V * es;
   int nchunk = (int)((row_bytes + 131071) / 131072);
@@ -77,7 +81,7 @@ Plan make_plan(int64_t rows, int batch, int V, size_t es, int excl_stride, int f
   pl.off_suboff = off;
   off = align_up(off + sizeof(int32_t) * (size_t)batch * pl.nsub);
   pl.off_upool = off;
-  off = align_up(off + sizeof(double2) * (size_t)batch * kUncPool);
+  off = align_up(off + (pool ? sizeof(double2) * (size_t)batch * kUncPool : 0));
   pl.off_ucount = off;
   off = align_up(off + sizeof(int32_t) * (size_t)batch);
   pl.total = off;
@@ -265,7 +269,7 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
   const float c = (float)(1.4426950408889634074 / T);
   const bool use_topp = s->top_p < 1.0;
 
-  RowSet rs{p_logits, q_logits, nP, nQ, V, B, (s->flags & PSISPEC_FIRST_FROM_TARGET) ? 1 : 0};
+  RowSet rs{p_logits, q_logits, nP, nQ, V, B, (s->flags & PSISPEC_FIRST_FROM_TARGET) ? 1 : 0, V};
   float2* part = carve<float2>(workspace, pl.off_part);
   RowStat* rowstat = carve<RowStat>(workspace, pl.off_rowstat);
   ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
@@ -355,7 +359,7 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
   const float c = (float)(1.4426950408889634074 / T);
   const bool use_topp = s->top_p < 1.0;
 
-  RowSet rs{p_logits, nullptr, nP, 0, V, 1, 0};
+  RowSet rs{p_logits, nullptr, nP, 0, V, 1, 0, V};
   float2* part = carve<float2>(workspace, pl.off_part);
   RowStat* rowstat = carve<RowStat>(workspace, pl.off_rowstat);
   ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
@@ -419,6 +423,87 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
   da.upool = carve<double2>(workspace, pl.off_upool);
   da.ucount = carve<int32_t>(workspace, pl.off_ucount);
   da.out_tokens = out_tokens;
+  da.status = status;
+  if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
+  return PSISPEC_OK;
+}
+
+// Drafting step: rows of the HBM pass are the AR rows (one per request, Uno layout) and the q rows;
+// the plan is sized for both so that the workspace query needs no flags.
+size_t psispec_sample_drafts_workspace(int32_t batch, int32_t B, int32_t V, psispec_dtype dtype) {
+  if (batch < 0 || B < 1 || B > 64 || V < 1) return 0;
+  if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return 0;
+  const int64_t rows = (int64_t)batch * (B + 1), jobs = (int64_t)batch * B;
+  return make_plan(rows, jobs, V, elem_size(dtype), 0, 0, false).total + kAlign;
+}
+
+psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
+                                     const void* q_logits, psispec_dtype dtype, int32_t batch,
+                                     int32_t B, int32_t V, const psispec_sampling* s,
+                                     int32_t* draft_tokens, int32_t* status, void* workspace,
+                                     size_t workspace_bytes, void* stream_ptr) {
+  if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return PSISPEC_EDTYPE;
+  if (batch < 0 || B < 1 || B > 64 || V < 1) return PSISPEC_EINVAL;
+  if (!sampling_ok(s)) return PSISPEC_EINVAL;
+  if (batch == 0) return PSISPEC_OK;
+  const bool fft = (s->flags & PSISPEC_FIRST_FROM_TARGET) != 0;
+  if (!draft_tokens) return PSISPEC_EINVAL;
+  if (fft && (!ar_logits || ar_stride < V)) return PSISPEC_EINVAL;
+  if (!q_logits && !(fft && B == 1)) return PSISPEC_EINVAL;
+  const int64_t rows_plan = (int64_t)batch * (B + 1), jobs = (int64_t)batch * B;
+  const Plan pl = make_plan(rows_plan, jobs, V, elem_size(dtype), 0, 0, false);
+  if (rows_plan * pl.nchunk > INT32_MAX || jobs * pl.nchunk_draw > INT32_MAX) return PSISPEC_EINVAL;
+  if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace % kAlign) != 0)
+    return PSISPEC_EWORKSPACE;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const double T = s->temperature;
+  const float c = (float)(1.4426950408889634074 / T);
+  const bool use_topp = s->top_p < 1.0;
+
+  // p rows: the AR row of each request (Uno layout only); q rows: [batch][B], position 0 skipped
+  // in the Uno layout
+  const int64_t nP = fft ? batch : 0, nQ = q_logits ? jobs : 0;
+  RowSet rs{fft ? ar_logits : nullptr, q_logits, nP, nQ, V, B, fft ? 1 : 0,
+            fft ? ar_stride : (int64_t)V};
+  float2* part = carve<float2>(workspace, pl.off_part);
+  RowStat* rowstat = carve<RowStat>(workspace, pl.off_rowstat);
+  ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
+  DrawDesc* desc = carve<DrawDesc>(workspace, pl.off_desc);
+
+  if (launch_rowstats(rs, dtype, pl.nchunk, pl.chunk_elems, c, part, stream) != hipSuccess)
+    return PSISPEC_EHIP;
+  if (launch_draft_rows(rs, batch, B, fft ? 1 : 0, part, pl.nchunk, c, rowstat, desc, stream) !=
+      hipSuccess)
+    return PSISPEC_EHIP;
+  if (use_topp && launch_topp(rs, dtype, pl.nchunk, c, s->top_p, part, topp, stream, rowstat) !=
+                      hipSuccess)
+    return PSISPEC_EHIP;
+
+  DrawArgs da{};
+  da.rs = rs;
+  da.batch = (int)jobs;
+  da.V = V;
+  da.nchunk_draw = pl.nchunk_draw;
+  da.chunk_elems_draw = pl.chunk_elems_draw;
+  da.nsub = pl.nsub;
+  da.inv_T = 1.0 / T;
+  da.use_topp = use_topp;
+  da.seed = s->seed;
+  da.step = s->step;
+  da.request_base = s->request_base;
+  da.rowstat = rowstat;
+  da.topp = topp;
+  da.desc = desc;
+  da.excl = nullptr;
+  da.excl_stride = 0;
+  da.esum = carve<double2>(workspace, pl.off_esum);
+  da.subsum = carve<double>(workspace, pl.off_subsum);
+  da.suba = carve<double2>(workspace, pl.off_suba);
+  da.subn = carve<int32_t>(workspace, pl.off_subn);
+  da.suboff = carve<int32_t>(workspace, pl.off_suboff);
+  da.upool = nullptr;  // draws without a q row keep no pool
+  da.ucount = carve<int32_t>(workspace, pl.off_ucount);
+  da.out_tokens = draft_tokens;
   da.status = status;
   if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
   return PSISPEC_OK;
@@ -518,7 +603,8 @@ psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, cons
   if (launch_lmhead(ha, stream) != hipSuccess) return PSISPEC_EHIP;
 
   // the verify itself, on the fp32 logits, with the epilogue's row pairs (one per column tile)
-  RowSet rs{L, L + (int64_t)nP * V, nP, nQ, V, B, (s->flags & PSISPEC_FIRST_FROM_TARGET) ? 1 : 0};
+  RowSet rs{L, L + (int64_t)nP * V, nP, nQ, V, B, (s->flags & PSISPEC_FIRST_FROM_TARGET) ? 1 : 0,
+            V};
   RowStat* rowstat = carve<RowStat>(workspace, pl.off_rowstat);
   ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
   DrawDesc* desc = carve<DrawDesc>(workspace, pl.off_desc);

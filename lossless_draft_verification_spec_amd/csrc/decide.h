@@ -178,6 +178,8 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
     dd.st = st;
     dd.nexcl = 0;
     dd.out_idx = (int32_t)((int64_t)r * Bp1 + k);
+    dd.ph_req = r;
+    dd.purpose = kPurposeDraw;
     a.desc[r] = dd;
     a.ucount[r] = 0;
   }

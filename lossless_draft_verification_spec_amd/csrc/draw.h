@@ -319,7 +319,7 @@ __device__ inline void draw_select_request(const DrawArgs& a, int r) {
   // 1. mass of every sub-chunk: the positive-token sums plus its uncertain tokens (their pool
   //    segment is in token order, so the sum order is fixed); token-by-token sums only for
   //    sub-chunks whose segment did not fit and when the classification is void
-  const double2* pool = a.upool + (int64_t)r * kUncPool;
+  const double2* pool = a.upool ? a.upool + (int64_t)r * kUncPool : nullptr;
   const int32_t* suboff = a.suboff + (int64_t)r * a.nsub;
   for (int j = threadIdx.x; j < a.nsub; j += kThreads) {
     const double2 A = suba[j];
@@ -362,8 +362,8 @@ __device__ inline void draw_select_request(const DrawArgs& a, int r) {
   __syncthreads();
 
   // 2. locate u' S among the sub-chunks: each thread owns a contiguous run of them
-  const double u = philox_uniform(a.seed, a.request_base + (uint32_t)r, (uint32_t)d.pos,
-                                  kPurposeDraw, a.step);
+  const double u = philox_uniform(a.seed, a.request_base + (uint32_t)d.ph_req, (uint32_t)d.pos,
+                                  (uint32_t)d.purpose, a.step);
   const int per = (a.nsub + kThreads - 1) / kThreads;
   const int j0 = min(a.nsub, threadIdx.x * per), j1 = min(a.nsub, j0 + per);
   double mine = 0.0;

@@ -51,7 +51,8 @@ hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t strea
   if (a.batch == 0) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)a.batch * a.nchunk_draw);
   const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
-  const int vec_ok = ((size_t)a.V * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
+  const int vec_ok = ((size_t)a.V * es) % 16 == 0 &&
+                     ((size_t)a.rs.pstride * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
                      ((uintptr_t)a.rs.q % 16) == 0;
   timing_begin("draw_pass", stream);
   if (dtype == PSISPEC_BF16)

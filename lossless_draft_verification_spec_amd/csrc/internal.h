@@ -18,17 +18,19 @@ constexpr int kSub = 1024;          // tokens per sub-chunk of the fp64 residual
 constexpr int kUncPool = 8192;     // uncertain-sign residual tokens kept per request
 constexpr float kNegBig = -3.40282346638528859812e+38f;  // running-max floor (finite: -inf - floor = -inf)
 
-enum : uint32_t { kPurposeAccept = 0, kPurposeDraw = 1 };
+enum : uint32_t { kPurposeAccept = 0, kPurposeDraw = 1, kPurposeDraft = 2 };
 
-// Rows of one call: rows [0, nP) live in p, rows [nP, nP + nQ) in q, each V contiguous elements.
+// Rows of one call: rows [0, nP) live in p, pstride elements apart; rows [nP, nP + nQ) in q, V
+// elements apart; each row holds V contiguous elements.
 struct RowSet {
   const void* p;
   const void* q;
   int64_t nP;
   int64_t nQ;
   int V;
-  int qB;        // q rows per request (linear: B), used to skip position-0 q rows
-  int skip_q0;   // 1: q rows at position 0 are not read (first-from-target layout)
+  int qB;          // q rows per request (linear: B), used to skip position-0 q rows
+  int skip_q0;     // 1: q rows at position 0 are not read (first-from-target layout)
+  int64_t pstride; // elements from one p row to the next (V for packed rows)
 };
 
 // Per-row softmax statistics of the raw logits: lmax = max logit, Z = sum exp((l - lmax) / T).
@@ -54,6 +56,8 @@ struct DrawDesc {
   int32_t st;       // status bits found before the draw
   int32_t nexcl;    // number of excluded tokens
   int32_t out_idx;  // where the drawn token goes in out_tokens (flat index), -1 = nowhere
+  int32_t ph_req;   // Philox counter word 0 is request_base + ph_req
+  int32_t purpose;  // Philox counter word 2
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -97,7 +101,7 @@ __device__ inline float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.bi
 
 template <typename T>
 __device__ inline const T* row_ptr(const RowSet& rs, int64_t row) {
-  if (row < rs.nP) return static_cast<const T*>(rs.p) + row * (int64_t)rs.V;
+  if (row < rs.nP) return static_cast<const T*>(rs.p) + row * rs.pstride;
   return static_cast<const T*>(rs.q) + (row - rs.nP) * (int64_t)rs.V;
 }
 

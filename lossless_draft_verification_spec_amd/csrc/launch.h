@@ -46,6 +46,11 @@ hipError_t launch_decide_linear(const LinearArgs& a, psispec_dtype dtype, hipStr
 hipError_t launch_combine_rows(const RowSet& rs, const float2* part, int nchunk, float c,
                                RowStat* rowstat, hipStream_t stream);
 
+// drafts.hip -- per drafted token: its row's statistics from the row-pass pairs and its draw
+hipError_t launch_draft_rows(const RowSet& rs, int batch, int B, int first_from_target,
+                             const float2* part, int nchunk, float c, RowStat* rowstat,
+                             DrawDesc* desc, hipStream_t stream);
+
 // tree.hip
 struct TreeArgs {
   RowSet rs;
@@ -70,7 +75,7 @@ struct TreeArgs {
 };
 hipError_t launch_decide_tree(const TreeArgs& a, psispec_dtype dtype, hipStream_t stream);
 
-// resample.hip -- the fp64 final draw shared by both entry points
+// draw.hip -- the fp64 inverse-CDF draw shared by the verify entry points and the drafting step
 struct DrawArgs {
   RowSet rs;
   int batch, V, nchunk_draw, chunk_elems_draw, nsub;

@@ -29,7 +29,8 @@ hipError_t launch_rowstats(const RowSet& rs, psispec_dtype dtype, int nchunk, in
   const int64_t tasks = (rs.nP + rs.nQ) * (int64_t)nchunk;
   if (tasks == 0) return hipSuccess;
   const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
-  const int vec_ok = ((size_t)rs.V * es) % 16 == 0 && ((uintptr_t)rs.p % 16) == 0 &&
+  const int vec_ok = ((size_t)rs.V * es) % 16 == 0 && ((size_t)rs.pstride * es) % 16 == 0 &&
+                     ((uintptr_t)rs.p % 16) == 0 &&
                      ((uintptr_t)rs.q % 16) == 0 && (chunk_elems % 8) == 0;
   timing_begin("rowstats", stream);
   if (dtype == PSISPEC_BF16)

@@ -136,7 +136,8 @@ hipError_t launch_topp(const RowSet& rs, psispec_dtype dtype, int nchunk, float 
   double pmin = (1.0 - top_p) / (4.0 * (double)rs.V);
   if (pmin < 1e-30) pmin = 0.0;
   const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
-  const int vec_ok = ((size_t)rs.V * es) % 16 == 0 && ((uintptr_t)rs.p % 16) == 0 &&
+  const int vec_ok = ((size_t)rs.V * es) % 16 == 0 && ((size_t)rs.pstride * es) % 16 == 0 &&
+                     ((uintptr_t)rs.p % 16) == 0 &&
                      ((uintptr_t)rs.q % 16) == 0;
   timing_begin("topp", stream);
   if (dtype == PSISPEC_BF16)

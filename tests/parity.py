@@ -175,3 +175,39 @@ def oracle_tree_requests(p_host, parent, tokens, rows, max_depth, T, top_p, seed
                                top_p=top_p, seed=seed, step=step, request_base=request_base + r)
         outs.append(o)
     return {k: np.concatenate([o[k] for o in outs]) for k in outs[0]}
+
+
+def compare_drafts(tally: Tally, g_tokens, g_status, o: dict, rows, top_p: float):
+    """Drafting step: every drafted token is one draw decision (plus one nucleus decision per row
+    with top-p).  g_tokens/g_status: GPU [batch][B]; o: oracle outputs of the requests `rows`."""
+    for j, r in enumerate(rows):
+        tally.requests += 1
+        for i in range(g_tokens.shape[1]):
+            sg, so = int(g_status[r, i]), int(o["status"][j, i])
+            if sg or so:
+                tally.status_requests += 1
+                if not _status_equal(sg, so):
+                    tally.failures.append(("status", r, i, sg, so))
+                continue
+            ms, mt = o["margin_sample"][j, i], o["margin_topp"][j, i]
+            tally.decisions += 2 if top_p < 1.0 else 1
+            tally.near_ties += int(ms < TIE) + int(top_p < 1.0 and mt < TIE)
+            gt, ot = int(g_tokens[r, i]), int(o["tokens"][j, i])
+            if gt != ot:
+                if ms < TIE or (top_p < 1.0 and mt < TIE):
+                    tally.tolerated += 1
+                else:
+                    tally.failures.append(("draft", r, i, gt, ot, float(ms)))
+
+
+def oracle_draft_requests(ar_host, q_host, rows, T, top_p, seed, step, flags=0, request_base=0):
+    """Oracle drafting for the listed requests (each with its own global request id); ar_host is
+    [batch][k][V] (row 0 read) or None."""
+    outs = []
+    for r in rows:
+        o = oracle.sample_drafts(None if ar_host is None else ar_host[r:r + 1],
+                                 None if q_host is None else q_host[r:r + 1], B=1, T=T,
+                                 top_p=top_p, seed=seed, step=step, request_base=request_base + r,
+                                 flags=flags)
+        outs.append(o)
+    return {k: np.concatenate([o[k] for o in outs]) for k in outs[0]}
