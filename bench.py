@@ -14,7 +14,8 @@ One JSON line is printed: verified rows/s (batch*B per step) as `value`, committ
 roofline of the dominant kernel (the HBM pass, timed with HIP events on the library's stream), the
 oracle timed on the host cores as `cpu_baseline`, the batch-256 B=8 shape as `target_shape`, the
 LM head + verify (batch 128, B=8, H=4096, rank-16 LoRA) with its MFMA roofline as `lmhead`, and the
-32-node tree verify as `tree`.  `--workload c3|c4|c5` prints the top-p, tree or LM-head line alone.
+32-node tree verify as `tree`, and the drafting step (batch 64, B=8, Uno layout) as `drafts`.
+`--workload c3|c4|c5|drafts` prints the top-p, tree, LM-head or drafting line alone.
 """
 from __future__ import annotations
 
@@ -36,13 +37,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=["c2", "ns", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c2", "ns", "c3", "c4", "c5", "drafts"])
     ap.add_argument("--no-lmhead", action="store_true", help="skip the fused LM-head measurement")
     ap.add_argument("--lmhead-steps", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-target", action="store_true", help="skip the batch-256 target shape")
     ap.add_argument("--no-tree", action="store_true", help="skip the tree verify measurement")
     ap.add_argument("--tree-steps", type=int, default=100)
+    ap.add_argument("--no-drafts", action="store_true", help="skip the drafting-step measurement")
+    ap.add_argument("--draft-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for counter scaling)")
@@ -180,6 +183,66 @@ def run_tree(steps, warmup, torch, pkg, workloads, name="c4"):
                           "bytes_per_launch": row_bytes, "avg_launch_us": round(rs_us, 2)})
 
 
+def run_drafts(steps, warmup, torch, pkg, workloads, name="c2"):
+    """Time psispec_sample_drafts on the batch-64, B=8, V=151936 bf16 block in the Uno layout: d_0
+    from the AR row (row 0 of the verify's p tensor, read in place), d_1..d_7 from q rows 1..7.
+    Rotation sets exceed the last-level cache.  HBM roofline of the bounded fp32 pass, which reads
+    the B sampled rows of every request once; the exact fp64 kernels that settle the remaining
+    draws are timed beside it (draw_pass, draw_select)."""
+    preset = workloads.PRESETS[name]
+    R = preset.rotations
+    t0 = time.time()
+    sets = [workloads.make_linear(preset, device="cuda", rotation=i, steps=0) for i in range(R)]
+    torch.cuda.synchronize()
+    log(f"drafts ({name}): generated {R} rotation sets in {time.time() - t0:.1f}s")
+    b, B, V = preset.batch, preset.B, preset.V
+    elem = 2 if preset.dtype == torch.bfloat16 else 4
+    dt = pkg.PSISPEC_BF16 if elem == 2 else pkg.PSISPEC_F32
+    ws = torch.empty(pkg.drafts_workspace_bytes(b, B, V, dt), dtype=torch.uint8, device="cuda")
+    out = dict(draft_tokens=torch.empty(b, B, dtype=torch.int32, device="cuda"),
+               status=torch.empty(b, B, dtype=torch.int32, device="cuda"))
+    F = pkg.PSISPEC_FIRST_FROM_TARGET
+
+    def step(s):
+        inp = sets[s % R]
+        pkg.psispec_sample_drafts(inp.q, ar_logits=inp.p, temperature=preset.T, top_p=preset.top_p,
+                                  seed=inp.seed, step=s, flags=F, workspace=ws, out=out)
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for s in range(warmup, warmup + steps):
+        step(s)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    pkg.timing_enable(True)
+    for s in range(warmup, warmup + steps):
+        step(s)
+    kern = pkg.timing_read()
+    pkg.timing_enable(False)
+    row_bytes = b * B * V * elem  # every sampled row read once
+    k_us = {k: 1e3 * v[0] / max(1, v[1]) for k, v in kern.items()}
+    bd_us = k_us.get("draft_bounds", 0.0)
+    del sets
+    torch.cuda.empty_cache()
+    gbs = row_bytes / (bd_us / 1e6) / 1e9 if bd_us > 0 else 0.0
+    return dict(workload=f"drafts ({name}): Uno-layout drafting batch={b} B={B} V={V} "
+                         f"{'bf16' if elem == 2 else 'fp32'} logits, T={preset.T}, "
+                         f"top_p={preset.top_p}",
+                ms_per_step=round(ms / steps, 4),
+                drafted_tokens_per_s=round(steps * b * B / (ms / 1e3), 1),
+                hbm_gbs_step=round(row_bytes / (ms / steps / 1e3) / 1e9, 1),
+                kernels_avg_us={k: round(v, 2) for k, v in k_us.items()},
+                roofline={"bound": "hbm", "kernel": "k_draft_bounds", "achieved": round(gbs, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "traffic": read_traffic("draft_bounds", name),
+                          "bytes_per_launch": row_bytes, "avg_launch_us": round(bd_us, 2)})
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, datasheet
 
 
@@ -239,11 +302,19 @@ def run_lmhead(steps, warmup, torch, pkg, workloads):
                           "flops_per_launch": flops, "avg_launch_us": round(gemm_us, 2)})
 
 
-def rowstats_source_sha():
-    """Hash of the sources the row-pass kernel is built from (kernel, device body, helpers)."""
+# Sources each measured kernel is built from (kernel, device bodies, shared helpers): a counter
+# summary applies only while their hash matches.
+KERNEL_SOURCES = {
+    "rowstats": ("rows.hip", "rows.h", "internal.h"),
+    "draft_bounds": ("drafts.hip", "draw.h", "decide.h", "launch.h", "internal.h"),
+}
+
+
+def source_sha(kernel="rowstats"):
+    """Hash of the sources the kernel is built from."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("rows.hip", "rows.h", "internal.h"):
+    for f in KERNEL_SOURCES[kernel]:
         h.update(open(os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -259,7 +330,7 @@ def read_traffic(kernel, workload):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256_16") != rowstats_source_sha():
+    if kv.get("source_sha256_16") != source_sha(kernel):
         return None
     try:
         return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
@@ -331,6 +402,9 @@ def main():
     if args.workload == "c4":
         print(json.dumps(run_tree(args.tree_steps, 5, torch, pkg, workloads)), flush=True)
         return
+    if args.workload == "drafts":
+        print(json.dumps(run_drafts(args.draft_steps, 5, torch, pkg, workloads)), flush=True)
+        return
     res, host = run_workload(args.workload, args.steps, args.warmup, torch, pkg, workloads)
     pr = res["preset"]
     log(f"{args.workload}: {res['ms_per_step'] * 1e3:.1f} us/step, kernels {res['kernels']}")
@@ -356,6 +430,10 @@ def main():
     if not args.no_tree:
         tree = run_tree(args.tree_steps, 5, torch, pkg, workloads)
         log(f"c4: {tree['ms_per_step'] * 1e3:.1f} us/step, kernels {tree['kernels_avg_us']}")
+    drafts = None
+    if not args.no_drafts:
+        drafts = run_drafts(args.draft_steps, 5, torch, pkg, workloads)
+        log(f"drafts: {drafts['ms_per_step'] * 1e3:.1f} us/step, kernels {drafts['kernels_avg_us']}")
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(host, pr, args.cpu_seconds)
@@ -392,6 +470,7 @@ def main():
         "target_shape": target,
         "lmhead": lmhead,
         "tree": tree,
+        "drafts": drafts,
     }
     print(json.dumps(line), flush=True)
 

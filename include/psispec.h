@@ -147,8 +147,10 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
  * block, the diffusion path proposes the others in parallel).  Draws d_0..d_{B-1} of every request,
  * each from its row after the transform the verify applies (softmax(logits / temperature), then the
  * nucleus of mass top_p, renormalised): the verify is lossless only for drafts drawn from exactly
- * that q'.  Each draw is an inverse CDF by ascending token id, computed in fp64 like the verify's
- * final draw, with the Philox uniform of (request_base + request, i, purpose 2 = draft, step).
+ * that q'.  Each draw is an inverse CDF by ascending token id with the Philox uniform of
+ * (request_base + request, i, purpose 2 = draft, step), decided as in exact arithmetic: an fp32 pass
+ * with a rigorous error bound settles a draw when the bound cannot change it, the others are drawn
+ * in fp64 like the verify's final draw.
  *
  *   ar_logits    AR rows, read only with PSISPEC_FIRST_FROM_TARGET (may be NULL otherwise): the row
  *                of request r starts at element r * ar_stride; d_0 is drawn from it.  ar_stride >= V

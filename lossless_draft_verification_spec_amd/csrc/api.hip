@@ -26,7 +26,7 @@ struct Plan {
   int nchunk, chunk_elems;          // main pass split of a row
   int nchunk_draw, chunk_elems_draw, nsub;
   size_t off_part, off_rowstat, off_topp, off_desc, off_excl, off_esum, off_suba, off_subn,
-      off_subsum, off_suboff, off_upool, off_ucount, off_extra;
+      off_subsum, off_suboff, off_upool, off_ucount, off_rec, off_list, off_extra;
   size_t total;
 };
 
@@ -36,8 +36,9 @@ struct Plan {
 // (multiples of 64 elements).
 // rows: rows of the HBM pass; batch: draws (one per request, or one per drafted token); pool: the
 // draws have a q row (residual draws keep a pool of uncertain-sign tokens).
+// bounded: the drafting step's fp32 sub-chunk records and its list of unsettled draws.
 Plan make_plan(int64_t rows, int64_t batch, int V, size_t es, int excl_stride, int fixed_nchunk = 0,
-               bool pool = true) {
+               bool pool = true, bool bounded = false) {
   Plan pl{};
   const size_t row_bytes = (size_t)V * es;
   int nchunk = (int)((row_bytes + 131071) / 131072);
@@ -84,6 +85,11 @@ Plan make_plan(int64_t rows, int64_t batch, int V, size_t es, int excl_stride, i
   off = align_up(off + (pool ? sizeof(double2) * (size_t)batch * kUncPool : 0));
   pl.off_ucount = off;
   off = align_up(off + sizeof(int32_t) * (size_t)batch);
+  pl.off_rec = off;
+  off = align_up(off + (bounded ? sizeof(BoundRec) * (size_t)batch * pl.nsub : 0));
+  // the count, then (256 bytes on) the list of draws left to the exact pass
+  pl.off_list = off;
+  off = align_up(off + (bounded ? kAlign + sizeof(int32_t) * (size_t)batch : 0));
   pl.total = off;
   pl.off_extra = off;
   return pl;
@@ -434,7 +440,7 @@ size_t psispec_sample_drafts_workspace(int32_t batch, int32_t B, int32_t V, psis
   if (batch < 0 || B < 1 || B > 64 || V < 1) return 0;
   if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return 0;
   const int64_t rows = (int64_t)batch * (B + 1), jobs = (int64_t)batch * B;
-  return make_plan(rows, jobs, V, elem_size(dtype), 0, 0, false).total + kAlign;
+  return make_plan(rows, jobs, V, elem_size(dtype), 0, 0, false, true).total + kAlign;
 }
 
 psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
@@ -451,7 +457,7 @@ psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
   if (fft && (!ar_logits || ar_stride < V)) return PSISPEC_EINVAL;
   if (!q_logits && !(fft && B == 1)) return PSISPEC_EINVAL;
   const int64_t rows_plan = (int64_t)batch * (B + 1), jobs = (int64_t)batch * B;
-  const Plan pl = make_plan(rows_plan, jobs, V, elem_size(dtype), 0, 0, false);
+  const Plan pl = make_plan(rows_plan, jobs, V, elem_size(dtype), 0, 0, false, true);
   if (rows_plan * pl.nchunk > INT32_MAX || jobs * pl.nchunk_draw > INT32_MAX) return PSISPEC_EINVAL;
   if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace % kAlign) != 0)
     return PSISPEC_EWORKSPACE;
@@ -470,14 +476,46 @@ psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
   ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
   DrawDesc* desc = carve<DrawDesc>(workspace, pl.off_desc);
 
-  if (launch_rowstats(rs, dtype, pl.nchunk, pl.chunk_elems, c, part, stream) != hipSuccess)
-    return PSISPEC_EHIP;
-  if (launch_draft_rows(rs, batch, B, fft ? 1 : 0, part, pl.nchunk, c, rowstat, desc, stream) !=
-      hipSuccess)
-    return PSISPEC_EHIP;
-  if (use_topp && launch_topp(rs, dtype, pl.nchunk, c, s->top_p, part, topp, stream, rowstat) !=
-                      hipSuccess)
-    return PSISPEC_EHIP;
+  // The bounded fp32 pass settles most draws (sub-chunk masses in LDS: V <= 2M tokens); the exact
+  // fp64 draw takes the rest.  The row statistics are needed first only for the nucleus, or when
+  // every draw takes the exact path.
+  const bool bounded = pl.nsub <= kMassLds;
+  int32_t* count = carve<int32_t>(workspace, pl.off_list);
+  int32_t* list = carve<int32_t>(workspace, pl.off_list + kAlign);
+  if (use_topp || !bounded) {
+    if (launch_rowstats(rs, dtype, pl.nchunk, pl.chunk_elems, c, part, stream) != hipSuccess)
+      return PSISPEC_EHIP;
+    if (launch_draft_rows(rs, batch, B, fft ? 1 : 0, part, pl.nchunk, c, rowstat, desc, stream) !=
+        hipSuccess)
+      return PSISPEC_EHIP;
+    if (use_topp && launch_topp(rs, dtype, pl.nchunk, c, s->top_p, part, topp, stream, rowstat) !=
+                        hipSuccess)
+      return PSISPEC_EHIP;
+  }
+  if (bounded) {
+    DraftArgs fa{};
+    fa.rs = rs;
+    fa.batch = batch;
+    fa.B = B;
+    fa.V = V;
+    fa.nsub = pl.nsub;
+    fa.first_from_target = fft ? 1 : 0;
+    fa.c = c;
+    fa.inv_T = 1.0 / T;
+    fa.use_topp = use_topp;
+    fa.seed = s->seed;
+    fa.step = s->step;
+    fa.request_base = s->request_base;
+    fa.topp = topp;
+    fa.rowstat = rowstat;
+    fa.desc = desc;
+    fa.rec = carve<BoundRec>(workspace, pl.off_rec);
+    fa.list = list;
+    fa.count = count;
+    fa.out_tokens = draft_tokens;
+    fa.status = status;
+    if (launch_draft_bounded(fa, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
+  }
 
   DrawArgs da{};
   da.rs = rs;
@@ -505,6 +543,8 @@ psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
   da.ucount = carve<int32_t>(workspace, pl.off_ucount);
   da.out_tokens = draft_tokens;
   da.status = status;
+  da.list = bounded ? list : nullptr;  // the draws the bounded pass could not settle
+  da.count = bounded ? count : nullptr;
   if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
   return PSISPEC_OK;
 }

@@ -80,7 +80,6 @@ __device__ inline double term(float l, float lmax, float thr, double inv_T, cons
 
 constexpr double kBand = 1e-5;  // relative band of uncertain residual signs
 constexpr int kEsLds = 512;     // chunk normaliser pairs staged in LDS by the select
-constexpr int kMassLds = 2048;  // sub-chunk masses kept in LDS by the select (V <= 2M tokens)
 
 __device__ inline bool excluded(int x, const int* excl, int nexcl) {
   for (int i = 0; i < nexcl; ++i)

@@ -36,20 +36,47 @@ namespace {
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_draw_pass(DrawArgs a, int vec_ok) {
-  const int r = blockIdx.x / a.nchunk_draw;
-  draw_pass_task<T>(a, r, blockIdx.x - r * a.nchunk_draw, vec_ok);
+  if (!a.list) {
+    const int r = blockIdx.x / a.nchunk_draw;
+    draw_pass_task<T>(a, r, blockIdx.x - r * a.nchunk_draw, vec_ok);
+    return;
+  }
+  // listed draws only: the grid loops over (list entry, chunk) pairs
+  const int n = *a.count * a.nchunk_draw;
+  for (int w = blockIdx.x; w < n; w += gridDim.x) {
+    const int e = w / a.nchunk_draw;
+    draw_pass_task<T>(a, a.list[e], w - e * a.nchunk_draw, vec_ok);
+    __syncthreads();  // the next task refills the block's LDS
+  }
 }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_draw_select(DrawArgs a) {
-  draw_select_request<T>(a, blockIdx.x);
+  if (!a.list) {
+    draw_select_request<T>(a, blockIdx.x);
+    return;
+  }
+  const int n = *a.count;
+  for (int e = blockIdx.x; e < n; e += gridDim.x) {
+    draw_select_request<T>(a, a.list[e]);
+    __syncthreads();
+  }
 }
+
+constexpr unsigned kListPassBlocks = 1024;   // grid of the pass over listed draws
+constexpr unsigned kListSelectBlocks = 256;  // grid of the select over listed draws
+
 
 }  // namespace
 
 hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((int64_t)a.batch * a.nchunk_draw);
+  unsigned grid = (unsigned)((int64_t)a.batch * a.nchunk_draw);
+  unsigned sgrid = (unsigned)a.batch;
+  if (a.list) {
+    grid = grid < kListPassBlocks ? grid : kListPassBlocks;
+    sgrid = sgrid < kListSelectBlocks ? sgrid : kListSelectBlocks;
+  }
   const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
   const int vec_ok = ((size_t)a.V * es) % 16 == 0 &&
                      ((size_t)a.rs.pstride * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
@@ -64,9 +91,9 @@ hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t strea
   if (e != hipSuccess) return e;
   timing_begin("draw_select", stream);
   if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL(k_draw_select<bf16_t>, dim3(a.batch), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_draw_select<bf16_t>, dim3(sgrid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_draw_select<float>, dim3(a.batch), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_draw_select<float>, dim3(sgrid), dim3(kThreads), 0, stream, a);
   timing_end("draw_select", stream);
   return hipGetLastError();
 }

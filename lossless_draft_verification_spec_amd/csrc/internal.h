@@ -16,6 +16,7 @@ namespace psispec {
 constexpr int kThreads = 256;       // workgroup size of the streaming kernels (4 wave64)
 constexpr int kSub = 1024;          // tokens per sub-chunk of the fp64 residual prefix sums
 constexpr int kUncPool = 8192;     // uncertain-sign residual tokens kept per request
+constexpr int kMassLds = 2048;     // sub-chunk masses a select keeps in LDS (V <= 2M tokens)
 constexpr float kNegBig = -3.40282346638528859812e+38f;  // running-max floor (finite: -inf - floor = -inf)
 
 enum : uint32_t { kPurposeAccept = 0, kPurposeDraw = 1, kPurposeDraft = 2 };

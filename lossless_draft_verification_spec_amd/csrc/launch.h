@@ -46,10 +46,38 @@ hipError_t launch_decide_linear(const LinearArgs& a, psispec_dtype dtype, hipStr
 hipError_t launch_combine_rows(const RowSet& rs, const float2* part, int nchunk, float c,
                                RowStat* rowstat, hipStream_t stream);
 
-// drafts.hip -- per drafted token: its row's statistics from the row-pass pairs and its draw
+// drafts.hip -- the drafting step
+// Per drafted token: its row's statistics from the row-pass pairs and its draw description.
 hipError_t launch_draft_rows(const RowSet& rs, int batch, int B, int first_from_target,
                              const float2* part, int nchunk, float c, RowStat* rowstat,
                              DrawDesc* desc, hipStream_t stream);
+// One sub-chunk of a drafted token's row as summed by the bounded fp32 pass: m = max kept logit,
+// s = sum of 2^((l - m) c) over the kept tokens (fp32 terms, fp64 sum), A = sum of |(l - m) c| times
+// those terms (the argument-rounding part of the error bound).
+struct BoundRec {
+  double s;
+  float m;
+  float A;
+};
+struct DraftArgs {
+  RowSet rs;
+  int batch, B, V, nsub, first_from_target;
+  float c;              // log2(e) / T in fp32
+  double inv_T;         // 1 / T in fp64
+  int use_topp;
+  uint64_t seed;
+  uint32_t step, request_base;
+  const ToppStat* topp;
+  RowStat* rowstat;     // written for the draws left to the exact pass
+  DrawDesc* desc;       // idem
+  BoundRec* rec;        // [batch*B][nsub]
+  int32_t* list;        // [batch*B] the draws left to the exact pass, in no particular order
+  int32_t* count;       // their number (zeroed by the bounded pass)
+  int32_t* out_tokens;  // [batch*B]
+  int32_t* status;      // [batch*B] or null
+};
+// The bounded fp32 pass and the select that settles every draw whose bound allows it.
+hipError_t launch_draft_bounded(const DraftArgs& a, psispec_dtype dtype, hipStream_t stream);
 
 // tree.hip
 struct TreeArgs {
@@ -97,6 +125,10 @@ struct DrawArgs {
   double* subsum;     // [batch][nsub] sub-chunk masses (written by the select)
   int32_t* out_tokens;
   int32_t* status;
+  // null: every draw r < batch.  Otherwise only the draws list[0 .. *count - 1] (draws already
+  // settled elsewhere are skipped); a fixed grid then loops over them.
+  const int32_t* list;
+  const int32_t* count;
 };
 hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t stream);
 

@@ -97,6 +97,32 @@ def test_drafts_first_from_target_layouts(dtype):
     t.check()
 
 
+@pytest.mark.parametrize("noise", [0.0, 1e-3, 0.05])
+def test_drafts_flat_rows(noise):
+    """Near-uniform rows over the full vocabulary: the cumulative-weight breakpoints are about S / V
+    apart, closer than the bound of the fp32 pass, so many draws are left to the exact fp64 kernels;
+    every token must still match the oracle."""
+    batch, B, V = 4, 4, 151936
+    g = torch.Generator(device="cpu").manual_seed(int(noise * 1e4) + 1)
+    q = (torch.randn(batch, B, V, generator=g) * noise).to(DEV)
+    t = _compare(q, steps=range(4))
+    print(t)
+    t.check()
+    qb = q.to(torch.bfloat16)
+    t = _compare(qb, top_p=0.9, steps=range(2))
+    t.check()
+
+
+def test_drafts_vocab_beyond_bounded_pass():
+    """V > 2^21 tokens: more sub-chunks than the bounded select keeps in LDS, so every draw takes the
+    exact fp64 kernels (whose select then keeps its sub-chunk masses in the workspace)."""
+    _, q = _rand_rows(1, 2, 2100000, torch.bfloat16, seed=21)
+    t = _compare(q, steps=range(2))
+    t.check()
+    t = _compare(q, top_p=0.95, steps=range(1))
+    t.check()
+
+
 def test_drafts_seed_step_request_base_extremes():
     _, q = _rand_rows(4, 4, 777, torch.float32, seed=6)
     t = _compare(q, seed=2**64 - 1, steps=(0, 9, 2**32 - 1), request_base=2**32 - 2)
