@@ -15,7 +15,8 @@ roofline of the dominant kernel (the HBM pass, timed with HIP events on the libr
 oracle timed on the host cores as `cpu_baseline`, the batch-256 B=8 shape as `target_shape`, the
 LM head + verify (batch 128, B=8, H=4096, rank-16 LoRA) with its MFMA roofline as `lmhead`, and the
 32-node tree verify as `tree`, and the drafting step (batch 64, B=8, Uno layout) as `drafts`.
-`--workload c3|c4|c5|drafts` prints the top-p, tree, LM-head or drafting line alone.
+`--workload c3|c4|c5|drafts` prints the top-p, tree, LM-head or drafting line alone;
+`--workload sweep` prints the linear-vs-tree batch sweep (batch 1..256).
 """
 from __future__ import annotations
 
@@ -37,7 +38,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=["c2", "ns", "c3", "c4", "c5", "drafts"])
+    ap.add_argument("--workload", default="c2",
+                    choices=["c2", "ns", "c3", "c4", "c5", "drafts", "sweep"])
+    ap.add_argument("--sweep-batches", default="1,2,4,8,16,32,64,128,256",
+                    help="batch sizes of the linear-vs-tree sweep")
+    ap.add_argument("--sweep-steps", type=int, default=40)
+    ap.add_argument("--sweep-noise", type=float, default=1.0,
+                    help="draft noise sigma of the sweep (draft = target + N(0, sigma^2))")
+    ap.add_argument("--sweep-boost", type=float, default=1.0,
+                    help="Zipf boost scale of the sweep's target rows (2: concentrated rows)")
     ap.add_argument("--no-lmhead", action="store_true", help="skip the fused LM-head measurement")
     ap.add_argument("--lmhead-steps", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -243,6 +252,91 @@ def run_drafts(steps, warmup, torch, pkg, workloads, name="c2"):
                           "bytes_per_launch": row_bytes, "avg_launch_us": round(bd_us, 2)})
 
 
+def _time_calls(torch, pkg, call, steps, warmup):
+    """Mean device time per call (torch events over `steps` calls after `warmup`), the summed
+    outputs of the timed calls, and the library's per-kernel mean times (a second pass)."""
+    for s in range(warmup):
+        call(s)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    outs = []
+    ev0.record()
+    for s in range(warmup, warmup + steps):
+        outs.append(call(s))
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    pkg.timing_enable(True)
+    for s in range(warmup, warmup + steps):
+        call(s)
+    kern = pkg.timing_read()
+    pkg.timing_enable(False)
+    return ms / steps, outs, {k: 1e3 * v[0] / max(1, v[1]) for k, v in kern.items()}
+
+
+def run_sweep(batches, steps, torch, pkg, workloads, noise=1.0, boost=1.0):
+    """Linear vs tree verify over batch sizes at fixed B=8 (linear) and N=32, depth <= 8, top-4
+    (tree), V=151936 bf16, one draft/target model for both (N(0, 3^2) target rows plus `boost` times
+    the Zipf boost, draft = target + N(0, noise^2)).  Each point cycles rotation sets totalling >= 600 MB so every
+    call reads its rows from HBM.  Per point: device time per call, committed tokens per call and per
+    second, rows read per call and the row pass's share of HBM peak."""
+    from dataclasses import replace
+    pl = replace(workloads.PRESETS["sweep_linear"], sigmas=(noise,), boost=boost)
+    pt = replace(workloads.PRESETS["sweep_tree"], q_noise=noise, boost=boost)
+    V, B, N = pl.V, pl.B, pt.N
+    points = []
+    for b in batches:
+        lin_bytes, tree_bytes = b * (2 * B + 1) * V * 2, b * (N + 1) * V * 2
+        R = max(2, min(64, -(-600_000_000 // lin_bytes)))
+        sets = [workloads.make_linear(pl, device="cuda", rotation=i, batch=b,
+                                      steps=(steps + 3) // R + 2) for i in range(R)]
+        ws = torch.empty(pkg.linear_workspace_bytes(b, B, V, pkg.PSISPEC_BF16), dtype=torch.uint8,
+                         device="cuda")
+
+        def lin(s):
+            inp = sets[s % R]
+            return pkg.psispec_verify_linear(inp.p, inp.q, inp.drafts[s // R], seed=inp.seed,
+                                             step=s, workspace=ws)["accept_len"]
+
+        ms_l, acc_l, k_l = _time_calls(torch, pkg, lin, steps, 3)
+        com_l = float(sum((a.to(torch.int64) + 1).sum().item() for a in acc_l)) / steps
+        del sets, ws
+        Rt = max(2, min(64, -(-600_000_000 // tree_bytes)))
+        tsets = [workloads.make_tree(pt, device="cuda", rotation=i, batch=b) for i in range(Rt)]
+        wst = torch.empty(pkg.tree_workspace_bytes(b, N, V, pkg.PSISPEC_BF16), dtype=torch.uint8,
+                          device="cuda")
+
+        def tree(s):
+            inp = tsets[s % Rt]
+            return pkg.psispec_verify_tree(inp.p, inp.parent, inp.node_tokens, pt.depth,
+                                           seed=inp.seed, step=s, workspace=wst)["accept_len"]
+
+        ms_t, acc_t, k_t = _time_calls(torch, pkg, tree, steps, 3)
+        com_t = float(sum((a.to(torch.int64) + 1).sum().item() for a in acc_t)) / steps
+        del tsets, wst
+        torch.cuda.empty_cache()
+
+        def leg(ms, com, rows, nbytes, k):
+            rs = k.get("rowstats", 0.0)
+            return dict(us_per_call=round(1e3 * ms, 2), committed_per_call=round(com, 3),
+                        committed_tokens_per_s=round(com / (ms / 1e3), 1), rows_per_call=rows,
+                        rowstats_us=round(rs, 2),
+                        rowstats_frac_of_hbm_peak=round(nbytes / (rs / 1e6) / 1e9 / HBM_PEAK_GBS, 4)
+                        if rs > 0 else None,
+                        kernels_avg_us={kk: round(v, 2) for kk, v in k.items()})
+
+        pt_ = dict(batch=b, linear=leg(ms_l, com_l, b * (2 * B + 1), lin_bytes, k_l),
+                   tree=leg(ms_t, com_t, b * (N + 1), tree_bytes, k_t))
+        log(f"sweep batch {b}: linear {pt_['linear']['us_per_call']} us "
+            f"{pt_['linear']['committed_tokens_per_s']:.0f} tok/s; tree {pt_['tree']['us_per_call']} us "
+            f"{pt_['tree']['committed_tokens_per_s']:.0f} tok/s")
+        points.append(pt_)
+    return dict(workload=f"linear (B={B}) vs tree (N={N}, depth<={pt.depth}, top-{pt.k}) verify, "
+                         f"V={V} bf16, N(0,3^2) target rows + {boost} x Zipf boost, draft = "
+                         f"target + N(0,{noise}^2), T=1",
+                steps_per_point=steps, points=points)
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, datasheet
 
 
@@ -401,6 +495,11 @@ def main():
         return
     if args.workload == "c4":
         print(json.dumps(run_tree(args.tree_steps, 5, torch, pkg, workloads)), flush=True)
+        return
+    if args.workload == "sweep":
+        batches = [int(x) for x in args.sweep_batches.split(",") if x]
+        print(json.dumps(run_sweep(batches, args.sweep_steps, torch, pkg, workloads,
+                                   args.sweep_noise, args.sweep_boost)), flush=True)
         return
     if args.workload == "drafts":
         print(json.dumps(run_drafts(args.draft_steps, 5, torch, pkg, workloads)), flush=True)

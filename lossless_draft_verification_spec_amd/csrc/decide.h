@@ -7,7 +7,7 @@ namespace psispec {
 namespace {
 
 constexpr int kMaxB = 64;
-constexpr int kStageChunks = 16;  // row pairs per row staged in LDS (more: the wave-reduce path)
+constexpr int kStagePairs = (2 * kMaxB + 1) * 16;  // row pairs of a request staged in LDS
 
 __device__ inline int row_status(float lmax, double Z) {
   const bool ok = (lmax > kNegBig) && (lmax < __builtin_huge_valf()) && (Z > 0.0) && (Z < 1e300);
@@ -43,10 +43,11 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
   __shared__ float s_lmax[2 * kMaxB + 1];
   __shared__ double s_Z[2 * kMaxB + 1];
   __shared__ int s_st[2 * kMaxB + 1];
-  __shared__ float2 s_pair[(2 * kMaxB + 1) * kStageChunks];
+  __shared__ float2 s_pair[kStagePairs];
 
-  // 1. finish the row statistics (rows 0..B of p, then rows 0..B-1 of q).  Few chunks: one lane
-  //    per row; many (LM-head column tiles): the wave reduces each row's chunks in a fixed order.
+  // 1. finish the row statistics (rows 0..B of p, then rows 0..B-1 of q).  When the request's pairs
+  //    fit in LDS: one lane per row; else (LM-head column tiles at large B) the wave reduces each
+  //    row's chunks in a fixed order.
   if (t >= 64) {
     // other waves of a larger block only join the barrier
   } else if (a.rowstat_ready) {
@@ -64,7 +65,7 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
       s_Z[j] = rw.Z;
       s_st[j] = rw.st;
     }
-  } else if (a.nchunk <= kStageChunks) {
+  } else if ((2 * B + 1) * a.nchunk <= kStagePairs) {
     // the request's pairs: p rows then q rows, each a contiguous run of the workspace, loaded by
     // the whole wave in one round
     const int np = Bp1 * a.nchunk, nq = B * a.nchunk;

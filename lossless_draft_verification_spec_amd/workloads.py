@@ -33,6 +33,7 @@ class LinearPreset:
     p_std: float = 3.0
     sigmas: tuple = (0.3, 1.0, 2.0)  # draft noise, chosen per request as sigmas[r % len]
     rotations: int = 1
+    boost: float = 1.0  # scale of the Zipf boost (2: rows as concentrated as typical LM outputs)
 
 
 @dataclass(frozen=True)
@@ -51,7 +52,9 @@ class TreePreset:
     p_std: float = 3.0
     q_noise: float = 1.0
     peaked: bool = False  # coverage variant: q = p and Zipf-boosted p, so walks go deep
+    zipf: bool = False    # Zipf-boosted p as in the linear blocks, q = p + N(0, q_noise^2)
     rotations: int = 1
+    boost: float = 1.0    # scale of that Zipf boost
 
 
 @dataclass(frozen=True)
@@ -84,6 +87,12 @@ PRESETS = {
     "c4b": TreePreset("c4b", 8, 32, 8, 4, 151936, steps=20, seed=14, peaked=True),
     # 5: fused LM head: batch 128, B=8, H=4096, rank-16 LoRA on the draft rows
     "c5": LMHeadPreset("c5", 128, 8, 4096, 151936, 16),
+    # linear-vs-tree batch sweep: one draft/target model for both samplers (bf16, Zipf-boosted
+    # N(0, 3^2) target rows, draft = target + N(0, 1)); the batch is set per point of the sweep
+    "sweep_linear": LinearPreset("sweep_linear", 1, 8, 151936, torch.bfloat16, steps=50, seed=7,
+                                 sigmas=(1.0,)),
+    "sweep_tree": TreePreset("sweep_tree", 1, 32, 8, 4, 151936, dtype=torch.bfloat16, steps=50,
+                             seed=8, zipf=True),
 }
 
 
@@ -171,7 +180,7 @@ def make_linear(preset: LinearPreset | str, device="cpu", rotation: int = 0, ste
         p = torch.randn(b, B + 1, V, generator=g, device=device) * preset.p_std
     else:
         p = torch.randn(b, B + 1, V, generator=g, device=device) * preset.p_std
-        p += zipf_boost(b * (B + 1), V, g, device).view(b, B + 1, V)
+        p += zipf_boost(b * (B + 1), V, g, device).view(b, B + 1, V) * preset.boost
     sig = torch.tensor([preset.sigmas[r % len(preset.sigmas)] for r in range(b)], device=device,
                        dtype=torch.float32).view(b, 1, 1)
     q = p[:, :B, :] + sig * torch.randn(b, B, V, generator=g, device=device)
@@ -214,6 +223,9 @@ def make_tree(preset: TreePreset | str, device="cpu", rotation: int = 0, batch=N
     if preset.peaked:
         p += zipf_boost(b * (N + 1), V, g, device).view(b, N + 1, V) * 2.0
         q = p.clone()
+    elif preset.zipf:
+        p += zipf_boost(b * (N + 1), V, g, device).view(b, N + 1, V) * preset.boost
+        q = p + preset.q_noise * torch.randn(b, N + 1, V, generator=g, device=device)
     else:
         q = p + preset.q_noise * torch.randn(b, N + 1, V, generator=g, device=device)
     p = p.to(preset.dtype).contiguous()

@@ -289,3 +289,30 @@ def test_full_size_tree(name):
                       T=pr.T, top_p=pr.top_p, seed=inp.seed, steps=range(3))
     print(name, t)
     t.check()
+
+
+@pytest.mark.parametrize("batch,nreq,boost", [(1, 1, 1.0), (16, 3, 1.0), (256, 4, 1.0), (8, 4, 2.0)])
+def test_sweep_shapes(batch, nreq, boost):
+    """The linear-vs-tree sweep workload (one draft/target model for both samplers, bf16,
+    V = 151,936) at three of its batch sizes, and with concentrated rows (deep tree walks), compared
+    on sampled requests."""
+    from dataclasses import replace
+    rows = list(range(0, batch, max(1, batch // nreq)))[:nreq]
+    pt = replace(workloads.PRESETS["sweep_tree"], boost=boost)
+    pl = replace(workloads.PRESETS["sweep_linear"], boost=boost)
+    tin = workloads.make_tree(pt, device=DEV, batch=batch)
+    t = _tree_compare(tin.p, tin.parent.cpu().numpy(), tin.node_tokens.cpu().numpy(),
+                      tin.preset.depth, seed=tin.seed, steps=(0, 1), rows=rows)
+    print("tree", batch, t)
+    t.check()
+    del tin
+    lin = workloads.make_linear(pl, device=DEV, batch=batch, steps=2)
+    ph, qh = host_logits(lin.p), host_logits(lin.q)
+    tally = Tally()
+    for step, d in enumerate(lin.drafts):
+        out = psispec_verify_linear(lin.p, lin.q, d, seed=lin.seed, step=step)
+        g = gpu_linear_numpy(out)
+        o = oracle_linear_requests(ph, qh, d.cpu().numpy(), rows, 1.0, 1.0, lin.seed, step)
+        compare_linear(tally, g, o, rows, lin.preset.B, 1.0)
+    print("linear", batch, tally)
+    tally.check()
