@@ -23,6 +23,7 @@ F32, BF16, F64 = 0, 1, 2
 FIRST_FROM_TARGET = 1
 PURPOSE_ACCEPT, PURPOSE_RESAMPLE, PURPOSE_DRAFT = 0, 1, 2
 ST_NONFINITE, ST_BAD_TOKEN, ST_Q_ZERO, ST_RESID_ZERO, ST_BAD_PARENT = 1, 2, 4, 8, 16
+ST_BAD_KEEP = 32
 
 
 def build(force: bool = True) -> str:
@@ -62,6 +63,9 @@ def lib():
         L.psispec_oracle_sample_drafts.argtypes = (
             [P, ctypes.c_int64, P, i32, i32, i32, i32, dbl, dbl, u64, u32, u32, u32] + [P] * 5)
         L.psispec_oracle_sample_drafts.restype = i32
+        L.psispec_oracle_kv_commit.argtypes = [P, ctypes.c_int64, ctypes.c_int64, i32, i32, P, i32, P,
+                                               P, P, i32]
+        L.psispec_oracle_kv_commit.restype = i32
         L.psispec_oracle_lmhead_logits.argtypes = [P, P, P, P, dbl, i32, i32, i32, i32, P]
         L.psispec_oracle_lmhead_logits.restype = i32
         _lib = L
@@ -201,6 +205,25 @@ def verify_tree(p, parent, node_tokens, max_depth, T=1.0, top_p=1.0, seed=0, ste
     if rc != 0:
         raise ValueError(f"oracle verify_tree rejected its arguments (code {rc})")
     return out
+
+
+def kv_commit(kv, blk, n_keep, length, keep=None):
+    """KV commit on host arrays.  kv: [batch][Lmax][row] array of any dtype (rows are opaque bytes),
+    changed in place; keep [batch][k] int32 or None (the prefix); n_keep, length [batch] int32
+    (length changed in place).  Returns the status array."""
+    assert kv.flags.c_contiguous
+    batch, Lmax = kv.shape[0], kv.shape[1]
+    row_bytes = kv.strides[1]
+    keep_a = None if keep is None else np.ascontiguousarray(keep, dtype=np.int32)
+    nk = np.ascontiguousarray(n_keep, dtype=np.int32)
+    assert length.dtype == np.int32 and length.flags.c_contiguous
+    st = np.zeros(batch, np.int32)
+    rc = lib().psispec_oracle_kv_commit(
+        _ptr(kv), kv.strides[0], row_bytes, Lmax, blk, _ptr(keep_a),
+        0 if keep_a is None else keep_a.shape[1], _ptr(nk), _ptr(length), _ptr(st), batch)
+    if rc != 0:
+        raise ValueError(f"oracle kv_commit rejected its arguments (code {rc})")
+    return st
 
 
 def lmhead_logits(h, W, A=None, Bl=None, scale=1.0):

@@ -560,3 +560,45 @@ int psispec_oracle_lmhead_logits(const uint16_t* h, const uint16_t* W, const uin
   free(t);
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------------------------------
+ * KV commit after a verify ([lanes] "헤드냐, LoRA냐": the draft and the verify share one KV line per
+ * sequence, the AR verifies and appends; [alphalab] walkthrough step 4: the accepted prefix is kept,
+ * everything after the first rejection is discarded and drafted again next round).  Reading: the
+ * verify forward wrote the KV rows of the block's blk positions at positions len .. len+blk-1 of the
+ * request's line; the kept rows (their block positions keep[0..n-1], strictly increasing) move to
+ * len .. len+n-1 in that order, len grows by n, and the rows past the new length are free again.
+ * The rows are opaque bytes.  A request whose n, keep or len is invalid (n outside [0, blk],
+ * keep not strictly increasing within [0, blk), len < 0 or len + blk > Lmax) is left unchanged and
+ * flagged.
+ * ---------------------------------------------------------------------------------------------- */
+int psispec_oracle_kv_commit(void* kv, int64_t line_stride, int64_t row_bytes, int Lmax, int blk,
+                             const int32_t* keep, int keep_stride, const int32_t* n_keep,
+                             int32_t* len, int32_t* status, int batch) {
+  if (!kv || !n_keep || !len || batch < 0 || row_bytes < 1 || Lmax < 1 || blk < 1 || blk > Lmax)
+    return ORC_EINVAL;
+  if (keep && keep_stride < 1) return ORC_EINVAL;
+  unsigned char* old = (unsigned char*)malloc((size_t)blk * (size_t)row_bytes);
+  for (int r = 0; r < batch; ++r) {
+    int n = n_keep[r], L = len[r];
+    int ok = n >= 0 && n <= blk && L >= 0 && L <= Lmax - blk && (!keep || n <= keep_stride);
+    for (int i = 0; ok && keep && i < n; ++i) {
+      int k = keep[(size_t)r * keep_stride + i];
+      if (k < 0 || k >= blk) ok = 0;
+      if (i > 0 && k <= keep[(size_t)r * keep_stride + i - 1]) ok = 0;
+    }
+    if (status) status[r] = ok ? 0 : ORC_ST_BAD_KEEP;
+    if (!ok) continue;
+    unsigned char* block = (unsigned char*)kv + (size_t)r * (size_t)line_stride +
+                           (size_t)L * (size_t)row_bytes;
+    memcpy(old, block, (size_t)blk * (size_t)row_bytes);
+    for (int i = 0; i < n; ++i) {
+      int k = keep ? keep[(size_t)r * keep_stride + i] : i;
+      memcpy(block + (size_t)i * (size_t)row_bytes, old + (size_t)k * (size_t)row_bytes,
+             (size_t)row_bytes);
+    }
+    len[r] = L + n;
+  }
+  free(old);
+  return ORC_OK;
+}

@@ -43,6 +43,7 @@ extern "C" {
 #define ORC_ST_Q_ZERO 4      /* draft probability of a drafted token is zero */
 #define ORC_ST_RESID_ZERO 8  /* residual mass zero at a rejection: fell back to the target row */
 #define ORC_ST_BAD_PARENT 16 /* tree: parent[j] not in [-1, j-1] or depth beyond max_depth */
+#define ORC_ST_BAD_KEEP 32   /* KV commit: kept count, kept positions or length invalid */
 
 /* return codes */
 #define ORC_OK 0
@@ -92,6 +93,13 @@ int psispec_oracle_verify_tree(const void* p, int dtype, const int32_t* parent,
 int psispec_oracle_lmhead_logits(const uint16_t* h, const uint16_t* W, const uint16_t* A,
                                  const uint16_t* Bl, double scale, int M, int H, int V, int r,
                                  double* out);
+
+/* KV commit: in line r (kv + r * line_stride bytes, rows of row_bytes), the block's rows at
+ * len[r] + keep[r][i] (keep NULL: i) move to len[r] + i for i < n_keep[r]; len[r] += n_keep[r].
+ * status [batch] nullable. */
+int psispec_oracle_kv_commit(void* kv, int64_t line_stride, int64_t row_bytes, int Lmax, int blk,
+                             const int32_t* keep, int keep_stride, const int32_t* n_keep,
+                             int32_t* len, int32_t* status, int batch);
 
 #ifdef __cplusplus
 }
