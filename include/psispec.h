@@ -70,6 +70,7 @@ typedef enum { PSISPEC_F32 = 0, PSISPEC_BF16 = 1 } psispec_dtype;
                                     1 if the target probability is positive, else 0) */
 #define PSISPEC_ST_RESID_ZERO 8  /* residual mass 0 at a rejection: drew from the target row */
 #define PSISPEC_ST_BAD_PARENT 16 /* tree: parent[j] outside [-1, j-1] or depth beyond max_depth */
+#define PSISPEC_ST_BAD_KEEP 32   /* KV commit: kept count, kept positions or length invalid */
 
 typedef struct {
   double temperature;    /* > 0 and finite: logits are divided by it */
@@ -175,6 +176,33 @@ psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
                                      int32_t B, int32_t V, const psispec_sampling* s,
                                      int32_t* draft_tokens, int32_t* status, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/*
+ * KV commit after a verify ([lanes] §"헤드냐, LoRA냐": drafting and verifying share one KV line per
+ * sequence, the AR verifies and appends; [alphalab] walkthrough step 4: the accepted prefix is kept,
+ * the rest is discarded and drafted again).  The verify forward has written the KV rows of the
+ * block's blk positions at positions len[r] .. len[r]+blk-1 of line r.  The kept rows, block
+ * positions keep[r][0..n_keep[r]-1], move to len[r] .. len[r]+n_keep[r]-1 in that order and
+ * len[r] grows by n_keep[r]; the rows past the new length are free (rolled back, untouched).
+ *
+ *   kv           device; line r starts at kv + r * line_stride bytes, position t at
+ *                + t * row_bytes; rows are opaque bytes (any layout of layers, heads and K/V)
+ *   line_stride  bytes, multiple of 16, >= Lmax * row_bytes
+ *   row_bytes    bytes per position, a multiple of 16;  kv 16-byte aligned
+ *   Lmax         positions per line;  blk: 1..min(Lmax, 1024) block positions
+ *   keep         [batch][keep_stride] int32 kept block positions, strictly increasing in [0, blk)
+ *                (the tree verify's accept_nodes as they are, keep_stride = max_depth), or NULL:
+ *                the first n_keep positions (the linear verify: nothing moves)
+ *   n_keep       [batch] int32 in [0, blk] (and <= keep_stride): the verify's accept_len
+ *   len          [batch] int32, in/out, with len + blk <= Lmax
+ *   status       [batch] int32, nullable: PSISPEC_ST_BAD_KEEP when n_keep, keep or len is invalid;
+ *                that request's line and length are then left unchanged
+ * Asynchronous on `stream`; no workspace.  Host-detectable errors return PSISPEC_EINVAL.
+ */
+psispec_status psispec_kv_commit(void* kv, int64_t line_stride, int64_t row_bytes, int32_t Lmax,
+                                 int32_t blk, const int32_t* keep, int32_t keep_stride,
+                                 const int32_t* n_keep, int32_t* len, int32_t* status,
+                                 int32_t batch, void* stream);
 
 /*
  * LM head + linear verify ([lanes] §"헤드냐, LoRA냐": the draft path is the frozen AR weights plus a

@@ -18,11 +18,13 @@ LIB_PATH = os.path.join(_PKG, "libpsispec.so")
 PSISPEC_F32, PSISPEC_BF16 = 0, 1
 PSISPEC_FIRST_FROM_TARGET = 1
 ST_NONFINITE, ST_BAD_TOKEN, ST_Q_ZERO, ST_RESID_ZERO, ST_BAD_PARENT = 1, 2, 4, 8, 16
+ST_BAD_KEEP = 32
 
 EXPORTS = ("psispec_verify_linear_workspace", "psispec_verify_linear",
            "psispec_verify_tree_workspace", "psispec_verify_tree", "psispec_lmhead_verify_workspace",
            "psispec_lmhead_verify", "psispec_sample_drafts_workspace", "psispec_sample_drafts",
-           "psispec_strerror", "psispec_timing_enable", "psispec_timing_read")
+           "psispec_kv_commit", "psispec_strerror", "psispec_timing_enable",
+           "psispec_timing_read")
 
 
 class PsispecError(RuntimeError):
@@ -67,6 +69,9 @@ def lib():
         L.psispec_sample_drafts.argtypes = [P, ctypes.c_int64, P, i32, i32, i32, i32, P, P, P, P, sz,
                                             P]
         L.psispec_sample_drafts.restype = i32
+        L.psispec_kv_commit.argtypes = [P, ctypes.c_int64, ctypes.c_int64, i32, i32, P, i32, P, P, P,
+                                        i32, P]
+        L.psispec_kv_commit.restype = i32
         L.psispec_strerror.argtypes = [i32]
         L.psispec_strerror.restype = ctypes.c_char_p
         L.psispec_timing_enable.argtypes = [i32]
@@ -327,6 +332,40 @@ def psispec_sample_drafts(q_logits: torch.Tensor | None, ar_logits: torch.Tensor
         _stream(stream))
     _check(rc, "psispec_sample_drafts")
     return out
+
+
+def psispec_kv_commit(kv: torch.Tensor, blk: int, n_keep: torch.Tensor, length: torch.Tensor,
+                      keep: torch.Tensor | None = None, status: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor | None:
+    """KV commit after a verify.  kv: contiguous GPU tensor [batch][Lmax][...] (any dtype; a
+    position's row is kv[r][t], opaque bytes, a multiple of 16 bytes); the verify forward wrote the
+    block's blk rows at positions length[r] .. length[r]+blk-1.  The kept rows keep[r][:n_keep[r]]
+    (int32 [batch][k], strictly increasing; None: the first n_keep rows) move to length[r] onwards
+    and length (int32 [batch]) grows by n_keep, in place.  Returns `status` (int32 [batch],
+    ST_BAD_KEEP for an invalid request) when given."""
+    if kv.dim() < 2:
+        raise PsispecError("kv must be [batch][Lmax][...]")
+    batch, Lmax = kv.shape[0], kv.shape[1]
+    _dev(kv, "kv")
+    es = kv.element_size()
+    row_bytes = (kv.numel() // max(1, batch * Lmax)) * es
+    for name, t in (("n_keep", n_keep), ("length", length)):
+        if tuple(t.shape) != (batch,) or t.dtype != torch.int32:
+            raise PsispecError(f"{name} must be int32 [batch]")
+        _dev(t, name)
+    ks = 0
+    if keep is not None:
+        if keep.dim() != 2 or keep.shape[0] != batch or keep.dtype != torch.int32:
+            raise PsispecError("keep must be int32 [batch][k]")
+        _dev(keep, "keep")
+        ks = keep.shape[1]
+    if status is not None:
+        _dev(status, "status")
+    rc = lib().psispec_kv_commit(_ptr(kv), kv.stride(0) * es, row_bytes, Lmax, int(blk), _ptr(keep),
+                                 ks, _ptr(n_keep), _ptr(length), _ptr(status), batch,
+                                 _stream(stream))
+    _check(rc, "psispec_kv_commit")
+    return status
 
 
 def timing_enable(on: bool = True):

@@ -549,6 +549,34 @@ psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
   return PSISPEC_OK;
 }
 
+psispec_status psispec_kv_commit(void* kv, int64_t line_stride, int64_t row_bytes, int32_t Lmax,
+                                 int32_t blk, const int32_t* keep, int32_t keep_stride,
+                                 const int32_t* n_keep, int32_t* len, int32_t* status,
+                                 int32_t batch, void* stream_ptr) {
+  if (batch < 0 || Lmax < 1 || blk < 1 || blk > Lmax || blk > kMaxKvBlock) return PSISPEC_EINVAL;
+  if (row_bytes < 16 || row_bytes % 16 || line_stride % 16 || line_stride < (int64_t)Lmax * row_bytes)
+    return PSISPEC_EINVAL;
+  if (keep && keep_stride < 1) return PSISPEC_EINVAL;
+  if (batch == 0) return PSISPEC_OK;
+  if (!kv || !n_keep || !len || ((uintptr_t)kv % 16) != 0) return PSISPEC_EINVAL;
+  const int64_t ntiles = (row_bytes + 4095) / 4096;
+  if ((int64_t)batch * ntiles > INT32_MAX) return PSISPEC_EINVAL;
+  KvArgs a{};
+  a.kv = kv;
+  a.line_stride = line_stride;
+  a.row_bytes = row_bytes;
+  a.Lmax = Lmax;
+  a.blk = blk;
+  a.keep = keep;
+  a.keep_stride = keep_stride;
+  a.n_keep = n_keep;
+  a.len = len;
+  a.status = status;
+  a.batch = batch;
+  if (launch_kv_commit(a, static_cast<hipStream_t>(stream_ptr)) != hipSuccess) return PSISPEC_EHIP;
+  return PSISPEC_OK;
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------------------------

@@ -132,6 +132,22 @@ struct DrawArgs {
 };
 hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t stream);
 
+// kv.hip -- the KV commit after a verify
+constexpr int kMaxKvBlock = 1024;  // block positions of a commit (B or N)
+struct KvArgs {
+  void* kv;               // line r at kv + r * line_stride bytes; position t at + t * row_bytes
+  int64_t line_stride;    // bytes
+  int64_t row_bytes;      // bytes per position (multiple of 16)
+  int Lmax, blk;          // positions per line; block positions written by the verify forward
+  const int32_t* keep;    // [batch][keep_stride] kept block positions, or null (the prefix)
+  int keep_stride;
+  const int32_t* n_keep;  // [batch]
+  int32_t* len;           // [batch] in/out
+  int32_t* status;        // [batch] or null
+  int batch;
+};
+hipError_t launch_kv_commit(const KvArgs& a, hipStream_t stream);
+
 // lmhead.hip -- LM head on MFMA feeding the linear verify
 struct LMHeadArgs {
   const uint16_t* h_ar;     // bf16 [nP][K]

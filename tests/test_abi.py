@@ -97,3 +97,21 @@ def test_sample_drafts_host_checks(libpsispec):
     s.temperature = float("nan")
     assert L.psispec_sample_drafts(fake, 100, fake, 1, 2, 4, 100, ctypes.byref(s), out, None, fake,
                                    1 << 30, None) == -1
+
+
+def test_kv_commit_host_checks(libpsispec):
+    L = libpsispec
+    fake = ctypes.c_void_p(256)
+    # row bytes not a multiple of 16, line stride too small, block beyond the line or 1024
+    assert L.psispec_kv_commit(fake, 1000, 24, 10, 4, None, 0, fake, fake, None, 2, None) == -1
+    assert L.psispec_kv_commit(fake, 128, 32, 10, 4, None, 0, fake, fake, None, 2, None) == -1
+    assert L.psispec_kv_commit(fake, 320, 32, 10, 11, None, 0, fake, fake, None, 2, None) == -1
+    assert L.psispec_kv_commit(fake, 2048 * 32, 32, 2048, 1025, None, 0, fake, fake, None, 2,
+                               None) == -1
+    # missing lengths, misaligned lines, keep without a stride
+    assert L.psispec_kv_commit(fake, 320, 32, 10, 4, None, 0, fake, None, None, 2, None) == -1
+    assert L.psispec_kv_commit(ctypes.c_void_p(8), 320, 32, 10, 4, None, 0, fake, fake, None, 2,
+                               None) == -1
+    assert L.psispec_kv_commit(fake, 320, 32, 10, 4, fake, 0, fake, fake, None, 2, None) == -1
+    # an empty batch launches nothing
+    assert L.psispec_kv_commit(None, 320, 32, 10, 4, None, 0, None, None, None, 0, None) == 0
