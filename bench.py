@@ -14,8 +14,9 @@ One JSON line is printed: verified rows/s (batch*B per step) as `value`, committ
 roofline of the dominant kernel (the HBM pass, timed with HIP events on the library's stream), the
 oracle timed on the host cores as `cpu_baseline`, the batch-256 B=8 shape as `target_shape`, the
 LM head + verify (batch 128, B=8, H=4096, rank-16 LoRA) with its MFMA roofline as `lmhead`, and the
-32-node tree verify as `tree`, and the drafting step (batch 64, B=8, Uno layout) as `drafts`.
-`--workload c3|c4|c5|drafts` prints the top-p, tree, LM-head or drafting line alone;
+32-node tree verify as `tree`, the drafting step (batch 64, B=8, Uno layout) as `drafts`, and the
+KV commit after tree verifies (batch 256, 114,688-byte rows) as `kv_commit`.
+`--workload c3|c4|c5|drafts|kv` prints the top-p, tree, LM-head, drafting or KV-commit line alone;
 `--workload sweep` prints the linear-vs-tree batch sweep (batch 1..256).
 """
 from __future__ import annotations
@@ -39,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2",
-                    choices=["c2", "ns", "c3", "c4", "c5", "drafts", "sweep"])
+                    choices=["c2", "ns", "c3", "c4", "c5", "drafts", "sweep", "kv"])
     ap.add_argument("--sweep-batches", default="1,2,4,8,16,32,64,128,256",
                     help="batch sizes of the linear-vs-tree sweep")
     ap.add_argument("--sweep-steps", type=int, default=40)
@@ -54,6 +55,8 @@ def parse():
     ap.add_argument("--no-tree", action="store_true", help="skip the tree verify measurement")
     ap.add_argument("--tree-steps", type=int, default=100)
     ap.add_argument("--no-drafts", action="store_true", help="skip the drafting-step measurement")
+    ap.add_argument("--no-kv", action="store_true", help="skip the KV-commit measurement")
+    ap.add_argument("--kv-steps", type=int, default=50)
     ap.add_argument("--draft-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -337,6 +340,76 @@ def run_sweep(batches, steps, torch, pkg, workloads, noise=1.0, boost=1.0):
                 steps_per_point=steps, points=points)
 
 
+KV_ROW_BYTES = 28 * 2 * 8 * 128 * 2  # one position: 28 layers x (K, V) x 8 KV heads x 128 dims, bf16
+
+
+def run_kv(steps, warmup, torch, pkg, workloads):
+    """Time psispec_kv_commit after tree verifies: batch 256 lines of 160 positions of 114,688-byte
+    rows (4.7 GB), 32-position blocks; the kept paths are the accepted nodes of tree verifies of the
+    concentrated sweep workload (N=32, depth <= 8, top-4, V=151936 bf16), one set per step, and each
+    step has its own line lengths.  HBM roofline of the copy kernel over the bytes it must move (each
+    moved row read once and written once)."""
+    from dataclasses import replace
+    b, Lmax, blk = 256, 160, 32
+    pt = replace(workloads.PRESETS["sweep_tree"], boost=2.0)
+    tin = workloads.make_tree(pt, device="cuda", batch=b)
+    n_all, keep_all = [], []
+    for s in range(warmup + steps):
+        o = pkg.psispec_verify_tree(tin.p, tin.parent, tin.node_tokens, pt.depth, seed=tin.seed,
+                                    step=s)
+        n_all.append(o["accept_len"].clone())
+        keep_all.append(o["accept_nodes"].clone())
+    del tin
+    torch.cuda.empty_cache()
+    g = torch.Generator(device="cuda").manual_seed(9)
+    len0 = torch.randint(0, Lmax - blk + 1, (warmup + steps, b), generator=g, device="cuda",
+                         dtype=torch.int32)
+    kv = torch.zeros(b, Lmax, KV_ROW_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    moved = 0
+    for s in range(warmup, warmup + steps):
+        n = n_all[s].cpu()
+        k = keep_all[s].cpu()
+        for r in range(b):
+            moved += int((k[r, :int(n[r])] != torch.arange(int(n[r]), dtype=torch.int32)).sum())
+    lens = [len0.clone(), len0.clone()]
+
+    def call(s, phase=0):
+        pkg.psispec_kv_commit(kv, blk, n_all[s], lens[phase][s], keep=keep_all[s])
+
+    for s in range(warmup):
+        call(s)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for s in range(warmup, warmup + steps):
+        call(s)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    pkg.timing_enable(True)
+    for s in range(warmup, warmup + steps):
+        call(s, 1)
+    kern = pkg.timing_read()
+    pkg.timing_enable(False)
+    ok = bool((lens[0][warmup:] == len0[warmup:] + torch.stack(n_all[warmup:])).all().item())
+    del kv
+    torch.cuda.empty_cache()
+    k_us = {k: 1e3 * v[0] / max(1, v[1]) for k, v in kern.items()}
+    cp_us = k_us.get("kv_commit", 0.0)
+    alg = 2 * KV_ROW_BYTES * moved / steps  # bytes per call
+    gbs = alg / (cp_us / 1e6) / 1e9 if cp_us > 0 else 0.0
+    return dict(workload=f"kv commit: batch {b} lines x {Lmax} positions x {KV_ROW_BYTES} B rows "
+                         f"(bf16, 28 layers x K,V x 8 heads x 128), {blk}-position tree blocks, kept "
+                         f"paths from tree verifies (N=32, depth<=8, concentrated rows)",
+                us_per_call=round(1e3 * ms / steps, 2), lengths_ok=ok,
+                moved_rows_per_call=round(moved / steps, 1),
+                kernels_avg_us={k: round(v, 2) for k, v in k_us.items()},
+                roofline={"bound": "hbm", "kernel": "k_kv_commit", "achieved": round(gbs, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "traffic": read_traffic("kv_commit", "tree"),
+                          "bytes_per_launch": int(alg), "avg_launch_us": round(cp_us, 2)})
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, datasheet
 
 
@@ -401,6 +474,7 @@ def run_lmhead(steps, warmup, torch, pkg, workloads):
 KERNEL_SOURCES = {
     "rowstats": ("rows.hip", "rows.h", "internal.h"),
     "draft_bounds": ("drafts.hip", "draw.h", "decide.h", "launch.h", "internal.h"),
+    "kv_commit": ("kv.hip", "launch.h", "internal.h"),
 }
 
 
@@ -501,6 +575,9 @@ def main():
         print(json.dumps(run_sweep(batches, args.sweep_steps, torch, pkg, workloads,
                                    args.sweep_noise, args.sweep_boost)), flush=True)
         return
+    if args.workload == "kv":
+        print(json.dumps(run_kv(args.kv_steps, 3, torch, pkg, workloads)), flush=True)
+        return
     if args.workload == "drafts":
         print(json.dumps(run_drafts(args.draft_steps, 5, torch, pkg, workloads)), flush=True)
         return
@@ -533,6 +610,10 @@ def main():
     if not args.no_drafts:
         drafts = run_drafts(args.draft_steps, 5, torch, pkg, workloads)
         log(f"drafts: {drafts['ms_per_step'] * 1e3:.1f} us/step, kernels {drafts['kernels_avg_us']}")
+    kvc = None
+    if not args.no_kv:
+        kvc = run_kv(args.kv_steps, 3, torch, pkg, workloads)
+        log(f"kv: {kvc['us_per_call']} us/call, kernels {kvc['kernels_avg_us']}")
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(host, pr, args.cpu_seconds)
@@ -570,6 +651,7 @@ def main():
         "lmhead": lmhead,
         "tree": tree,
         "drafts": drafts,
+        "kv_commit": kvc,
     }
     print(json.dumps(line), flush=True)
 

@@ -559,8 +559,7 @@ psispec_status psispec_kv_commit(void* kv, int64_t line_stride, int64_t row_byte
   if (keep && keep_stride < 1) return PSISPEC_EINVAL;
   if (batch == 0) return PSISPEC_OK;
   if (!kv || !n_keep || !len || ((uintptr_t)kv % 16) != 0) return PSISPEC_EINVAL;
-  const int64_t ntiles = (row_bytes + 4095) / 4096;
-  if ((int64_t)batch * ntiles > INT32_MAX) return PSISPEC_EINVAL;
+  if ((int64_t)batch * ((row_bytes + 4095) / 4096) > INT32_MAX) return PSISPEC_EINVAL;  // grid size
   KvArgs a{};
   a.kv = kv;
   a.line_stride = line_stride;
