@@ -60,6 +60,9 @@ def lib():
         L.psispec_oracle_verify_tree.argtypes = (
             [P, i32, P, P, i32, i32, i32, i32, dbl, dbl, u64, u32, u32, P, P] + [P] * 10)
         L.psispec_oracle_verify_tree.restype = i32
+        L.psispec_oracle_verify_tree_sampled.argtypes = (
+            [P, P, i32, P, P, i32, i32, i32, i32, dbl, dbl, u64, u32, u32, P, P] + [P] * 10)
+        L.psispec_oracle_verify_tree_sampled.restype = i32
         L.psispec_oracle_sample_drafts.argtypes = (
             [P, ctypes.c_int64, P, i32, i32, i32, i32, dbl, dbl, u64, u32, u32, u32] + [P] * 5)
         L.psispec_oracle_sample_drafts.restype = i32
@@ -224,6 +227,43 @@ def kv_commit(kv, blk, n_keep, length, keep=None):
     if rc != 0:
         raise ValueError(f"oracle kv_commit rejected its arguments (code {rc})")
     return st
+
+
+def verify_tree_sampled(p, q, parent, node_tokens, max_depth, T=1.0, top_p=1.0, seed=0, step=0,
+                        request_base=0, u_accept=None, u_resample=None, want_resid=False):
+    """Tree verify with candidates drawn from q: p, q [batch][N+1][V] (row 0 = root, row j+1 =
+    node j; q row v+1 is the distribution node v's children were drawn from)."""
+    p = np.ascontiguousarray(p)
+    q = np.ascontiguousarray(q)
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    node_tokens = np.ascontiguousarray(node_tokens, dtype=np.int32)
+    batch, N1, V = p.shape
+    N = N1 - 1
+    if q.shape != p.shape or q.dtype != p.dtype:
+        raise ValueError("q must match p")
+    if parent.shape != (batch, N) or node_tokens.shape != (batch, N):
+        raise ValueError("parent and node_tokens must be [batch][N]")
+    ua = None if u_accept is None else np.ascontiguousarray(u_accept, dtype=np.float64)
+    ur = None if u_resample is None else np.ascontiguousarray(u_resample, dtype=np.float64)
+    out = dict(
+        accept_len=np.zeros(batch, np.int32), accept_nodes=np.zeros((batch, max_depth), np.int32),
+        out_tokens=np.zeros((batch, max_depth + 1), np.int32),
+        node_ratios=np.zeros((batch, N), np.float64), status=np.zeros(batch, np.int32),
+        margin_accept=np.zeros((batch, N), np.float64), margin_sample=np.zeros(batch, np.float64),
+        margin_topp=np.zeros((batch, 2 * (N + 1)), np.float64))
+    if want_resid:
+        out["resid_w"] = np.zeros((batch, V), np.float64)
+        out["resid_S"] = np.zeros(batch, np.float64)
+    rc = lib().psispec_oracle_verify_tree_sampled(
+        _ptr(p), _ptr(q), _dtype_code(p), _ptr(parent), _ptr(node_tokens), batch, N, V, max_depth,
+        float(T), float(top_p), seed & (2**64 - 1), step, request_base, _ptr(ua), _ptr(ur),
+        _ptr(out["accept_len"]), _ptr(out["accept_nodes"]), _ptr(out["out_tokens"]),
+        _ptr(out["node_ratios"]), _ptr(out["status"]), _ptr(out["margin_accept"]),
+        _ptr(out["margin_sample"]), _ptr(out["margin_topp"]), _ptr(out.get("resid_w")),
+        _ptr(out.get("resid_S")))
+    if rc != 0:
+        raise ValueError(f"oracle verify_tree_sampled rejected its arguments (code {rc})")
+    return out
 
 
 def lmhead_logits(h, W, A=None, Bl=None, scale=1.0):

@@ -562,6 +562,175 @@ int psispec_oracle_lmhead_logits(const uint16_t* h, const uint16_t* W, const uin
 }
 
 /* ------------------------------------------------------------------------------------------------
+ * Tree verify with sampled candidates ([alphalab] "Linear 與 Tree sampler" leaves the candidate rule
+ * open).  Reading: the children of node v were drawn independently from v's draft distribution
+ * q'_v (row v+1 of q; row 0 for the root), in ascending node index.  The lossless rule for such
+ * candidates is recursive rejection: with r_0 = p'_v, child i (the i-th child of v) is kept with
+ * probability min(1, r_{i-1}(x_i) / q'_v(x_i)); when it is rejected the residual becomes
+ * r_i = max(0, r_{i-1} - q'_v) renormalised.  If no child is kept (or v is a leaf) one token is drawn
+ * from r_m, m the number of children.  q'_v(x_i) = 0 (x_i could not have been drawn): the ratio is 1
+ * when r_{i-1}(x_i) > 0, else 0, and status Q_ZERO is set; a zero residual mass (unreachable in
+ * exact arithmetic: r_{i-1} = q'_v accepts every candidate) keeps r_{i-1} and sets RESID_ZERO.
+ * Node ratios are computed for every node as if all its earlier siblings were rejected.
+ * Uniforms as in the deterministic tree: child c at (request, c+1, ACCEPT), the draw at (request,
+ * row of the stopping node, RESAMPLE).  margin_topp: [batch][2(N+1)], p rows then q rows.
+ * ---------------------------------------------------------------------------------------------- */
+static double residual_step(double* res, const double* qv, int V) {
+  double Z = 0.0;
+  for (int x = 0; x < V; ++x) {
+    double d = res[x] - qv[x];
+    res[x] = d > 0.0 ? d : 0.0;
+    Z += res[x];
+  }
+  if (Z > 0.0)
+    for (int x = 0; x < V; ++x) res[x] = res[x] / Z;
+  return Z;
+}
+
+int psispec_oracle_verify_tree_sampled(const void* p, const void* q, int dtype,
+                                       const int32_t* parent, const int32_t* node_tokens,
+                                       int batch, int N, int V, int max_depth, double T,
+                                       double top_p, uint64_t seed, uint32_t step,
+                                       uint32_t request_base, const double* u_accept,
+                                       const double* u_resample, int32_t* accept_len,
+                                       int32_t* accept_nodes, int32_t* out_tokens,
+                                       double* node_ratios, int32_t* status,
+                                       double* margin_accept, double* margin_sample,
+                                       double* margin_topp, double* resid_w, double* resid_S) {
+  if (!p || !q || !parent || !node_tokens || !accept_len || !accept_nodes || !out_tokens)
+    return ORC_EINVAL;
+  if (batch < 0 || N < 1 || V < 1 || max_depth < 1) return ORC_EINVAL;
+  if (!(T > 0.0) || !isfinite(T) || !(top_p > 0.0) || !(top_p <= 1.0)) return ORC_EINVAL;
+  size_t es = elem_size(dtype);
+  double* pi = (double*)malloc(sizeof(double) * (size_t)V);
+  double* qv = (double*)malloc(sizeof(double) * (size_t)V);
+  double* res = (double*)malloc(sizeof(double) * (size_t)V);
+  int* depth = (int*)malloc(sizeof(int) * (size_t)N);
+  double* ratio = (double*)malloc(sizeof(double) * (size_t)N);
+
+  for (int r = 0; r < batch; ++r) {
+    const char* prows = (const char*)p + (size_t)r * (size_t)(N + 1) * (size_t)V * es;
+    const char* qrows = (const char*)q + (size_t)r * (size_t)(N + 1) * (size_t)V * es;
+    const int32_t* par = parent + (size_t)r * N;
+    const int32_t* tok = node_tokens + (size_t)r * N;
+    uint32_t req = request_base + (uint32_t)r;
+    int st = 0;
+
+    for (int j = 0; j < N; ++j) {
+      if (par[j] < -1 || par[j] >= j) {
+        st |= ORC_ST_BAD_PARENT;
+        depth[j] = 1;
+        continue;
+      }
+      depth[j] = par[j] < 0 ? 1 : depth[par[j]] + 1;
+      if (depth[j] > max_depth) st |= ORC_ST_BAD_PARENT;
+    }
+
+    /* data-parallel node ratios: the residual sequence of every node with children */
+    for (int row = 0; row <= N; ++row) {
+      double mp = INFINITY, mq = INFINITY;
+      st |= psispec_oracle_row_probs(prows + (size_t)row * V * es, dtype, V, T, top_p, pi, &mp);
+      st |= psispec_oracle_row_probs(qrows + (size_t)row * V * es, dtype, V, T, top_p, qv, &mq);
+      if (margin_topp) {
+        margin_topp[(size_t)r * 2 * (N + 1) + row] = mp;
+        margin_topp[(size_t)r * 2 * (N + 1) + (N + 1) + row] = mq;
+      }
+      int v = row - 1;
+      memcpy(res, pi, sizeof(double) * (size_t)V);
+      for (int c = 0; c < N; ++c) {
+        if (par[c] != v) continue;
+        double rc = 0.0;
+        if (tok[c] < 0 || tok[c] >= V) {
+          st |= ORC_ST_BAD_TOKEN;
+        } else if (qv[tok[c]] > 0.0) {
+          rc = res[tok[c]] / qv[tok[c]];
+          if (rc > 1.0) rc = 1.0;
+        } else {
+          rc = res[tok[c]] > 0.0 ? 1.0 : 0.0;
+          st |= ORC_ST_Q_ZERO;
+        }
+        ratio[c] = rc;
+        /* the residual if this child is rejected (the next sibling's test uses it) */
+        double* keep = (double*)malloc(sizeof(double) * (size_t)V);
+        memcpy(keep, res, sizeof(double) * (size_t)V);
+        if (!(residual_step(res, qv, V) > 0.0)) memcpy(res, keep, sizeof(double) * (size_t)V);
+        free(keep);
+      }
+    }
+    for (int c = 0; c < N; ++c) {
+      if (node_ratios) node_ratios[(size_t)r * N + c] = ratio[c];
+      if (margin_accept) margin_accept[(size_t)r * N + c] = INFINITY;
+    }
+
+    int32_t* nodes = accept_nodes + (size_t)r * max_depth;
+    int32_t* out = out_tokens + (size_t)r * (max_depth + 1);
+    for (int i = 0; i < max_depth; ++i) nodes[i] = -1;
+    for (int i = 0; i < max_depth + 1; ++i) out[i] = -1;
+    if (st & ORC_ST_BAD_PARENT) {
+      accept_len[r] = 0;
+      if (status) status[r] = st;
+      if (margin_sample) margin_sample[r] = INFINITY;
+      if (resid_S) resid_S[r] = 0.0;
+      continue;
+    }
+
+    /* the walk: at each node the children in index order against the current residual */
+    int cur = -1, dep = 0;
+    for (;;) {
+      int row = cur + 1;
+      psispec_oracle_row_probs(prows + (size_t)row * V * es, dtype, V, T, top_p, pi, NULL);
+      psispec_oracle_row_probs(qrows + (size_t)row * V * es, dtype, V, T, top_p, qv, NULL);
+      memcpy(res, pi, sizeof(double) * (size_t)V);
+      int next = -1;
+      for (int c = 0; c < N; ++c) {
+        if (par[c] != cur) continue;
+        double u = u_accept ? u_accept[(size_t)r * N + c]
+                            : psispec_oracle_uniform(seed, req, (uint32_t)(c + 1), ORC_PURPOSE_ACCEPT,
+                                                     step);
+        if (margin_accept) margin_accept[(size_t)r * N + c] = fabs(u - ratio[c]);
+        if (u < ratio[c]) {
+          next = c;
+          break;
+        }
+        double* keep = (double*)malloc(sizeof(double) * (size_t)V);
+        memcpy(keep, res, sizeof(double) * (size_t)V);
+        if (!(residual_step(res, qv, V) > 0.0)) {
+          st |= ORC_ST_RESID_ZERO;
+          memcpy(res, keep, sizeof(double) * (size_t)V);
+        }
+        free(keep);
+      }
+      if (next >= 0) {
+        nodes[dep] = next;
+        out[dep] = tok[next];
+        ++dep;
+        cur = next;
+        continue;
+      }
+      double S = 0.0;
+      for (int x = 0; x < V; ++x) S += res[x];
+      double u2 = u_resample ? u_resample[r]
+                             : psispec_oracle_uniform(seed, req, (uint32_t)row, ORC_PURPOSE_RESAMPLE,
+                                                      step);
+      double ms = 0.0;
+      out[dep] = inverse_cdf(res, V, S, u2, &ms);
+      if (margin_sample) margin_sample[r] = ms;
+      if (resid_w) memcpy(resid_w + (size_t)r * V, res, sizeof(double) * (size_t)V);
+      if (resid_S) resid_S[r] = S;
+      break;
+    }
+    accept_len[r] = dep;
+    if (status) status[r] = st;
+  }
+  free(pi);
+  free(qv);
+  free(res);
+  free(depth);
+  free(ratio);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------------------------------
  * KV commit after a verify ([lanes] "헤드냐, LoRA냐": the draft and the verify share one KV line per
  * sequence, the AR verifies and appends; [alphalab] walkthrough step 4: the accepted prefix is kept,
  * everything after the first rejection is discarded and drafted again next round).  Reading: the

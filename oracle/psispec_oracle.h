@@ -70,6 +70,19 @@ int psispec_oracle_verify_linear(const void* p, const void* q, int dtype, const 
                                  double* margin_sample, double* margin_topp, double* resid_w,
                                  double* resid_S);
 
+/* Tree verify with candidates drawn from q (recursive rejection); q [batch][N+1][V] like p;
+ * margin_topp [batch][2(N+1)]. */
+int psispec_oracle_verify_tree_sampled(const void* p, const void* q, int dtype,
+                                       const int32_t* parent, const int32_t* node_tokens,
+                                       int batch, int N, int V, int max_depth, double T,
+                                       double top_p, uint64_t seed, uint32_t step,
+                                       uint32_t request_base, const double* u_accept,
+                                       const double* u_resample, int32_t* accept_len,
+                                       int32_t* accept_nodes, int32_t* out_tokens,
+                                       double* node_ratios, int32_t* status,
+                                       double* margin_accept, double* margin_sample,
+                                       double* margin_topp, double* resid_w, double* resid_S);
+
 /* Drafting: tokens[r][i] ~ p'(row) by inverse CDF with the Philox value at (request, i, DRAFT, step)
  * (or u_draw[r][i]); row = AR row r (ar + r * ar_stride elements) for i = 0 with FIRST_FROM_TARGET,
  * else q[r][i].  status/margins [batch][B], nullable. */
