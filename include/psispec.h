@@ -118,8 +118,16 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
  * from res; when no child is kept (or v is a leaf) one token is drawn from res.  Node ratios are
  * computed for every node as if all its earlier siblings were rejected.
  *
+ * With q_logits (candidates drawn from the draft), the rule is recursive rejection: at node v the
+ * children were drawn independently from q'_v, in ascending node index; child i is kept when
+ * u < min(1, r_{i-1}(tok) / q'_v(tok)), r_0 = p'_v, and a rejection replaces the residual by
+ * max(0, r_{i-1} - q'_v) renormalised; with no child kept one token is drawn from the last
+ * residual.  At most 8 children per node (PSISPEC_ST_BAD_PARENT otherwise).
+ *
  *   p_logits     [batch][N+1][V]  row 0 = root, row j+1 = node j
- *   q_logits     must be NULL (sampled-candidate trees are not implemented: PSISPEC_EUNSUPPORTED)
+ *   q_logits     NULL (candidates chosen, e.g. top-k of the draft), or [batch][N+1][V] draft logits
+ *                whose row v+1 (row 0: the root) is the distribution node v's children were drawn
+ *                from (the tree's shape must not depend on the drawn tokens)
  *   parent       [batch][N] int32 parent node of node j, -1 = root, must be < j
  *   node_tokens  [batch][N] int32 token of node j
  *   N            1..1024 nodes per request;  V >= 1;  batch >= 0 (0 launches nothing)
@@ -132,6 +140,7 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
  *   out_tokens   [batch][max_depth+1]     their tokens, then the drawn token, then -1
  *   node_ratios  [batch][N] f32           nullable
  *   status       [batch] int32            nullable
+ * The workspace query covers both rules.
  */
 size_t psispec_verify_tree_workspace(int32_t batch, int32_t N, int32_t V, psispec_dtype dtype);
 

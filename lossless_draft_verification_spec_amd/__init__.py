@@ -174,8 +174,11 @@ def psispec_verify_tree(p_logits: torch.Tensor, parent: torch.Tensor, node_token
                         workspace: torch.Tensor | None = None, out: dict | None = None,
                         stream=None) -> dict:
     """Tree verify.  p_logits [batch][N+1][V] (row 0 = root, row j+1 = node j), parent and
-    node_tokens int32 [batch][N].  Returns accept_len, accept_nodes [batch][max_depth],
-    out_tokens [batch][max_depth+1], node_ratios [batch][N], status."""
+    node_tokens int32 [batch][N].  With q_logits ([batch][N+1][V], p's dtype: row v+1 is the
+    distribution node v's children were drawn from) the candidates are taken as drawn from the
+    draft and verified by recursive rejection; without it, as chosen (e.g. top-k).  Returns
+    accept_len, accept_nodes [batch][max_depth], out_tokens [batch][max_depth+1], node_ratios
+    [batch][N], status."""
     if p_logits.dim() != 3:
         raise PsispecError("p_logits must be [batch][N+1][V]")
     batch, Np1, V = p_logits.shape
@@ -187,6 +190,10 @@ def psispec_verify_tree(p_logits: torch.Tensor, parent: torch.Tensor, node_token
     dt = _dtype_code(p_logits)
     dev = p_logits.device
     _dev(p_logits, "p_logits")
+    if q_logits is not None:
+        if tuple(q_logits.shape) != tuple(p_logits.shape) or q_logits.dtype != p_logits.dtype:
+            raise PsispecError("q_logits must be [batch][N+1][V] with the dtype of p_logits")
+        _dev(q_logits, "q_logits")
     if out is None:
         out = dict(accept_len=torch.empty(batch, dtype=torch.int32, device=dev),
                    accept_nodes=torch.empty(batch, max_depth, dtype=torch.int32, device=dev),

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpsispec.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["api.hip", "rows.hip", "topp.hip", "linear.hip", "tree.hip", "draw.hip", "drafts.hip",
-           "kv.hip", "lmhead.hip"]
+           "kv.hip", "treeq.hip", "lmhead.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for every HIP object.

@@ -97,6 +97,31 @@ Plan make_plan(int64_t rows, int64_t batch, int V, size_t es, int excl_stride, i
 
 size_t elem_size(psispec_dtype d) { return d == PSISPEC_BF16 ? 2 : 4; }
 
+// Tree verify with sampled candidates: the rows of p and q, then per node row its children count,
+// the chain passes' partial sums and its residual chain.
+struct TreeQPlan {
+  Plan pl;
+  size_t off_nchild, off_epart, off_spart, off_chain, total;
+};
+
+TreeQPlan make_treeq_plan(int batch, int N, int V, size_t es) {
+  TreeQPlan tp{};
+  const int64_t nP = (int64_t)batch * (N + 1);
+  tp.pl = make_plan(2 * nP, batch, V, es, N);
+  const size_t nc = (size_t)tp.pl.nchunk_draw;
+  size_t off = tp.pl.total;
+  tp.off_nchild = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)nP);
+  tp.off_epart = off;
+  off = align_up(off + sizeof(double2) * (size_t)nP * nc);
+  tp.off_spart = off;
+  off = align_up(off + sizeof(double) * (size_t)(kMaxSampledChildren - 1) * (size_t)nP * nc);
+  tp.off_chain = off;
+  off = align_up(off + sizeof(NodeChain) * (size_t)nP);
+  tp.total = off;
+  return tp;
+}
+
 bool sampling_ok(const psispec_sampling* s) {
   if (!s) return false;
   if (!(s->temperature > 0.0) || !isfinite(s->temperature)) return false;
@@ -199,6 +224,104 @@ void timing_end(const char* name, hipStream_t stream) {
 
 using namespace psispec;
 
+namespace {
+
+// Tree verify with candidates drawn from q (recursive rejection): row pass over the p and q rows,
+// their statistics and nuclei, the chain passes (level 0: exact normalisers; level i: residual mass
+// after i rejections), the walk, and the final draw of the stopping node's residual.
+psispec_status verify_tree_sampled(const void* p_logits, const void* q_logits, psispec_dtype dtype,
+                                   const int32_t* parent, const int32_t* node_tokens, int32_t batch,
+                                   int32_t N, int32_t V, int32_t max_depth,
+                                   const psispec_sampling* s, int32_t* accept_len,
+                                   int32_t* accept_nodes, int32_t* out_tokens, float* node_ratios,
+                                   int32_t* status, void* workspace, size_t workspace_bytes,
+                                   void* stream_ptr) {
+  const int64_t nP = (int64_t)batch * (N + 1);
+  const TreeQPlan tp = make_treeq_plan(batch, N, V, elem_size(dtype));
+  const Plan& pl = tp.pl;
+  if (!workspace || workspace_bytes < tp.total || ((uintptr_t)workspace % kAlign) != 0)
+    return PSISPEC_EWORKSPACE;
+  if (2 * nP * pl.nchunk > INT32_MAX || nP * pl.nchunk_draw > INT32_MAX) return PSISPEC_EINVAL;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const double T = s->temperature;
+  const float c = (float)(1.4426950408889634074 / T);
+  const bool use_topp = s->top_p < 1.0;
+  RowSet rs{p_logits, q_logits, nP, nP, V, N + 1, 0, V};
+  float2* part = carve<float2>(workspace, pl.off_part);
+  RowStat* rowstat = carve<RowStat>(workspace, pl.off_rowstat);
+  ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
+  DrawDesc* desc = carve<DrawDesc>(workspace, pl.off_desc);
+  if (launch_rowstats(rs, dtype, pl.nchunk, pl.chunk_elems, c, part, stream) != hipSuccess)
+    return PSISPEC_EHIP;
+  if (launch_combine_rows(rs, part, pl.nchunk, c, rowstat, stream) != hipSuccess)
+    return PSISPEC_EHIP;
+  if (use_topp && launch_topp(rs, dtype, pl.nchunk, c, s->top_p, part, topp, stream, rowstat) !=
+                      hipSuccess)
+    return PSISPEC_EHIP;
+
+  TreeQArgs ta{};
+  ta.rs = rs;
+  ta.parent = parent;
+  ta.node_tokens = node_tokens;
+  ta.batch = batch;
+  ta.N = N;
+  ta.V = V;
+  ta.max_depth = max_depth;
+  ta.nchunk_c = pl.nchunk_draw;
+  ta.chunk_elems_c = pl.chunk_elems_draw;
+  ta.inv_T = 1.0 / T;
+  ta.use_topp = use_topp;
+  ta.seed = s->seed;
+  ta.step = s->step;
+  ta.request_base = s->request_base;
+  ta.rowstat = rowstat;
+  ta.topp = topp;
+  ta.nchild = carve<int32_t>(workspace, tp.off_nchild);
+  ta.e_part = carve<double2>(workspace, tp.off_epart);
+  ta.s_part = carve<double>(workspace, tp.off_spart);
+  ta.chain = carve<NodeChain>(workspace, tp.off_chain);
+  ta.desc = desc;
+  ta.ucount = carve<int32_t>(workspace, pl.off_ucount);
+  ta.accept_len = accept_len;
+  ta.accept_nodes = accept_nodes;
+  ta.out_tokens = out_tokens;
+  ta.node_ratios = node_ratios;
+  for (int level = 0; level < kMaxSampledChildren; ++level)
+    if (launch_tree_chain_pass(ta, level, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
+  if (launch_decide_tree_sampled(ta, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
+
+  DrawArgs da{};
+  da.rs = rs;
+  da.batch = batch;
+  da.V = V;
+  da.nchunk_draw = pl.nchunk_draw;
+  da.chunk_elems_draw = pl.chunk_elems_draw;
+  da.nsub = pl.nsub;
+  da.inv_T = 1.0 / T;
+  da.use_topp = use_topp;
+  da.seed = s->seed;
+  da.step = s->step;
+  da.request_base = s->request_base;
+  da.rowstat = rowstat;
+  da.topp = topp;
+  da.desc = desc;
+  da.excl = nullptr;
+  da.excl_stride = 0;
+  da.esum = carve<double2>(workspace, pl.off_esum);
+  da.subsum = carve<double>(workspace, pl.off_subsum);
+  da.suba = carve<double2>(workspace, pl.off_suba);
+  da.subn = carve<int32_t>(workspace, pl.off_subn);
+  da.suboff = carve<int32_t>(workspace, pl.off_suboff);
+  da.upool = carve<double2>(workspace, pl.off_upool);
+  da.ucount = carve<int32_t>(workspace, pl.off_ucount);
+  da.out_tokens = out_tokens;
+  da.status = status;
+  if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
+  return PSISPEC_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* psispec_strerror(psispec_status code) {
@@ -252,7 +375,10 @@ size_t psispec_verify_tree_workspace(int32_t batch, int32_t N, int32_t V, psispe
   if (batch < 0 || N < 1 || N > 1024 || V < 1) return 0;
   if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return 0;
   const int64_t rows = (int64_t)batch * (N + 1);
-  return make_plan(rows, batch, V, elem_size(dtype), N).total + kAlign;
+  // sized for both rules (candidates chosen, or drawn from q)
+  const size_t det = make_plan(rows, batch, V, elem_size(dtype), N).total;
+  const size_t smp = make_treeq_plan(batch, N, V, elem_size(dtype)).total;
+  return (det > smp ? det : smp) + kAlign;
 }
 
 psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits, psispec_dtype dtype,
@@ -349,13 +475,16 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
                                    int32_t* status, void* workspace, size_t workspace_bytes,
                                    void* stream_ptr) {
   if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return PSISPEC_EDTYPE;
-  if (q_logits) return PSISPEC_EUNSUPPORTED;
   if (batch < 0 || N < 1 || N > 1024 || V < 1 || max_depth < 1 || max_depth > 64)
     return PSISPEC_EINVAL;
   if (!sampling_ok(s) || (s->flags & PSISPEC_FIRST_FROM_TARGET)) return PSISPEC_EINVAL;
   if (batch == 0) return PSISPEC_OK;
   if (!p_logits || !parent || !node_tokens || !accept_len || !accept_nodes || !out_tokens)
     return PSISPEC_EINVAL;
+  if (q_logits)
+    return verify_tree_sampled(p_logits, q_logits, dtype, parent, node_tokens, batch, N, V,
+                               max_depth, s, accept_len, accept_nodes, out_tokens, node_ratios,
+                               status, workspace, workspace_bytes, stream_ptr);
   const int64_t nP = (int64_t)batch * (N + 1);
   const Plan pl = make_plan(nP, batch, V, elem_size(dtype), N);
   if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace % kAlign) != 0)

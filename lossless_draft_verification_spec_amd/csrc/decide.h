@@ -181,6 +181,7 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
     dd.out_idx = (int32_t)((int64_t)r * Bp1 + k);
     dd.ph_req = r;
     dd.purpose = kPurposeDraw;
+    dd.factor = 1.0;
     a.desc[r] = dd;
     a.ucount[r] = 0;
   }

@@ -58,6 +58,7 @@ __global__ __launch_bounds__(64) void k_draft_rows(RowSet rs, int B, int first_f
     d.out_idx = j;
     d.ph_req = r;
     d.purpose = kPurposeDraft;
+    d.factor = 1.0;
     desc[j] = d;
   }
 }
@@ -262,6 +263,7 @@ __global__ __launch_bounds__(kThreads) void k_draft_select(DraftArgs a) {
         d.out_idx = j;
         d.ph_req = r;
         d.purpose = kPurposeDraft;
+        d.factor = 1.0;
         a.desc[j] = d;
       }
     }

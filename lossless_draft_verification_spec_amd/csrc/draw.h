@@ -87,14 +87,15 @@ __device__ inline bool excluded(int x, const int* excl, int nexcl) {
   return false;
 }
 
-// ratio of the normalisers E_p / E_q as estimated by the HBM pass (sum over the kept tokens)
+// factor E_p / E_q as estimated from the HBM pass's normalisers (sums over the kept tokens): the
+// residual max(0, p' - factor q') is positive where e_p > rho e_q, rho = factor E_p / E_q
 __device__ inline double rho_estimate(const DrawArgs& a, const DrawDesc& d) {
   double ep = a.rowstat[d.prow].Z, eq = a.rowstat[d.qrow].Z;
   if (a.use_topp) {
     ep *= a.topp[d.prow].M;
     eq *= a.topp[d.qrow].M;
   }
-  return ep / eq;
+  return d.factor * ep / eq;
 }
 
 // Draw chunk c of request r (every thread of a kThreads block calls it).
@@ -304,8 +305,8 @@ __device__ inline void draw_select_request(const DrawArgs& a, int r) {
       Eq += e.y;
     }
     rEp = 1.0 / Ep;
-    rEq = 1.0 / Eq;
-    rho = Ep / Eq;
+    rEq = d.factor / Eq;
+    rho = d.factor * Ep / Eq;
     band_ok = fabs(rho / rho_estimate(a, d) - 1.0) <= 0.25 * kBand;
   }
   const int mode = has_q ? 0 : 1;

@@ -49,7 +49,8 @@ struct ToppStat {
 };
 
 // What the final draw of a request needs: the stopping row of p (and of q, or -1), the Philox
-// position of the draw, and the tokens removed from the residual (tree: rejected children).
+// position of the draw, the tokens removed from the residual (tree: rejected children) and the
+// weight of q in the residual.
 struct DrawDesc {
   int32_t prow;
   int32_t qrow;
@@ -59,6 +60,7 @@ struct DrawDesc {
   int32_t out_idx;  // where the drawn token goes in out_tokens (flat index), -1 = nowhere
   int32_t ph_req;   // Philox counter word 0 is request_base + ph_req
   int32_t purpose;  // Philox counter word 2
+  double factor;    // with a q row: the residual is max(0, p' - factor q') (1 for the linear rule)
 };
 
 // ---------------------------------------------------------------------------------------------

@@ -103,6 +103,46 @@ struct TreeArgs {
 };
 hipError_t launch_decide_tree(const TreeArgs& a, psispec_dtype dtype, hipStream_t stream);
 
+// treeq.hip -- tree verify with candidates drawn from the draft (recursive rejection)
+constexpr int kMaxSampledChildren = 8;  // children per node under the sampled rule
+// Per node: exact normalisers of its p and q rows and the residual chain: after k rejections the
+// residual is max(0, p' - c[k] q') / S[k], c[0] = 0, S[0] = 1, c[k] = c[k-1] + S[k-1] and
+// S[k] = sum_x max(0, p'(x) - c[k] q'(x)).  A zero residual (S[k] = 0, unreachable in exact
+// arithmetic) keeps the previous one: then c[j], S[j] = c[k-1], S[k-1] for every j >= k, and
+// stuck = k (else kMaxSampledChildren + 1).
+struct NodeChain {
+  double Ep, Eq;
+  double S[kMaxSampledChildren + 1];
+  double c[kMaxSampledChildren + 1];
+  int stuck;
+};
+struct TreeQArgs {
+  RowSet rs;                // p rows [0, nP), q rows [nP, 2 nP), nP = batch (N+1)
+  const int32_t* parent;
+  const int32_t* node_tokens;
+  int batch, N, V, max_depth;
+  int nchunk_c, chunk_elems_c;  // chain passes: 4096-token chunks of a row
+  double inv_T;
+  int use_topp;
+  uint64_t seed;
+  uint32_t step, request_base;
+  const RowStat* rowstat;   // every p and q row (combined)
+  const ToppStat* topp;
+  int32_t* nchild;          // [nP] children per node row (written by the level-0 pass)
+  double2* e_part;          // [nP][nchunk_c] (sum e_p, sum e_q) over the kept tokens
+  double* s_part;           // [kMaxSampledChildren - 1][nP][nchunk_c] residual masses
+  NodeChain* chain;         // [nP]
+  DrawDesc* desc;
+  int32_t* ucount;
+  int32_t* accept_len;
+  int32_t* accept_nodes;
+  int32_t* out_tokens;
+  float* node_ratios;
+};
+hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype dtype,
+                                  hipStream_t stream);
+hipError_t launch_decide_tree_sampled(const TreeQArgs& a, psispec_dtype dtype, hipStream_t stream);
+
 // draw.hip -- the fp64 inverse-CDF draw shared by the verify entry points and the drafting step
 struct DrawArgs {
   RowSet rs;

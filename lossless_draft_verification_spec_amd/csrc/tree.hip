@@ -204,6 +204,7 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
     dd.out_idx = (s_st & PSISPEC_ST_BAD_PARENT) ? -1 : (int32_t)((int64_t)r * Dp1 + dep);
     dd.ph_req = r;
     dd.purpose = kPurposeDraw;
+    dd.factor = 1.0;
     a.desc[r] = dd;
     a.ucount[r] = 0;
   }

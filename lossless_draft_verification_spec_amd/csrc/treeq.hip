@@ -1,0 +1,347 @@
+// treeq.hip -- tree verify with candidates drawn from the draft (recursive rejection).
+//
+// [alphalab] §"Linear 與 Tree sampler" leaves the candidate rule open.  When the children of node v
+// were drawn independently from v's draft distribution q'_v, the lossless rule is recursive
+// rejection: with r_0 = p'_v, child i is kept with probability min(1, r_{i-1}(x_i) / q'_v(x_i)); a
+// rejection replaces the residual by max(0, r_{i-1} - q'_v) renormalised; with no child kept one
+// token is drawn from the last residual.
+//
+// The residual after i rejections is max(0, p' - c_i q') / S_i with c_0 = 0, c_1 = 1,
+// c_{i+1} = c_i + S_i and S_i = sum_x max(0, p'(x) - c_i q'(x)): by induction, where p' > c_i q' the
+// next subtraction leaves p' - (c_i + S_i) q', and elsewhere both sides are 0.  So a node with m
+// children needs its exact normalisers and S_1 .. S_{m-1}, one fp64 pass over its p and q rows per
+// level (k_tree_chain; level 0 gives the normalisers).  The accept tests then need one gathered
+// token per child (k_decide_tree_sampled), and the final draw is the residual draw of the linear
+// rule with q weighted by c_m (or, at a leaf, the draw from p').
+#include "launch.h"
+#include "draw.h"
+
+namespace psispec {
+namespace {
+
+constexpr int kChainWaves = kThreads / 64;  // one 1024-token sub-chunk per wave
+
+// a b - c d with each product rounded on its own (no fused multiply-add), as the definition's
+// separately rounded terms: p' = c q' then gives exactly 0
+__device__ inline double sub_products(double a, double b, double c, double d) {
+#pragma clang fp contract(off)
+  return a * b - c * d;
+}
+
+// Block (g, chunk): node row g = r (N+1) + v + 1.  Level 0: children count (chunk 0 stores it) and,
+// for nodes with >= 2 children, the chunk's sums of e_p and e_q.  Level i >= 1: for nodes with
+// >= i+1 children, the chunk's sum of max(0, p' - c_i q').
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level, int vec_ok) {
+  __shared__ double tbl[64];
+  __shared__ int s_cnt;
+  __shared__ double2 s_sum[kChainWaves];
+  const int64_t g = blockIdx.x / a.nchunk_c;
+  const int chunk = (int)(blockIdx.x - g * a.nchunk_c);
+  const int r = (int)(g / (a.N + 1));
+  const int v = (int)(g - (int64_t)r * (a.N + 1)) - 1;
+  exp_table_fill(tbl);
+  int m;
+  if (level == 0) {
+    if (threadIdx.x == 0) s_cnt = 0;
+    __syncthreads();
+    int cnt = 0;
+    for (int j = threadIdx.x; j < a.N; j += kThreads) cnt += a.parent[(int64_t)r * a.N + j] == v;
+    if (cnt) atomicAdd(&s_cnt, cnt);
+    __syncthreads();
+    m = s_cnt;
+    if (chunk == 0 && threadIdx.x == 0) a.nchild[g] = m;
+  } else {
+    m = a.nchild[g];
+    __syncthreads();  // the exp table
+  }
+  if (m > kMaxSampledChildren || (level == 0 ? m < 2 : m < level + 1)) return;
+
+  const int64_t prow = g, qrow = a.rs.nP + g;
+  const T* pr = row_ptr<T>(a.rs, prow);
+  const T* qr = row_ptr<T>(a.rs, qrow);
+  const float lmp = a.rowstat[prow].lmax, lmq = a.rowstat[qrow].lmax;
+  const float thp = a.use_topp ? a.topp[prow].thr : -__builtin_huge_valf();
+  const float thq = a.use_topp ? a.topp[qrow].thr : -__builtin_huge_valf();
+  double invEp = 0.0, invEq = 0.0, ci = 0.0;
+  if (level > 0) {  // the node's normalisers and c_level from the earlier levels (fixed order)
+    double Ep = 0.0, Eq = 0.0;
+    for (int k = 0; k < a.nchunk_c; ++k) {
+      const double2 e = a.e_part[g * a.nchunk_c + k];
+      Ep += e.x;
+      Eq += e.y;
+    }
+    invEp = 1.0 / Ep;
+    invEq = 1.0 / Eq;
+    ci = 1.0;
+    const int64_t nP = a.rs.nP;
+    for (int j = 1; j < level; ++j) {
+      double S = 0.0;
+      for (int k = 0; k < a.nchunk_c; ++k) S += a.s_part[((int64_t)(j - 1) * nP + g) * a.nchunk_c + k];
+      ci += S;
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int x0 = chunk * a.chunk_elems_c + wave * kSub + lane * kPerLane;
+  float fp[kPerLane], fq[kPerLane];
+  load_run<T, kPerLane>(pr, x0, a.V, vec_ok, fp);
+  load_run<T, kPerLane>(qr, x0, a.V, vec_ok, fq);
+  double sp = 0.0, sq = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) {
+    const double ep = term(fp[e], lmp, thp, a.inv_T, tbl);
+    const double eq = term(fq[e], lmq, thq, a.inv_T, tbl);
+    if (level == 0) {
+      sp += ep;
+      sq += eq;
+    } else {
+      const double w = sub_products(ep, invEp, ci, eq * invEq);
+      sp += w > 0.0 ? w : 0.0;
+    }
+  }
+  sp = wave_sum(sp);
+  sq = wave_sum(sq);
+  if (lane == 0) s_sum[wave] = make_double2(sp, sq);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tp = 0.0, tq = 0.0;
+    for (int w = 0; w < kChainWaves; ++w) {
+      tp += s_sum[w].x;
+      tq += s_sum[w].y;
+    }
+    if (level == 0)
+      a.e_part[g * a.nchunk_c + chunk] = make_double2(tp, tq);
+    else
+      a.s_part[((int64_t)(level - 1) * a.rs.nP + g) * a.nchunk_c + chunk] = tp;
+  }
+}
+
+// p'(x) or q'(x) of one gathered token: exp((l - lmax) / T) / E over the nucleus
+template <typename T>
+__device__ inline double gathered_prob(const TreeQArgs& a, int64_t row, int tok, double E) {
+  const float l = to_f32(row_ptr<T>(a.rs, row)[tok]);
+  if (a.use_topp && !(l >= a.topp[row].thr)) return 0.0;
+  return exp(((double)l - (double)a.rowstat[row].lmax) * a.inv_T) / E;
+}
+
+// One wave per request: structure, residual chains, node ratios, the walk, the draw description.
+template <typename T>
+__global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
+  const int r = blockIdx.x;
+  const int t = threadIdx.x;
+  const int N = a.N, V = a.V;
+  const int64_t row0 = (int64_t)r * (N + 1);
+  const int64_t nP = a.rs.nP;
+  const int32_t* par = a.parent + (int64_t)r * N;
+  const int32_t* tok = a.node_tokens + (int64_t)r * N;
+
+  __shared__ int32_t s_par[1024], s_tok[1024];
+  __shared__ double s_u[1024], s_ratio[1024];
+  __shared__ int s_st;
+
+  for (int j = t; j < N; j += 64) {
+    s_par[j] = par[j];
+    s_tok[j] = tok[j];
+    s_u[j] = philox_uniform(a.seed, a.request_base + (uint32_t)r, (uint32_t)(j + 1), kPurposeAccept,
+                            a.step);
+  }
+  __syncthreads();
+
+  // 1. structure: parents precede children, depth within max_depth, at most kMaxSampledChildren
+  //    children per node (the level-0 pass counted them); row statistics of the request's rows
+  int bad = 0, st = 0;
+  for (int j = t; j < N; j += 64) {
+    const int pj = s_par[j];
+    if (pj < -1 || pj >= j) {
+      bad = 1;
+      continue;
+    }
+    int d = 1, pnode = pj;
+    while (pnode >= 0 && d <= a.max_depth) {
+      const int q = s_par[pnode];
+      if (q < -1 || q >= pnode) break;
+      ++d;
+      pnode = q;
+    }
+    if (d > a.max_depth) bad = 1;
+  }
+  for (int j = t; j <= N; j += 64) {
+    if (a.nchild[row0 + j] > kMaxSampledChildren) bad = 1;
+    st |= a.rowstat[row0 + j].st | a.rowstat[nP + row0 + j].st;
+  }
+  {
+    const uint64_t bm = __ballot(bad);
+    if (t == 0) s_st = bm ? PSISPEC_ST_BAD_PARENT : 0;
+  }
+
+  // 2. residual chains of the nodes with children (lane per node; fixed-order sums)
+  for (int j = t; j <= N; j += 64) {
+    const int64_t g = row0 + j;
+    const int m = a.nchild[g];
+    if (m < 1 || m > kMaxSampledChildren) continue;
+    NodeChain ch;
+    ch.c[0] = 0.0;
+    ch.S[0] = 1.0;
+    ch.stuck = kMaxSampledChildren + 1;
+    if (m >= 2) {
+      double Ep = 0.0, Eq = 0.0;
+      for (int k = 0; k < a.nchunk_c; ++k) {
+        const double2 e = a.e_part[g * a.nchunk_c + k];
+        Ep += e.x;
+        Eq += e.y;
+      }
+      ch.Ep = Ep;
+      ch.Eq = Eq;
+    } else {  // one child: the HBM pass's normalisers suffice for its ratio
+      double Ep = a.rowstat[g].Z, Eq = a.rowstat[nP + g].Z;
+      if (a.use_topp) {
+        Ep *= a.topp[g].M;
+        Eq *= a.topp[nP + g].M;
+      }
+      ch.Ep = Ep;
+      ch.Eq = Eq;
+    }
+    for (int k = 1; k <= m; ++k) {
+      if (ch.stuck <= k) {  // a zero residual earlier: the residual stays
+        ch.c[k] = ch.c[k - 1];
+        ch.S[k] = ch.S[k - 1];
+        continue;
+      }
+      ch.c[k] = ch.c[k - 1] + ch.S[k - 1];
+      double S = 1.0;  // S[m] is never used (the final draw normalises its own weights)
+      if (k < m) {
+        S = 0.0;
+        for (int q = 0; q < a.nchunk_c; ++q) S += a.s_part[((int64_t)(k - 1) * nP + g) * a.nchunk_c + q];
+      }
+      if (!(S > 0.0)) {
+        ch.stuck = k;
+        ch.c[k] = ch.c[k - 1];
+        ch.S[k] = ch.S[k - 1];
+      } else {
+        ch.S[k] = S;
+      }
+    }
+    a.chain[g] = ch;
+  }
+  __syncthreads();
+
+  // 3. node ratios: child j is the i-th child of v (siblings in index order)
+  for (int j = t; j < N; j += 64) {
+    const int v = s_par[j], tj = s_tok[j];
+    double ratio = 0.0;
+    if (tj < 0 || tj >= V) {
+      st |= PSISPEC_ST_BAD_TOKEN;
+    } else if (v >= -1 && v < j) {
+      int i = 1;
+      for (int s = 0; s < j; ++s) i += s_par[s] == v;
+      const int64_t g = row0 + v + 1;
+      if (i <= kMaxSampledChildren) {
+        const NodeChain& ch = a.chain[g];
+        const double pp = gathered_prob<T>(a, g, tj, ch.Ep);
+        const double qq = gathered_prob<T>(a, nP + g, tj, ch.Eq);
+        double R = sub_products(pp, 1.0, ch.c[i - 1], qq);  // residual after i-1 rejections
+        R = R > 0.0 ? R : 0.0;
+        const double S = ch.S[i - 1];
+        if (qq > 0.0) {
+          ratio = fmin(1.0, (R / S) / qq);
+        } else {
+          ratio = R > 0.0 ? 1.0 : 0.0;
+          st |= PSISPEC_ST_Q_ZERO;
+        }
+      }
+    }
+    s_ratio[j] = ratio;
+    if (a.node_ratios) a.node_ratios[(int64_t)r * N + j] = (float)ratio;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) st |= __shfl_xor(st, off, 64);
+  __syncthreads();
+
+  // 4. the walk: at each node the children in index order, 64 at a time; the first accepted
+  //    child (ballot) is the next node
+  const int Dp1 = a.max_depth + 1;
+  int32_t* nodes = a.accept_nodes + (int64_t)r * a.max_depth;
+  int32_t* out = a.out_tokens + (int64_t)r * Dp1;
+  int cur = -1, dep = 0;
+  st |= s_st;
+  if (!(s_st & PSISPEC_ST_BAD_PARENT)) {
+    for (;;) {
+      int next = -1, rejected = 0;
+      for (int c0 = 0; c0 < N && next < 0; c0 += 64) {
+        const int c = c0 + t;
+        const bool child = c < N && s_par[c] == cur;
+        const uint64_t am = __ballot(child && s_u[c] < s_ratio[c]);
+        const uint64_t cm = __ballot(child);
+        if (am) {
+          next = c0 + __builtin_ctzll(am);
+          rejected += __builtin_popcountll(cm & ((1ull << (next - c0)) - 1ull));
+        } else {
+          rejected += __builtin_popcountll(cm);
+        }
+      }
+      {
+        const int m = a.nchild[row0 + cur + 1];
+        if (m >= 1 && rejected >= a.chain[row0 + cur + 1].stuck) st |= PSISPEC_ST_RESID_ZERO;
+      }
+      if (next < 0) break;
+      if (t == 0) {
+        nodes[dep] = next;
+        out[dep] = s_tok[next];
+      }
+      ++dep;
+      cur = next;
+    }
+  }
+  if (t == 0) {
+    for (int i = dep; i < a.max_depth; ++i) nodes[i] = -1;
+    for (int i = dep; i < Dp1; ++i) out[i] = -1;
+    a.accept_len[r] = dep;
+    const int64_t g = row0 + cur + 1;
+    const int m = (s_st & PSISPEC_ST_BAD_PARENT) ? 0 : a.nchild[g];
+    DrawDesc dd;
+    dd.prow = (int32_t)g;
+    dd.qrow = m >= 1 ? (int32_t)(nP + g) : -1;  // every child rejected: residual of c_m q'
+    dd.pos = cur + 1;
+    dd.st = st;
+    dd.nexcl = 0;
+    dd.out_idx = (s_st & PSISPEC_ST_BAD_PARENT) ? -1 : (int32_t)((int64_t)r * Dp1 + dep);
+    dd.ph_req = r;
+    dd.purpose = kPurposeDraw;
+    dd.factor = m >= 1 ? a.chain[g].c[m] : 1.0;
+    a.desc[r] = dd;
+    a.ucount[r] = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype dtype,
+                                  hipStream_t stream) {
+  const int64_t blocks = a.rs.nP * (int64_t)a.nchunk_c;
+  if (blocks == 0) return hipSuccess;
+  const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
+  const int vec_ok = ((size_t)a.V * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
+                     ((uintptr_t)a.rs.q % 16) == 0;
+  timing_begin("tree_chain", stream);
+  if (dtype == PSISPEC_BF16)
+    hipLaunchKernelGGL(k_tree_chain<bf16_t>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a,
+                       level, vec_ok);
+  else
+    hipLaunchKernelGGL(k_tree_chain<float>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a,
+                       level, vec_ok);
+  timing_end("tree_chain", stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_decide_tree_sampled(const TreeQArgs& a, psispec_dtype dtype, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  timing_begin("decide_tree_sampled", stream);
+  if (dtype == PSISPEC_BF16)
+    hipLaunchKernelGGL(k_decide_tree_sampled<bf16_t>, dim3(a.batch), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_decide_tree_sampled<float>, dim3(a.batch), dim3(64), 0, stream, a);
+  timing_end("decide_tree_sampled", stream);
+  return hipGetLastError();
+}
+
+}  // namespace psispec

@@ -85,6 +85,8 @@ PRESETS = {
     # 4: tree, batch 8, depth 8, top-4 candidates, 32 nodes, fp32 rows N(0, 3^2), q = p + N(0, 1)
     "c4": TreePreset("c4", 8, 32, 8, 4, 151936, steps=200, seed=4, rotations=4),
     "c4b": TreePreset("c4b", 8, 32, 8, 4, 151936, steps=20, seed=14, peaked=True),
+    # tree with candidates drawn from the draft (recursive rejection), c4's sizes, fp32 rows
+    "c4s": TreePreset("c4s", 8, 32, 8, 4, 151936, steps=200, seed=24, rotations=4),
     # 5: fused LM head: batch 128, B=8, H=4096, rank-16 LoRA on the draft rows
     "c5": LMHeadPreset("c5", 128, 8, 4096, 151936, 16),
     # linear-vs-tree batch sweep: one draft/target model for both samplers (bf16, Zipf-boosted
@@ -205,6 +207,7 @@ class TreeInputs:
     parent: torch.Tensor       # int32 [batch][N]
     node_tokens: torch.Tensor  # int32 [batch][N]
     seed: int
+    q: torch.Tensor | None = None  # [batch][N+1][V] draft logits (sampled candidates only)
 
 
 def make_tree(preset: TreePreset | str, device="cpu", rotation: int = 0, batch=None, V=None, N=None,
@@ -258,6 +261,50 @@ def make_tree(preset: TreePreset | str, device="cpu", rotation: int = 0, batch=N
             raise ValueError("tree preset cannot reach N nodes within the depth limit")
     seed = (preset.seed * 1000003 + rotation) & (2**64 - 1)
     return TreeInputs(preset, p, parent.to(device), tokens.to(device), seed)
+
+
+def make_tree_sampled(preset: TreePreset | str, device="cpu", rotation: int = 0, batch=None, V=None,
+                      N=None, branching=(4, 2, 2, 1, 1, 1, 1, 1)) -> TreeInputs:
+    """Trees whose candidates are drawn from the draft: the shape is fixed in advance (breadth
+    first, branching[d] children for every node at depth d, until N nodes exist), and each child's
+    token is drawn independently from its parent's draft row softmax(q / T) restricted to the
+    row's nucleus.  The shape must not depend on the drawn tokens for the recursive-rejection rule
+    to be lossless, hence the fixed schedule."""
+    if isinstance(preset, str):
+        preset = PRESETS[preset]
+    preset = replace(preset, batch=batch or preset.batch, V=V or preset.V, N=N or preset.N)
+    b, N, V = preset.batch, preset.N, preset.V
+    g = _gen(device, preset.seed, rotation, 0x5A3)
+    p = torch.randn(b, N + 1, V, generator=g, device=device) * preset.p_std
+    if preset.zipf or preset.peaked:
+        p += zipf_boost(b * (N + 1), V, g, device).view(b, N + 1, V) * preset.boost
+    q = p + preset.q_noise * torch.randn(b, N + 1, V, generator=g, device=device)
+    p = p.to(preset.dtype).contiguous()
+    q = q.to(preset.dtype).contiguous()
+    # the fixed shape: parent of every node, breadth first
+    parent_list, depth_list = [], []
+    frontier = [(-1, 0)]
+    while len(parent_list) < N and frontier:
+        nxt = []
+        for v, d in frontier:
+            k = branching[d] if d < len(branching) else 1
+            for _ in range(k):
+                if len(parent_list) == N or d + 1 > preset.depth:
+                    break
+                parent_list.append(v)
+                depth_list.append(d + 1)
+                nxt.append((len(parent_list) - 1, d + 1))
+        frontier = nxt
+    if len(parent_list) < N:
+        raise ValueError("the branching schedule cannot reach N nodes within the depth limit")
+    parent = torch.tensor([parent_list] * b, dtype=torch.int32)
+    # each child's token from its parent's draft row (row v+1), drawn per node
+    par_rows = torch.tensor([v + 1 for v in parent_list], dtype=torch.long, device=device)
+    gd = _gen(device, preset.seed, rotation, 0xC4D)
+    rows = q[:, par_rows, :]  # [b][N][V]
+    tokens = sample_drafts(rows, preset.T, preset.top_p, gd)
+    seed = (preset.seed * 1000003 + rotation) & (2**64 - 1)
+    return TreeInputs(preset, p, parent.to(device), tokens.to(device), seed, q)
 
 
 @dataclass

@@ -177,6 +177,17 @@ def oracle_tree_requests(p_host, parent, tokens, rows, max_depth, T, top_p, seed
     return {k: np.concatenate([o[k] for o in outs]) for k in outs[0]}
 
 
+def oracle_tree_sampled_requests(p_host, q_host, parent, tokens, rows, max_depth, T, top_p, seed,
+                                 step, request_base=0):
+    outs = []
+    for r in rows:
+        o = oracle.verify_tree_sampled(p_host[r:r + 1], q_host[r:r + 1], parent[r:r + 1],
+                                       tokens[r:r + 1], max_depth, T=T, top_p=top_p, seed=seed,
+                                       step=step, request_base=request_base + r)
+        outs.append(o)
+    return {k: np.concatenate([o[k] for o in outs]) for k in outs[0]}
+
+
 def compare_drafts(tally: Tally, g_tokens, g_status, o: dict, rows, top_p: float):
     """Drafting step: every drafted token is one draw decision (plus one nucleus decision per row
     with top-p).  g_tokens/g_status: GPU [batch][B]; o: oracle outputs of the requests `rows`."""

@@ -61,7 +61,11 @@ def test_workspace_queries_and_host_checks(libpsispec):
     assert rc == -3  # no workspace
     rc = L.psispec_verify_tree(ctypes.c_void_p(16), ctypes.c_void_p(16), 0, None, None, 1, 4, 10, 4,
                                ctypes.byref(s), None, None, None, None, None, None, 0, None)
-    assert rc == -5  # sampled-candidate trees not implemented
+    assert rc == -1  # sampled-candidate tree without parent / node tokens / outputs
+    fake = ctypes.c_void_p(256)
+    rc = L.psispec_verify_tree(fake, fake, 0, fake, fake, 1, 4, 10, 4, ctypes.byref(s), fake, fake,
+                               fake, None, None, None, 0, None)
+    assert rc == -3  # sampled-candidate tree without a workspace
     assert L.psispec_strerror(-3).decode().startswith("workspace")
     # batch 0 is a no-op that succeeds without touching anything
     rc = L.psispec_verify_linear(None, None, 1, None, 0, 4, 10, ctypes.byref(s), None, None, None,

@@ -1,0 +1,99 @@
+"""Parity of the tree verify with candidates drawn from the draft (recursive rejection) on the GPU
+(through the C ABI) with the CPU oracle: small, ragged and full-size trees, temperature and top-p,
+draft rows equal to the target rows, too many children, non-finite rows."""
+import numpy as np
+import pytest
+import torch
+
+from lossless_draft_verification_spec_amd import (ST_BAD_PARENT, ST_NONFINITE, psispec_verify_tree,
+                                                  workloads)
+from parity import Tally, compare_tree, host_logits, oracle_tree_sampled_requests
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _compare(tin, T=1.0, top_p=1.0, steps=(0,), rows=None, seed=None, q=None):
+    p, q = tin.p, (tin.q if q is None else q)
+    ph, qh = host_logits(p), host_logits(q)
+    par = tin.parent.cpu().numpy()
+    tok = tin.node_tokens.cpu().numpy()
+    D = tin.preset.depth
+    seed = tin.seed if seed is None else seed
+    rows = list(range(p.shape[0])) if rows is None else rows
+    tally = Tally()
+    for step in steps:
+        out = psispec_verify_tree(p, tin.parent, tin.node_tokens, D, temperature=T, top_p=top_p,
+                                  seed=seed, step=step, q_logits=q)
+        torch.cuda.synchronize()
+        g = {k: v.cpu().numpy() for k, v in out.items()}
+        o = oracle_tree_sampled_requests(ph, qh, par, tok, rows, D, float(T), float(top_p), seed, step)
+        compare_tree(tally, g, o, rows, float(top_p))
+    return tally
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("batch,N,V,branching", [
+    (4, 10, 64, (3, 2, 1)), (3, 32, 5003, (4, 2, 2, 1, 1, 1, 1, 1)), (2, 1, 100, (1,)),
+    (5, 40, 999, (8, 2, 1, 1)), (2, 7, 4097, (1, 1, 1, 1, 1, 1, 1))])
+def test_sampled_tree_small(dtype, batch, N, V, branching):
+    from dataclasses import replace
+    pr = replace(workloads.PRESETS["c4s"], dtype=dtype, depth=8)
+    tin = workloads.make_tree_sampled(pr, device=DEV, batch=batch, V=V, N=N, branching=branching)
+    t = _compare(tin, steps=range(5))
+    print(t)
+    t.check()
+
+
+@pytest.mark.parametrize("T,top_p", [(0.7, 1.0), (1.0, 0.9), (0.7, 0.95), (1.0, 0.5)])
+def test_sampled_tree_temperature_top_p(T, top_p):
+    from dataclasses import replace
+    pr = replace(workloads.PRESETS["c4s"], dtype=torch.bfloat16, T=T, top_p=top_p)
+    tin = workloads.make_tree_sampled(pr, device=DEV, batch=4, V=3001, N=24)
+    t = _compare(tin, T=T, top_p=top_p, steps=range(4))
+    print(t)
+    t.check()
+
+
+def test_equal_draft_accepts_first_children():
+    tin = workloads.make_tree_sampled("c4s", device=DEV, batch=3, V=2000, N=20)
+    out = psispec_verify_tree(tin.p, tin.parent, tin.node_tokens, 8, seed=1, q_logits=tin.p)
+    par = tin.parent[0].cpu().numpy()
+    first_path = []
+    v = -1
+    while True:
+        kids = [c for c in range(len(par)) if par[c] == v]
+        if not kids:
+            break
+        first_path.append(kids[0])
+        v = kids[0]
+    acc = out["accept_len"].cpu().numpy()
+    nodes = out["accept_nodes"].cpu().numpy()
+    assert (acc == len(first_path)).all()
+    assert (nodes[:, :len(first_path)] == np.array(first_path)).all()
+    t = _compare(tin, q=tin.p)
+    t.check()
+
+
+def test_too_many_children_and_nonfinite_rows():
+    tin = workloads.make_tree_sampled("c4s", device=DEV, batch=3, V=500, N=12,
+                                      branching=(9, 1, 1))
+    out = psispec_verify_tree(tin.p, tin.parent, tin.node_tokens, 8, seed=2, q_logits=tin.q)
+    assert (out["status"].cpu().numpy() & ST_BAD_PARENT).all()
+    tin = workloads.make_tree_sampled("c4s", device=DEV, batch=3, V=500, N=12)
+    q = tin.q.clone()
+    q[1, 0, 7] = float("nan")
+    out = psispec_verify_tree(tin.p, tin.parent, tin.node_tokens, 8, seed=2, q_logits=q)
+    st = out["status"].cpu().numpy()
+    assert st[1] & ST_NONFINITE and not (st[0] & ST_NONFINITE) and not (st[2] & ST_NONFINITE)
+    t = _compare(tin, q=q)
+    assert t.status_requests >= 1
+    t.check()
+
+
+def test_full_size_sampled_tree():
+    tin = workloads.make_tree_sampled("c4s", device=DEV)
+    t = _compare(tin, steps=range(2), rows=[0, 3, 7])
+    print(t)
+    t.check()
