@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2",
-                    choices=["c2", "ns", "c3", "c4", "c5", "drafts", "sweep", "kv"])
+                    choices=["c2", "ns", "c3", "c4", "c4s", "c5", "drafts", "sweep", "kv"])
     ap.add_argument("--sweep-batches", default="1,2,4,8,16,32,64,128,256",
                     help="batch sizes of the linear-vs-tree sweep")
     ap.add_argument("--sweep-steps", type=int, default=40)
@@ -140,11 +140,15 @@ def run_workload(name, steps, warmup, torch, pkg, workloads):
 
 def run_tree(steps, warmup, torch, pkg, workloads, name="c4"):
     """Time psispec_verify_tree on the 8-request, 32-node, V=151936 fp32 tree workload (rotation
-    sets exceeding the last-level cache); HBM roofline of the row pass over the N+1 node rows."""
+    sets exceeding the last-level cache); HBM roofline of the row pass over the N+1 node rows (and
+    the N+1 draft rows for `c4s`, whose candidates are drawn from the draft and verified by
+    recursive rejection)."""
     preset = workloads.PRESETS[name]
+    sampled = name == "c4s"
     R = preset.rotations
     t0 = time.time()
-    sets = [workloads.make_tree(preset, device="cuda", rotation=i) for i in range(R)]
+    make = workloads.make_tree_sampled if sampled else workloads.make_tree
+    sets = [make(preset, device="cuda", rotation=i) for i in range(R)]
     torch.cuda.synchronize()
     log(f"{name}: generated {R} rotation sets in {time.time() - t0:.1f}s")
     b, N, V = preset.batch, preset.N, preset.V
@@ -157,7 +161,7 @@ def run_tree(steps, warmup, torch, pkg, workloads, name="c4"):
         inp = sets[s % R]
         return pkg.psispec_verify_tree(inp.p, inp.parent, inp.node_tokens, preset.depth,
                                        temperature=preset.T, top_p=preset.top_p, seed=inp.seed,
-                                       step=s, workspace=ws)
+                                       step=s, workspace=ws, q_logits=inp.q if sampled else None)
 
     for s in range(warmup):
         step(s)
@@ -176,13 +180,15 @@ def run_tree(steps, warmup, torch, pkg, workloads, name="c4"):
         step(s)
     kern = pkg.timing_read()
     pkg.timing_enable(False)
-    row_bytes = b * (N + 1) * V * elem
+    row_bytes = b * (N + 1) * V * elem * (2 if sampled else 1)
     rs = kern.get("rowstats", (0.0, 1))
     rs_us = 1e3 * rs[0] / max(1, rs[1])
     del sets
     torch.cuda.empty_cache()
+    rule = "candidates drawn from the draft (recursive rejection)" if sampled else \
+        "top-4 candidates"
     return dict(workload=f"{name}: tree verify batch={b} N={N} nodes depth<={preset.depth} V={V} "
-                         f"{'bf16' if elem == 2 else 'fp32'} logits, T={preset.T}",
+                         f"{'bf16' if elem == 2 else 'fp32'} logits, T={preset.T}, {rule}",
                 ms_per_step=round(ms / steps, 4),
                 nodes_per_s=round(steps * b * N / (ms / 1e3), 1),
                 committed_tokens_per_s=round(committed / (ms / 1e3), 1),
@@ -567,8 +573,9 @@ def main():
     if args.workload == "c5":
         print(json.dumps(run_lmhead(args.lmhead_steps, 3, torch, pkg, workloads)), flush=True)
         return
-    if args.workload == "c4":
-        print(json.dumps(run_tree(args.tree_steps, 5, torch, pkg, workloads)), flush=True)
+    if args.workload in ("c4", "c4s"):
+        print(json.dumps(run_tree(args.tree_steps, 5, torch, pkg, workloads, args.workload)),
+              flush=True)
         return
     if args.workload == "sweep":
         batches = [int(x) for x in args.sweep_batches.split(",") if x]

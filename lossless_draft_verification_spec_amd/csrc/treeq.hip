@@ -10,9 +10,9 @@
 // c_{i+1} = c_i + S_i and S_i = sum_x max(0, p'(x) - c_i q'(x)): by induction, where p' > c_i q' the
 // next subtraction leaves p' - (c_i + S_i) q', and elsewhere both sides are 0.  So a node with m
 // children needs its exact normalisers and S_1 .. S_{m-1}, one fp64 pass over its p and q rows per
-// level (k_tree_chain; level 0 gives the normalisers).  The accept tests then need one gathered
-// token per child (k_decide_tree_sampled), and the final draw is the residual draw of the linear
-// rule with q weighted by c_m (or, at a leaf, the draw from p').
+// level (k_tree_chain; level 0 gives the normalisers), then its chain (k_tree_chain_final).  The
+// accept tests need one gathered token per child (k_decide_tree_sampled), and the final draw is the
+// residual draw of the linear rule with q weighted by c_m (or, at a leaf, the draw from p').
 #include "launch.h"
 #include "draw.h"
 
@@ -28,92 +28,160 @@ __device__ inline double sub_products(double a, double b, double c, double d) {
   return a * b - c * d;
 }
 
-// Block (g, chunk): node row g = r (N+1) + v + 1.  Level 0: children count (chunk 0 stores it) and,
-// for nodes with >= 2 children, the chunk's sums of e_p and e_q.  Level i >= 1: for nodes with
-// >= i+1 children, the chunk's sum of max(0, p' - c_i q').
+// Sum of the n entries p[0], p[stride], ... by one full wave in a fixed order: lane l adds entries
+// l, l+64, ... in turn, then a butterfly (every lane ends with the same bits).  Every kernel that
+// recombines a node's partial sums uses it, so they all see identical values.
+__device__ inline double wave_sum_fixed(const double* p, int n, int stride) {
+  const int l = threadIdx.x & 63;
+  double s = 0.0;
+  for (int k = l; k < n; k += 64) s += p[(int64_t)k * stride];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  return s;
+}
+
+__device__ inline const double* e_part_of(const TreeQArgs& a, int64_t g) {
+  return reinterpret_cast<const double*>(a.e_part + g * a.nchunk_c);
+}
+__device__ inline const double* s_part_of(const TreeQArgs& a, int level, int64_t g) {
+  return a.s_part + ((int64_t)(level - 1) * a.rs.nP + g) * a.nchunk_c;
+}
+
+// Work item (g, chunk) of a level: node row g = r (N+1) + v + 1, 4096 tokens of its p and q rows.
+// Level 0: children count (chunk 0 stores it) and, for nodes with >= 2 children, the chunk's sums
+// of e_p and e_q.  Level i >= 1: for nodes with >= i+1 children, the chunk's sum of
+// max(0, p' - c_i q').  A fixed grid loops over the items, so levels without work cost little.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level, int vec_ok) {
   __shared__ double tbl[64];
   __shared__ int s_cnt;
   __shared__ double2 s_sum[kChainWaves];
-  const int64_t g = blockIdx.x / a.nchunk_c;
-  const int chunk = (int)(blockIdx.x - g * a.nchunk_c);
-  const int r = (int)(g / (a.N + 1));
-  const int v = (int)(g - (int64_t)r * (a.N + 1)) - 1;
+  __shared__ double s_inv[2], s_c;
   exp_table_fill(tbl);
-  int m;
-  if (level == 0) {
-    if (threadIdx.x == 0) s_cnt = 0;
-    __syncthreads();
-    int cnt = 0;
-    for (int j = threadIdx.x; j < a.N; j += kThreads) cnt += a.parent[(int64_t)r * a.N + j] == v;
-    if (cnt) atomicAdd(&s_cnt, cnt);
-    __syncthreads();
-    m = s_cnt;
-    if (chunk == 0 && threadIdx.x == 0) a.nchild[g] = m;
-  } else {
-    m = a.nchild[g];
-    __syncthreads();  // the exp table
-  }
-  if (m > kMaxSampledChildren || (level == 0 ? m < 2 : m < level + 1)) return;
-
-  const int64_t prow = g, qrow = a.rs.nP + g;
-  const T* pr = row_ptr<T>(a.rs, prow);
-  const T* qr = row_ptr<T>(a.rs, qrow);
-  const float lmp = a.rowstat[prow].lmax, lmq = a.rowstat[qrow].lmax;
-  const float thp = a.use_topp ? a.topp[prow].thr : -__builtin_huge_valf();
-  const float thq = a.use_topp ? a.topp[qrow].thr : -__builtin_huge_valf();
-  double invEp = 0.0, invEq = 0.0, ci = 0.0;
-  if (level > 0) {  // the node's normalisers and c_level from the earlier levels (fixed order)
-    double Ep = 0.0, Eq = 0.0;
-    for (int k = 0; k < a.nchunk_c; ++k) {
-      const double2 e = a.e_part[g * a.nchunk_c + k];
-      Ep += e.x;
-      Eq += e.y;
-    }
-    invEp = 1.0 / Ep;
-    invEq = 1.0 / Eq;
-    ci = 1.0;
-    const int64_t nP = a.rs.nP;
-    for (int j = 1; j < level; ++j) {
-      double S = 0.0;
-      for (int k = 0; k < a.nchunk_c; ++k) S += a.s_part[((int64_t)(j - 1) * nP + g) * a.nchunk_c + k];
-      ci += S;
-    }
-  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int x0 = chunk * a.chunk_elems_c + wave * kSub + lane * kPerLane;
-  float fp[kPerLane], fq[kPerLane];
-  load_run<T, kPerLane>(pr, x0, a.V, vec_ok, fp);
-  load_run<T, kPerLane>(qr, x0, a.V, vec_ok, fq);
-  double sp = 0.0, sq = 0.0;
-#pragma unroll
-  for (int e = 0; e < kPerLane; ++e) {
-    const double ep = term(fp[e], lmp, thp, a.inv_T, tbl);
-    const double eq = term(fq[e], lmq, thq, a.inv_T, tbl);
+  const int64_t items = a.rs.nP * (int64_t)a.nchunk_c;
+  for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
+    const int64_t g = w / a.nchunk_c;
+    const int chunk = (int)(w - g * a.nchunk_c);
+    const int r = (int)(g / (a.N + 1));
+    const int v = (int)(g - (int64_t)r * (a.N + 1)) - 1;
+    int m;
     if (level == 0) {
-      sp += ep;
-      sq += eq;
+      if (threadIdx.x == 0) s_cnt = 0;
+      __syncthreads();
+      int cnt = 0;
+      for (int j = threadIdx.x; j < a.N; j += kThreads) cnt += a.parent[(int64_t)r * a.N + j] == v;
+      if (cnt) atomicAdd(&s_cnt, cnt);
+      __syncthreads();
+      m = s_cnt;
+      if (chunk == 0 && threadIdx.x == 0) a.nchild[g] = m;
     } else {
-      const double w = sub_products(ep, invEp, ci, eq * invEq);
-      sp += w > 0.0 ? w : 0.0;
+      m = a.nchild[g];
+    }
+    const bool work = m <= kMaxSampledChildren && (level == 0 ? m >= 2 : m >= level + 1);
+    if (work && level > 0 && wave == 0) {
+      // the node's normalisers and c_level = 1 + S_1 + ... + S_{level-1}
+      const double Ep = wave_sum_fixed(e_part_of(a, g), a.nchunk_c, 2);
+      const double Eq = wave_sum_fixed(e_part_of(a, g) + 1, a.nchunk_c, 2);
+      double ci = 1.0;
+      for (int j = 1; j < level; ++j) ci += wave_sum_fixed(s_part_of(a, j, g), a.nchunk_c, 1);
+      if (lane == 0) {
+        s_inv[0] = 1.0 / Ep;
+        s_inv[1] = 1.0 / Eq;
+        s_c = ci;
+      }
+    }
+    __syncthreads();
+    if (work) {
+      const int64_t prow = g, qrow = a.rs.nP + g;
+      const T* pr = row_ptr<T>(a.rs, prow);
+      const T* qr = row_ptr<T>(a.rs, qrow);
+      const float lmp = a.rowstat[prow].lmax, lmq = a.rowstat[qrow].lmax;
+      const float thp = a.use_topp ? a.topp[prow].thr : -__builtin_huge_valf();
+      const float thq = a.use_topp ? a.topp[qrow].thr : -__builtin_huge_valf();
+      const double invEp = level > 0 ? s_inv[0] : 0.0, invEq = level > 0 ? s_inv[1] : 0.0;
+      const double ci = level > 0 ? s_c : 0.0;
+      const int x0 = chunk * a.chunk_elems_c + wave * kSub + lane * kPerLane;
+      float fp[kPerLane], fq[kPerLane];
+      load_run<T, kPerLane>(pr, x0, a.V, vec_ok, fp);
+      load_run<T, kPerLane>(qr, x0, a.V, vec_ok, fq);
+      double sp = 0.0, sq = 0.0;
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e) {
+        const double ep = term(fp[e], lmp, thp, a.inv_T, tbl);
+        const double eq = term(fq[e], lmq, thq, a.inv_T, tbl);
+        if (level == 0) {
+          sp += ep;
+          sq += eq;
+        } else {
+          const double x = sub_products(ep, invEp, ci, eq * invEq);
+          sp += x > 0.0 ? x : 0.0;
+        }
+      }
+      sp = wave_sum(sp);
+      sq = wave_sum(sq);
+      if (lane == 0) s_sum[wave] = make_double2(sp, sq);
+    }
+    __syncthreads();
+    if (work && threadIdx.x == 0) {
+      double tp = 0.0, tq = 0.0;
+      for (int k = 0; k < kChainWaves; ++k) {
+        tp += s_sum[k].x;
+        tq += s_sum[k].y;
+      }
+      if (level == 0)
+        a.e_part[g * a.nchunk_c + chunk] = make_double2(tp, tq);
+      else
+        a.s_part[((int64_t)(level - 1) * a.rs.nP + g) * a.nchunk_c + chunk] = tp;
+    }
+    __syncthreads();  // the next item reuses the block's LDS
+  }
+}
+
+// One wave per node row with children: its normalisers and its residual chain (NodeChain).
+__global__ __launch_bounds__(64) void k_tree_chain_final(TreeQArgs a) {
+  const int64_t g = blockIdx.x;
+  const int m = a.nchild[g];
+  if (m < 1 || m > kMaxSampledChildren) return;
+  const int64_t nP = a.rs.nP;
+  double Ep, Eq;
+  if (m >= 2) {
+    Ep = wave_sum_fixed(e_part_of(a, g), a.nchunk_c, 2);
+    Eq = wave_sum_fixed(e_part_of(a, g) + 1, a.nchunk_c, 2);
+  } else {  // one child: the HBM pass's normalisers suffice for its ratio
+    Ep = a.rowstat[g].Z;
+    Eq = a.rowstat[nP + g].Z;
+    if (a.use_topp) {
+      Ep *= a.topp[g].M;
+      Eq *= a.topp[nP + g].M;
     }
   }
-  sp = wave_sum(sp);
-  sq = wave_sum(sq);
-  if (lane == 0) s_sum[wave] = make_double2(sp, sq);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double tp = 0.0, tq = 0.0;
-    for (int w = 0; w < kChainWaves; ++w) {
-      tp += s_sum[w].x;
-      tq += s_sum[w].y;
+  double S[kMaxSampledChildren];
+  for (int k = 1; k < m; ++k) S[k] = wave_sum_fixed(s_part_of(a, k, g), a.nchunk_c, 1);
+  if (threadIdx.x != 0) return;
+  NodeChain ch;
+  ch.Ep = Ep;
+  ch.Eq = Eq;
+  ch.c[0] = 0.0;
+  ch.S[0] = 1.0;
+  ch.stuck = kMaxSampledChildren + 1;
+  for (int k = 1; k <= m; ++k) {
+    if (ch.stuck <= k) {  // a zero residual earlier: the residual stays
+      ch.c[k] = ch.c[k - 1];
+      ch.S[k] = ch.S[k - 1];
+      continue;
     }
-    if (level == 0)
-      a.e_part[g * a.nchunk_c + chunk] = make_double2(tp, tq);
-    else
-      a.s_part[((int64_t)(level - 1) * a.rs.nP + g) * a.nchunk_c + chunk] = tp;
+    ch.c[k] = ch.c[k - 1] + ch.S[k - 1];
+    const double Sk = k < m ? S[k] : 1.0;  // S_m is never used: the final draw normalises itself
+    if (!(Sk > 0.0)) {
+      ch.stuck = k;
+      ch.c[k] = ch.c[k - 1];
+      ch.S[k] = ch.S[k - 1];
+    } else {
+      ch.S[k] = Sk;
+    }
   }
+  a.chain[g] = ch;
 }
 
 // p'(x) or q'(x) of one gathered token: exp((l - lmax) / T) / E over the nucleus
@@ -124,7 +192,7 @@ __device__ inline double gathered_prob(const TreeQArgs& a, int64_t row, int tok,
   return exp(((double)l - (double)a.rowstat[row].lmax) * a.inv_T) / E;
 }
 
-// One wave per request: structure, residual chains, node ratios, the walk, the draw description.
+// One wave per request: structure, node ratios, the walk, the draw description.
 template <typename T>
 __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
   const int r = blockIdx.x;
@@ -174,58 +242,7 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
     if (t == 0) s_st = bm ? PSISPEC_ST_BAD_PARENT : 0;
   }
 
-  // 2. residual chains of the nodes with children (lane per node; fixed-order sums)
-  for (int j = t; j <= N; j += 64) {
-    const int64_t g = row0 + j;
-    const int m = a.nchild[g];
-    if (m < 1 || m > kMaxSampledChildren) continue;
-    NodeChain ch;
-    ch.c[0] = 0.0;
-    ch.S[0] = 1.0;
-    ch.stuck = kMaxSampledChildren + 1;
-    if (m >= 2) {
-      double Ep = 0.0, Eq = 0.0;
-      for (int k = 0; k < a.nchunk_c; ++k) {
-        const double2 e = a.e_part[g * a.nchunk_c + k];
-        Ep += e.x;
-        Eq += e.y;
-      }
-      ch.Ep = Ep;
-      ch.Eq = Eq;
-    } else {  // one child: the HBM pass's normalisers suffice for its ratio
-      double Ep = a.rowstat[g].Z, Eq = a.rowstat[nP + g].Z;
-      if (a.use_topp) {
-        Ep *= a.topp[g].M;
-        Eq *= a.topp[nP + g].M;
-      }
-      ch.Ep = Ep;
-      ch.Eq = Eq;
-    }
-    for (int k = 1; k <= m; ++k) {
-      if (ch.stuck <= k) {  // a zero residual earlier: the residual stays
-        ch.c[k] = ch.c[k - 1];
-        ch.S[k] = ch.S[k - 1];
-        continue;
-      }
-      ch.c[k] = ch.c[k - 1] + ch.S[k - 1];
-      double S = 1.0;  // S[m] is never used (the final draw normalises its own weights)
-      if (k < m) {
-        S = 0.0;
-        for (int q = 0; q < a.nchunk_c; ++q) S += a.s_part[((int64_t)(k - 1) * nP + g) * a.nchunk_c + q];
-      }
-      if (!(S > 0.0)) {
-        ch.stuck = k;
-        ch.c[k] = ch.c[k - 1];
-        ch.S[k] = ch.S[k - 1];
-      } else {
-        ch.S[k] = S;
-      }
-    }
-    a.chain[g] = ch;
-  }
-  __syncthreads();
-
-  // 3. node ratios: child j is the i-th child of v (siblings in index order)
+  // 2. node ratios: child j is the i-th child of v (siblings in index order)
   for (int j = t; j < N; j += 64) {
     const int v = s_par[j], tj = s_tok[j];
     double ratio = 0.0;
@@ -257,7 +274,7 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
   for (int off = 32; off >= 1; off >>= 1) st |= __shfl_xor(st, off, 64);
   __syncthreads();
 
-  // 4. the walk: at each node the children in index order, 64 at a time; the first accepted
+  // 3. the walk: at each node the children in index order, 64 at a time; the first accepted
   //    child (ballot) is the next node
   const int Dp1 = a.max_depth + 1;
   int32_t* nodes = a.accept_nodes + (int64_t)r * a.max_depth;
@@ -317,8 +334,9 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
 
 hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype dtype,
                                   hipStream_t stream) {
-  const int64_t blocks = a.rs.nP * (int64_t)a.nchunk_c;
+  int64_t blocks = a.rs.nP * (int64_t)a.nchunk_c;
   if (blocks == 0) return hipSuccess;
+  if (blocks > 2048) blocks = 2048;  // a fixed grid loops over the work items
   const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
   const int vec_ok = ((size_t)a.V * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
                      ((uintptr_t)a.rs.q % 16) == 0;
@@ -335,6 +353,11 @@ hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype d
 
 hipError_t launch_decide_tree_sampled(const TreeQArgs& a, psispec_dtype dtype, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
+  timing_begin("tree_chain_final", stream);
+  hipLaunchKernelGGL(k_tree_chain_final, dim3((unsigned)a.rs.nP), dim3(64), 0, stream, a);
+  timing_end("tree_chain_final", stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   timing_begin("decide_tree_sampled", stream);
   if (dtype == PSISPEC_BF16)
     hipLaunchKernelGGL(k_decide_tree_sampled<bf16_t>, dim3(a.batch), dim3(64), 0, stream, a);
