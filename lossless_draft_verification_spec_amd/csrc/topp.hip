@@ -7,6 +7,16 @@
 namespace psispec {
 namespace {
 
+constexpr int kToppUnroll = 8;   // 16-byte loads in flight per thread
+constexpr int kCandQueue = 256;  // candidate logits queued per wave before they are processed
+
+template <typename T>
+__device__ inline T neg_inf();
+template <>
+__device__ inline float neg_inf<float>() { return -__builtin_huge_valf(); }
+template <>
+__device__ inline bf16_t neg_inf<bf16_t>() { return bf16_t{0xff80u}; }
+
 // ---------------------------------------------------------------------------------------------
 // Nucleus threshold by a mass-weighted radix select over the order keys of the logits, 8 bits per
 // round (2 rounds for bf16, 4 for fp32).  Masses are fixed-point integers (pi * 2^56) summed with
@@ -59,6 +69,7 @@ __global__ __launch_bounds__(kThreads) void k_topp(RowSet rs, int nchunk, float 
 
   // one histogram per wave (the candidates' keys crowd into few bins), summed in wave order
   __shared__ unsigned long long hist[kThreads / 64][256];
+  __shared__ float s_cand[kThreads / 64][kCandQueue];
   __shared__ uint32_t s_prefix;
   __shared__ unsigned long long s_above, s_kept;
   if (threadIdx.x == 0) {
@@ -66,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void k_topp(RowSet rs, int nchunk, float 
     s_above = 0;
     s_kept = 0;
   }
-  const int wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int E = 16 / (int)sizeof(T);
   const int nvec = vec_ok ? rs.V / E : 0;
   for (int round = 0; round < kRounds; ++round) {
@@ -74,29 +85,69 @@ __global__ __launch_bounds__(kThreads) void k_topp(RowSet rs, int nchunk, float 
     for (int w = 0; w < kThreads / 64; ++w) hist[w][threadIdx.x] = 0;
     __syncthreads();
     const uint32_t prefix = s_prefix;
+    // Candidates (few percent of the tokens, crowding into a few bins) are compacted per wave into
+    // an LDS queue and processed 64 at a time, so the exp and the histogram atomics run on full
+    // waves instead of on the scattered lanes of every token.
+    int fill = 0;  // queue length, the same in every lane
+    auto flush = [&]() {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      for (int k = lane; k < fill; k += 64) {
+        const float l = s_cand[wave][k];
+        const uint32_t key = kHalf ? order_key16((uint16_t)(__float_as_uint(l) >> 16)) : order_key(l);
+        const float pi = __builtin_amdgcn_exp2f((l - lmax) * c) * invZ;
+        if (!(pi >= pi_min) || pi == 0.f) continue;
+        const unsigned long long w = (unsigned long long)((double)pi * 0x1.0p56);
+        atomicAdd(&hist[wave][(key >> shift) & 255u], w);
+      }
+      __builtin_amdgcn_wave_barrier();
+      fill = 0;
+    };
     auto take = [&](T e) {
       const float l = to_f32(e);
-      if (!(l >= l_cut)) return;
-      uint32_t key;
-      if constexpr (kHalf) {
-        key = order_key16(e.bits);
-      } else {
-        key = order_key(l);
+      bool cand = l >= l_cut;
+      if (round > 0 && cand) {
+        uint32_t key;
+        if constexpr (kHalf) {
+          key = order_key16(e.bits);
+        } else {
+          key = order_key(l);
+        }
+        cand = (key >> (shift + 8)) == (prefix >> (shift + 8));
       }
-      if (round > 0 && (key >> (shift + 8)) != (prefix >> (shift + 8))) return;
-      const float pi = __builtin_amdgcn_exp2f((l - lmax) * c) * invZ;
-      if (!(pi >= pi_min) || pi == 0.f) return;
-      const unsigned long long w = (unsigned long long)((double)pi * 0x1.0p56);
-      atomicAdd(&hist[wave][(key >> shift) & 255u], w);
+      const uint64_t m = __ballot(cand);
+      if (cand) s_cand[wave][fill + __builtin_popcountll(m & ((1ull << lane) - 1ull))] = l;
+      fill += __builtin_popcountll(m);
+      if (fill > kCandQueue - 64) flush();
     };
     const u32x4* vp = reinterpret_cast<const u32x4*>(rp);
-    for (int i = threadIdx.x; i < nvec; i += kThreads) {
-      const u32x4 v = __builtin_nontemporal_load(vp + i);
+    int i = threadIdx.x;
+    // eight 16-byte loads in flight per thread, then their tokens; the loop bound is the same for
+    // every lane of a wave (the queue needs the whole wave in every step)
+    for (; i - lane + 63 + (kToppUnroll - 1) * kThreads < nvec; i += kToppUnroll * kThreads) {
+      u32x4 v[kToppUnroll];
+#pragma unroll
+      for (int u = 0; u < kToppUnroll; ++u) v[u] = __builtin_nontemporal_load(vp + i + u * kThreads);
+#pragma unroll
+      for (int u = 0; u < kToppUnroll; ++u) {
+        const T* ev = reinterpret_cast<const T*>(&v[u]);
+#pragma unroll
+        for (int k = 0; k < E; ++k) take(ev[k]);
+      }
+    }
+    // the rest: every lane of the wave takes part in each step (a token past the row is -inf)
+    const int nvec_w = (nvec + kThreads - 1) / kThreads * kThreads;
+    for (; i < nvec_w; i += kThreads) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (i < nvec) v = __builtin_nontemporal_load(vp + i);
       const T* ev = reinterpret_cast<const T*>(&v);
 #pragma unroll
-      for (int k = 0; k < E; ++k) take(ev[k]);
+      for (int k = 0; k < E; ++k) take(i < nvec ? ev[k] : neg_inf<T>());
     }
-    for (int x = nvec * E + threadIdx.x; x < rs.V; x += kThreads) take(rp[x]);
+    const int tail = nvec * E;
+    const int V_w = tail + (rs.V - tail + kThreads - 1) / kThreads * kThreads;
+    for (int x = tail + threadIdx.x; x < V_w; x += kThreads) take(x < rs.V ? rp[x] : neg_inf<T>());
+    flush();
     __syncthreads();
     {
       unsigned long long tot = 0;
