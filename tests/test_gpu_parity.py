@@ -65,6 +65,40 @@ def test_linear_temperature_and_top_p(T, top_p, dtype):
     t.check()
 
 
+@pytest.mark.parametrize("top_p", [0.9, 0.5, 0.9999999])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_top_p_wide_candidate_span(top_p, dtype):
+    """Flat rows (logits N(0, 0.5^2)): the candidates straddle zero and take tens of thousands of
+    distinct values, so bf16 rows go through the radix select rather than the one-pass count."""
+    batch, B, V = 5, 4, 20011
+    p, q, _ = _rand_linear(batch, B, V, dtype, seed=91, sigma=0.2, scale=0.5)
+    g = torch.Generator(device="cpu").manual_seed(6)
+    d = workloads.sample_drafts(q.cpu(), 1.0, top_p, g).to(DEV)
+    t = _run_and_compare(p, q, d, T=1.0, top_p=top_p, steps=range(4))
+    print(t)
+    t.check()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_top_p_signed_zero_boundary(dtype):
+    """The nucleus boundary falls on logit 0, held by +0 and -0 tokens alike: both are the boundary
+    value and all of them are kept (the kept mass is the whole row here)."""
+    batch, B, V = 3, 3, 64
+    p = torch.zeros(batch, B + 1, V)
+    p[..., 1::2] = -0.0
+    p[..., 5] = 1.0
+    p[..., 40] = 1.0
+    q = p[:, :B].clone()
+    q[..., 7] = 0.5
+    p, q = p.to(dtype), q.to(dtype)
+    assert (torch.signbit(p.float()) & (p.float() == 0)).any()
+    g = torch.Generator(device="cpu").manual_seed(8)
+    d = workloads.sample_drafts(q, 1.0, 0.5, g)
+    t = _run_and_compare(p.to(DEV), q.to(DEV), d.to(DEV), T=1.0, top_p=0.5, steps=range(8))
+    print(t)
+    t.check()
+
+
 def test_linear_first_from_target_layout():
     batch, B, V = 8, 6, 2048
     p, q, d = _rand_linear(batch, B, V, torch.bfloat16, seed=3)
