@@ -52,7 +52,8 @@ Plan make_plan(int64_t rows, int64_t batch, int V, size_t es, int excl_stride, i
   ce = (ce + 63) / 64 * 64;
   pl.nchunk = (V + ce - 1) / ce;
   pl.chunk_elems = ce;
-  if (fixed_nchunk > 0) {  // row pairs produced elsewhere (the LM-head epilogue), one per column tile
+  if (fixed_nchunk > 0) {  // row pairs produced elsewhere: one per column tile of the LM-head
+                           // epilogue, or one per row of the fused row pass and nucleus
     pl.nchunk = fixed_nchunk;
     pl.chunk_elems = 0;
   }
@@ -96,6 +97,14 @@ Plan make_plan(int64_t rows, int64_t batch, int V, size_t es, int excl_stride, i
 }
 
 size_t elem_size(psispec_dtype d) { return d == PSISPEC_BF16 ? 2 : 4; }
+
+// The row pass and the nucleus share one read of every row (one workgroup per row, the row's pair
+// as its one chunk) for bf16 rows under top-p, when the rows are many enough to fill the chip.
+constexpr int64_t kFuseRows = 256;
+bool fuse_topp(psispec_dtype dtype, int64_t rows, int V, double top_p) {
+  return dtype == PSISPEC_BF16 && top_p < 1.0 && (1.0 - top_p) / (4.0 * (double)V) >= 1e-30 &&
+         rows >= kFuseRows;
+}
 
 // Tree verify with sampled candidates: the rows of p and q, then per node row its children count,
 // the chain passes' partial sums and its residual chain.
@@ -393,7 +402,8 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
   if (batch == 0) return PSISPEC_OK;
   if (!p_logits || !q_logits || !draft_tokens || !accept_len || !out_tokens) return PSISPEC_EINVAL;
   const int64_t nP = (int64_t)batch * (B + 1), nQ = (int64_t)batch * B;
-  const Plan pl = make_plan(nP + nQ, batch, V, elem_size(dtype), 0);
+  const bool fuse = fuse_topp(dtype, nP + nQ, V, s->top_p);
+  const Plan pl = make_plan(nP + nQ, batch, V, elem_size(dtype), 0, fuse ? 1 : 0);
   if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace % kAlign) != 0)
     return PSISPEC_EWORKSPACE;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
@@ -407,10 +417,15 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
   ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
   DrawDesc* desc = carve<DrawDesc>(workspace, pl.off_desc);
 
-  if (launch_rowstats(rs, dtype, pl.nchunk, pl.chunk_elems, c, part, stream) != hipSuccess)
-    return PSISPEC_EHIP;
-  if (use_topp && launch_topp(rs, dtype, pl.nchunk, c, s->top_p, part, topp, stream) != hipSuccess)
-    return PSISPEC_EHIP;
+  if (fuse) {
+    if (launch_rowstats_topp(rs, c, s->top_p, part, topp, stream) != hipSuccess) return PSISPEC_EHIP;
+  } else {
+    if (launch_rowstats(rs, dtype, pl.nchunk, pl.chunk_elems, c, part, stream) != hipSuccess)
+      return PSISPEC_EHIP;
+    if (use_topp && launch_topp(rs, dtype, pl.nchunk, c, s->top_p, part, topp, stream) !=
+                        hipSuccess)
+      return PSISPEC_EHIP;
+  }
 
   LinearArgs la{};
   la.rs = rs;
@@ -586,7 +601,9 @@ psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
   if (fft && (!ar_logits || ar_stride < V)) return PSISPEC_EINVAL;
   if (!q_logits && !(fft && B == 1)) return PSISPEC_EINVAL;
   const int64_t rows_plan = (int64_t)batch * (B + 1), jobs = (int64_t)batch * B;
-  const Plan pl = make_plan(rows_plan, jobs, V, elem_size(dtype), 0, 0, false, true);
+  const int64_t rows_pass = (fft ? batch : 0) + (q_logits ? jobs : 0);
+  const bool fuse = fuse_topp(dtype, rows_pass, V, s->top_p);
+  const Plan pl = make_plan(rows_plan, jobs, V, elem_size(dtype), 0, fuse ? 1 : 0, false, true);
   if (rows_plan * pl.nchunk > INT32_MAX || jobs * pl.nchunk_draw > INT32_MAX) return PSISPEC_EINVAL;
   if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace % kAlign) != 0)
     return PSISPEC_EWORKSPACE;
@@ -611,7 +628,12 @@ psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
   const bool bounded = pl.nsub <= kMassLds;
   int32_t* count = carve<int32_t>(workspace, pl.off_list);
   int32_t* list = carve<int32_t>(workspace, pl.off_list + kAlign);
-  if (use_topp || !bounded) {
+  if (fuse) {  // the nucleus comes with the pairs
+    if (launch_rowstats_topp(rs, c, s->top_p, part, topp, stream) != hipSuccess) return PSISPEC_EHIP;
+    if (launch_draft_rows(rs, batch, B, fft ? 1 : 0, part, pl.nchunk, c, rowstat, desc, stream) !=
+        hipSuccess)
+      return PSISPEC_EHIP;
+  } else if (use_topp || !bounded) {
     if (launch_rowstats(rs, dtype, pl.nchunk, pl.chunk_elems, c, part, stream) != hipSuccess)
       return PSISPEC_EHIP;
     if (launch_draft_rows(rs, batch, B, fft ? 1 : 0, part, pl.nchunk, c, rowstat, desc, stream) !=

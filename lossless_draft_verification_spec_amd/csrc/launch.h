@@ -19,6 +19,10 @@ hipError_t launch_rowstats(const RowSet& rs, psispec_dtype dtype, int nchunk, in
 hipError_t launch_topp(const RowSet& rs, psispec_dtype dtype, int nchunk, float c, double top_p,
                        const float2* part, ToppStat* topp, hipStream_t stream,
                        const RowStat* rowstat = nullptr);
+// bf16 rows, top_p < 1 with (1 - top_p) / (4 V) >= 1e-30: the row pass (one pair per row, nchunk 1)
+// and the nucleus in one read of every row
+hipError_t launch_rowstats_topp(const RowSet& rs, float c, double top_p, float2* part,
+                                ToppStat* topp, hipStream_t stream);
 
 // linear.hip
 struct LinearArgs {

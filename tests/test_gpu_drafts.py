@@ -70,6 +70,16 @@ def test_drafts_temperature_and_top_p(T, top_p, dtype):
     t.check()
 
 
+@pytest.mark.parametrize("flags", [0, PSISPEC_FIRST_FROM_TARGET])
+@pytest.mark.parametrize("T,top_p", [(0.7, 0.95), (1.0, 0.5)])
+def test_drafts_fused_row_pass_top_p(T, top_p, flags):
+    """bf16 with top-p over at least 256 rows: the row pass and the nucleus share one read."""
+    p, q = _rand_rows(40, 8, 4096, torch.bfloat16, seed=17)
+    t = _compare(q, ar=p if flags else None, T=T, top_p=top_p, steps=range(3), flags=flags)
+    print(t)
+    t.check()
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_drafts_first_from_target_layouts(dtype):
     batch, B, V = 6, 5, 3000

@@ -99,6 +99,53 @@ def test_top_p_signed_zero_boundary(dtype):
     t.check()
 
 
+def _fused_rows(kind, batch, B, V, seed):
+    """bf16 blocks of at least 256 rows (the row pass and the nucleus then share one read)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    shape = (batch, B + 1, V)
+    if kind == "ramp_up":      # the maximum rises all along the row: the counts move every step
+        p = torch.linspace(-4.0, 9.0, V).expand(shape) + 0.3 * torch.randn(shape, generator=g)
+    elif kind == "ramp_down":  # the maximum comes first
+        p = torch.linspace(9.0, -4.0, V).expand(shape) + 0.3 * torch.randn(shape, generator=g)
+    elif kind == "flat":       # candidates straddle zero: the radix select after the pass
+        p = 0.5 * torch.randn(shape, generator=g)
+    else:                      # Zipf-boosted rows as in the batch-256 workload
+        p = 3.0 * torch.randn(shape, generator=g)
+        p += workloads.zipf_boost(batch * (B + 1), V, g, "cpu").view(shape)
+    q = p[:, :B] + torch.randn(batch, B, V, generator=g)
+    return p.to(torch.bfloat16), q.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("kind,V", [("zipf", 4096), ("zipf", 3001), ("ramp_up", 5000),
+                                    ("ramp_down", 4104), ("flat", 20011)])
+@pytest.mark.parametrize("T,top_p", [(0.7, 0.95), (1.0, 0.5)])
+def test_fused_row_pass_top_p(kind, V, T, top_p):
+    batch, B = 20, 8  # 340 rows
+    p, q = _fused_rows(kind, batch, B, V, seed=V + int(100 * top_p))
+    if kind == "zipf" and V == 3001:
+        p[3, 2, 17] = float("nan")  # a bad row among fused ones: its request is flagged
+    g = torch.Generator(device="cpu").manual_seed(9)
+    d = workloads.sample_drafts(q.float().nan_to_num(0.0), T, top_p, g)
+    t = _run_and_compare(p.to(DEV), q.to(DEV), d.to(DEV), T=T, top_p=top_p, steps=range(3))
+    print(t)
+    t.check()
+
+
+def test_fused_row_pass_signed_zero_boundary():
+    batch, B, V = 20, 7, 64  # 300 rows
+    p = torch.zeros(batch, B + 1, V)
+    p[..., 1::2] = -0.0
+    p[..., 5] = 1.0
+    p[..., 40] = 1.0
+    q = p[:, :B].clone()
+    q[..., 7] = 0.5
+    p, q = p.to(torch.bfloat16), q.to(torch.bfloat16)
+    g = torch.Generator(device="cpu").manual_seed(8)
+    d = workloads.sample_drafts(q, 1.0, 0.5, g)
+    t = _run_and_compare(p.to(DEV), q.to(DEV), d.to(DEV), T=1.0, top_p=0.5, steps=range(4))
+    t.check()
+
+
 def test_linear_first_from_target_layout():
     batch, B, V = 8, 6, 2048
     p, q, d = _rand_linear(batch, B, V, torch.bfloat16, seed=3)
