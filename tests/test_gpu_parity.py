@@ -146,6 +146,29 @@ def test_fused_row_pass_signed_zero_boundary():
     t.check()
 
 
+@pytest.mark.parametrize("regime", ["close", "flat", "sharp", "mixed"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_draw_regimes(regime, dtype):
+    """Final draws in the regimes that stress an inverse CDF: a draft almost equal to the target
+    (the residual is a sliver, or zero after bf16 rounding), near-uniform rows (breakpoints about
+    S / V apart), sharp rows (few heavy tokens) and a mix with equal rows (full accepts, bonus
+    draws).  Every token must match the oracle."""
+    batch, B, V = 12, 6, 6007
+    g = torch.Generator(device="cpu").manual_seed(len(regime) * 31)
+    scale = {"close": 3.0, "flat": 0.02, "sharp": 8.0, "mixed": 3.0}[regime]
+    sigma = {"close": 1e-3, "flat": 0.02, "sharp": 1.0, "mixed": 1.0}[regime]
+    p = torch.randn(batch, B + 1, V, generator=g) * scale
+    q = p[:, :B] + sigma * torch.randn(batch, B, V, generator=g)
+    if regime == "mixed":
+        q[::3] = p[::3, :B]                      # equal rows: full accepts, bonus draws
+        q[1::3] += 4.0 * torch.randn(q[1::3].shape, generator=g)
+    p, q = p.to(dtype), q.to(dtype)
+    d = workloads.sample_drafts(q, 1.0, 1.0, g)
+    t = _run_and_compare(p.to(DEV), q.to(DEV), d.to(DEV), steps=range(8))
+    print(t)
+    t.check()
+
+
 def test_linear_first_from_target_layout():
     batch, B, V = 8, 6, 2048
     p, q, d = _rand_linear(batch, B, V, torch.bfloat16, seed=3)
