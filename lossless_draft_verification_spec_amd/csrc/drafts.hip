@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_draft_bounds(DraftArgs a, int nblk
 // One block per drafted token.
 template <typename T, bool kTopp>
 __global__ __launch_bounds__(kThreads) void k_draft_select(DraftArgs a) {
-  __shared__ double tbl[64];
+  __shared__ double tbl[kExpTable];
   __shared__ double s_mass[kMassLds];
   __shared__ double s_err[kMassLds];
   __shared__ double s_wave[kThreads / 64];

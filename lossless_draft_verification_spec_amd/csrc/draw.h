@@ -74,8 +74,8 @@ __device__ inline RowView row_view(const DrawArgs& a, const DrawDesc& d) {
 
 // exp((l - lmax) / T) for a kept token, 0 outside the nucleus (and for l = -inf)
 __device__ inline double term(float l, float lmax, float thr, double inv_T, const double* tbl) {
-  if (!(l >= thr)) return 0.0;
-  return exp_tang(((double)l - (double)lmax) * inv_T, tbl);
+  const double e = exp_tang(((double)l - (double)lmax) * inv_T, tbl);
+  return l >= thr ? e : 0.0;
 }
 
 constexpr double kBand = 1e-5;  // relative band of uncertain residual signs
@@ -101,7 +101,7 @@ __device__ inline double rho_estimate(const DrawArgs& a, const DrawDesc& d) {
 // Draw chunk c of request r (every thread of a kThreads block calls it).
 template <typename T>
 __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_ok) {
-  __shared__ double tbl[64];
+  __shared__ double tbl[kExpTable];
   __shared__ int s_excl[1024];
   __shared__ double2 s_part[kThreads / 64];
   exp_table_fill(tbl);
@@ -264,7 +264,7 @@ __device__ inline double subchunk_mass(const T* prow, const T* qrow, int sub, in
 // Final draw of request r (every thread of a kThreads block calls it).
 template <typename T>
 __device__ inline void draw_select_request(const DrawArgs& a, int r) {
-  __shared__ double tbl[64];
+  __shared__ double tbl[kExpTable];
   __shared__ int s_excl[1024];
   __shared__ double s_wave[kThreads / 64];
   __shared__ int s_pick[kThreads / 64];

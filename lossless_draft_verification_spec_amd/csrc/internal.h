@@ -131,32 +131,34 @@ __device__ inline float key16_to_float(uint32_t k) {
 
 // ---------------------------------------------------------------------------------------------
 // fp64 exp by Tang's table-driven method (P. T. P. Tang, "Table-driven implementation of the
-// exponential function in IEEE floating-point arithmetic", ACM TOMS 15(2), 1989), with 64 table
-// entries: x = (64 m + j) ln2/64 + r, |r| <= ln2/128, exp(x) = 2^m * 2^(j/64) * exp(r), exp(r) - 1 by
-// its degree-5 Taylor polynomial (truncation below 3.5e-17 relative).  tbl[j] = 2^(j/64) lives in
+// exponential function in IEEE floating-point arithmetic", ACM TOMS 15(2), 1989), with 256 table
+// entries: x = (256 m + j) ln2/256 + r, |r| <= ln2/512, exp(x) = 2^m * 2^(j/256) * exp(r), exp(r) - 1
+// by its degree-4 Taylor polynomial (truncation below 4e-17 relative).  tbl[j] = 2^(j/256) lives in
 // LDS (filled by exp_table_fill).  Inputs are <= 0 here (logit minus row maximum); below -745 the
-// result underflows to 0.
+// result underflows to 0.  Branch-free: the clamped argument is always evaluated and the result
+// selected, so a wave's lanes never split on it.
 // ---------------------------------------------------------------------------------------------
+constexpr int kExpTable = 256;
 __device__ inline void exp_table_fill(double* tbl) {
-  for (int j = threadIdx.x; j < 64; j += blockDim.x) tbl[j] = exp2((double)j / 64.0);
+  for (int j = threadIdx.x; j < kExpTable; j += blockDim.x) tbl[j] = exp2((double)j / kExpTable);
 }
 
 __device__ inline double exp_tang(double x, const double* tbl) {
-  if (!(x > -745.0)) return 0.0;
-  const double kInvL = 92.33248261689366;     // 64 / ln 2
-  const double kL1 = 0.010830424696249145;    // ln 2 / 64 rounded to double
-  const double kL2 = 3.623510646634843e-19;   // ln 2 / 64 - kL1
-  const double kf = rint(x * kInvL);
+  const double xc = fmax(x, -745.0);
+  const double kInvL = 369.3299304675746;    // 256 / ln 2
+  const double kL1 = 0.0027076061740622863;  // ln 2 / 256 rounded to double
+  const double kL2 = 9.058776616587108e-20;  // ln 2 / 256 - kL1
+  const double kf = rint(xc * kInvL);
   const int k = (int)kf;
-  double r = fma(-kf, kL1, x);
+  double r = fma(-kf, kL1, xc);
   r = fma(-kf, kL2, r);
-  double t = fma(r, 1.0 / 120.0, 1.0 / 24.0);
-  t = fma(r, t, 1.0 / 6.0);
+  double t = fma(r, 1.0 / 24.0, 1.0 / 6.0);
   t = fma(r, t, 0.5);
   t = fma(r, t, 1.0);
   const double p = r * t;  // exp(r) - 1
-  const double tj = tbl[k & 63];
-  return ldexp(fma(tj, p, tj), k >> 6);
+  const double tj = tbl[k & (kExpTable - 1)];
+  const double v = ldexp(fma(tj, p, tj), k >> 8);
+  return x > -745.0 ? v : 0.0;
 }
 
 // online softmax accumulation: (m, s) with s = sum exp2((x - m) * c)

@@ -53,7 +53,7 @@ __device__ inline const double* s_part_of(const TreeQArgs& a, int level, int64_t
 // max(0, p' - c_i q').  A fixed grid loops over the items, so levels without work cost little.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level, int vec_ok) {
-  __shared__ double tbl[64];
+  __shared__ double tbl[kExpTable];
   __shared__ int s_cnt;
   __shared__ double2 s_sum[kChainWaves];
   __shared__ double s_inv[2], s_c;
