@@ -275,6 +275,21 @@ __device__ inline void draw_select_request(const DrawArgs& a, int r) {
   __shared__ double2 s_es[kEsLds];
   __shared__ double s_mass[kMassLds];
   exp_table_fill(tbl);
+  // Loads that need no descriptor go out with it: this request's chunk normalisers and this
+  // thread's first sub-chunk record (every record when nsub <= kThreads).
+  const double2* es = a.esum + (int64_t)r * a.nchunk_draw;
+  const double2* suba = a.suba + (int64_t)r * a.nsub;
+  const int32_t* subn = a.subn + (int64_t)r * a.nsub;
+  const int32_t* suboff = a.suboff + (int64_t)r * a.nsub;
+  const int t0 = threadIdx.x;
+  const double2 es_first = t0 < a.nchunk_draw ? es[t0] : make_double2(0.0, 0.0);
+  double2 A_first = make_double2(0.0, 0.0);
+  int n_first = 0, seg_first = -1;
+  if (t0 < a.nsub) {
+    A_first = suba[t0];
+    n_first = subn[t0];
+    seg_first = suboff[t0];
+  }
   const DrawDesc d = a.desc[r];
   if (d.out_idx < 0) {
     if (threadIdx.x == 0 && a.status) a.status[r] = d.st;
@@ -293,10 +308,10 @@ __device__ inline void draw_select_request(const DrawArgs& a, int r) {
   bool band_ok = true;
   if (has_q) {
     // the chunks' partial normalisers, loaded in parallel and summed in chunk order
-    const double2* es = a.esum + (int64_t)r * a.nchunk_draw;
     const bool in_lds = a.nchunk_draw <= kEsLds;
     if (in_lds) {
-      for (int k = threadIdx.x; k < a.nchunk_draw; k += kThreads) s_es[k] = es[k];
+      for (int k = threadIdx.x; k < a.nchunk_draw; k += kThreads)
+        s_es[k] = k == t0 ? es_first : es[k];
       __syncthreads();
     }
     double Ep = 0.0, Eq = 0.0;
@@ -313,23 +328,21 @@ __device__ inline void draw_select_request(const DrawArgs& a, int r) {
   const int mode = has_q ? 0 : 1;
   // sub-chunk masses: in LDS up to kMassLds sub-chunks, else in the workspace
   double* mass = a.nsub <= kMassLds ? s_mass : a.subsum + (int64_t)r * a.nsub;
-  const double2* suba = a.suba + (int64_t)r * a.nsub;
-  const int32_t* subn = a.subn + (int64_t)r * a.nsub;
   __syncthreads();
 
   // 1. mass of every sub-chunk: the positive-token sums plus its uncertain tokens (their pool
   //    segment is in token order, so the sum order is fixed); token-by-token sums only for
   //    sub-chunks whose segment did not fit and when the classification is void
   const double2* pool = a.upool ? a.upool + (int64_t)r * kUncPool : nullptr;
-  const int32_t* suboff = a.suboff + (int64_t)r * a.nsub;
   for (int j = threadIdx.x; j < a.nsub; j += kThreads) {
-    const double2 A = suba[j];
+    const bool first = j == t0;
+    const double2 A = first ? A_first : suba[j];
     if (!has_q) {
       mass[j] = A.x;
       continue;
     }
-    const int n = subn[j];
-    const int seg = n > 0 ? suboff[j] : 0;
+    const int n = first ? n_first : subn[j];
+    const int seg = n > 0 ? (first ? seg_first : suboff[j]) : 0;
     if (band_ok && seg >= 0) {
       double m = (A.x - rho * A.y) * rEp;
       m = m > 0.0 ? m : 0.0;
