@@ -50,80 +50,86 @@ __device__ inline const double* s_part_of(const TreeQArgs& a, int level, int64_t
 // Work item (g, chunk) of a level: node row g = r (N+1) + v + 1, 4096 tokens of its p and q rows.
 // Level 0: children count (chunk 0 stores it) and, for nodes with >= 2 children, the chunk's sums
 // of e_p and e_q.  Level i >= 1: for nodes with >= i+1 children, the chunk's sum of
-// max(0, p' - c_i q').  A fixed grid loops over the items, so levels without work cost little.
+// max(0, p' - c_i q').  A fixed grid loops over the items; from level 1 on, a block first looks up
+// the children counts of up to kThreads of its items in one round of loads and then works through
+// the items that have work only, so levels without work cost a launch and one load.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level, int vec_ok) {
   __shared__ double tbl[kExpTable];
   __shared__ int s_cnt;
   __shared__ double2 s_sum[kChainWaves];
   __shared__ double s_inv[2], s_c;
+  __shared__ int s_items[kThreads];
   exp_table_fill(tbl);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t items = a.rs.nP * (int64_t)a.nchunk_c;
-  for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
-    const int64_t g = w / a.nchunk_c;
-    const int chunk = (int)(w - g * a.nchunk_c);
-    const int r = (int)(g / (a.N + 1));
-    const int v = (int)(g - (int64_t)r * (a.N + 1)) - 1;
-    int m;
-    if (level == 0) {
-      if (threadIdx.x == 0) s_cnt = 0;
-      __syncthreads();
-      int cnt = 0;
-      for (int j = threadIdx.x; j < a.N; j += kThreads) cnt += a.parent[(int64_t)r * a.N + j] == v;
-      if (cnt) atomicAdd(&s_cnt, cnt);
-      __syncthreads();
-      m = s_cnt;
-      if (chunk == 0 && threadIdx.x == 0) a.nchild[g] = m;
-    } else {
-      m = a.nchild[g];
-    }
-    const bool work = m <= kMaxSampledChildren && (level == 0 ? m >= 2 : m >= level + 1);
-    if (work && level > 0 && wave == 0) {
-      // the node's normalisers and c_level = 1 + S_1 + ... + S_{level-1}
-      const double Ep = wave_sum_fixed(e_part_of(a, g), a.nchunk_c, 2);
-      const double Eq = wave_sum_fixed(e_part_of(a, g) + 1, a.nchunk_c, 2);
+
+  // the item's pass over its 4096 tokens (every thread of the block; block barriers inside)
+  auto do_item = [&](int64_t g, int chunk) {
+    if (level > 0 && wave == 0) {
+      // the node's normalisers and c_level = 1 + S_1 + ... + S_{level-1}: every array's entries
+      // loaded in one round, then summed in wave_sum_fixed's order (lane l: entries l, l+64, ...;
+      // then the butterfly)
+      const double* ep = e_part_of(a, g);
+      double se = 0.0, sq = 0.0, ss[kMaxSampledChildren - 1];
+#pragma unroll
+      for (int j = 0; j < kMaxSampledChildren - 1; ++j) ss[j] = 0.0;
+      for (int k = lane; k < a.nchunk_c; k += 64) {
+        se += ep[2 * (int64_t)k];
+        sq += ep[2 * (int64_t)k + 1];
+#pragma unroll
+        for (int j = 0; j < kMaxSampledChildren - 1; ++j)
+          if (j + 1 < level) ss[j] += s_part_of(a, j + 1, g)[k];
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        se += __shfl_xor(se, off, 64);
+        sq += __shfl_xor(sq, off, 64);
+#pragma unroll
+        for (int j = 0; j < kMaxSampledChildren - 1; ++j)
+          if (j + 1 < level) ss[j] += __shfl_xor(ss[j], off, 64);
+      }
       double ci = 1.0;
-      for (int j = 1; j < level; ++j) ci += wave_sum_fixed(s_part_of(a, j, g), a.nchunk_c, 1);
+#pragma unroll
+      for (int j = 0; j < kMaxSampledChildren - 1; ++j)
+        if (j + 1 < level) ci += ss[j];
       if (lane == 0) {
-        s_inv[0] = 1.0 / Ep;
-        s_inv[1] = 1.0 / Eq;
+        s_inv[0] = 1.0 / se;
+        s_inv[1] = 1.0 / sq;
         s_c = ci;
       }
     }
     __syncthreads();
-    if (work) {
-      const int64_t prow = g, qrow = a.rs.nP + g;
-      const T* pr = row_ptr<T>(a.rs, prow);
-      const T* qr = row_ptr<T>(a.rs, qrow);
-      const float lmp = a.rowstat[prow].lmax, lmq = a.rowstat[qrow].lmax;
-      const float thp = a.use_topp ? a.topp[prow].thr : -__builtin_huge_valf();
-      const float thq = a.use_topp ? a.topp[qrow].thr : -__builtin_huge_valf();
-      const double invEp = level > 0 ? s_inv[0] : 0.0, invEq = level > 0 ? s_inv[1] : 0.0;
-      const double ci = level > 0 ? s_c : 0.0;
-      const int x0 = chunk * a.chunk_elems_c + wave * kSub + lane * kPerLane;
-      float fp[kPerLane], fq[kPerLane];
-      load_run<T, kPerLane>(pr, x0, a.V, vec_ok, fp);
-      load_run<T, kPerLane>(qr, x0, a.V, vec_ok, fq);
-      double sp = 0.0, sq = 0.0;
+    const int64_t prow = g, qrow = a.rs.nP + g;
+    const T* pr = row_ptr<T>(a.rs, prow);
+    const T* qr = row_ptr<T>(a.rs, qrow);
+    const float lmp = a.rowstat[prow].lmax, lmq = a.rowstat[qrow].lmax;
+    const float thp = a.use_topp ? a.topp[prow].thr : -__builtin_huge_valf();
+    const float thq = a.use_topp ? a.topp[qrow].thr : -__builtin_huge_valf();
+    const double invEp = level > 0 ? s_inv[0] : 0.0, invEq = level > 0 ? s_inv[1] : 0.0;
+    const double ci = level > 0 ? s_c : 0.0;
+    const int x0 = chunk * a.chunk_elems_c + wave * kSub + lane * kPerLane;
+    float fp[kPerLane], fq[kPerLane];
+    load_run<T, kPerLane>(pr, x0, a.V, vec_ok, fp);
+    load_run<T, kPerLane>(qr, x0, a.V, vec_ok, fq);
+    double sp = 0.0, sq = 0.0;
 #pragma unroll
-      for (int e = 0; e < kPerLane; ++e) {
-        const double ep = term(fp[e], lmp, thp, a.inv_T, tbl);
-        const double eq = term(fq[e], lmq, thq, a.inv_T, tbl);
-        if (level == 0) {
-          sp += ep;
-          sq += eq;
-        } else {
-          const double x = sub_products(ep, invEp, ci, eq * invEq);
-          sp += x > 0.0 ? x : 0.0;
-        }
+    for (int e = 0; e < kPerLane; ++e) {
+      const double ep = term(fp[e], lmp, thp, a.inv_T, tbl);
+      const double eq = term(fq[e], lmq, thq, a.inv_T, tbl);
+      if (level == 0) {
+        sp += ep;
+        sq += eq;
+      } else {
+        const double x = sub_products(ep, invEp, ci, eq * invEq);
+        sp += x > 0.0 ? x : 0.0;
       }
-      sp = wave_sum(sp);
-      sq = wave_sum(sq);
-      if (lane == 0) s_sum[wave] = make_double2(sp, sq);
     }
+    sp = wave_sum(sp);
+    sq = wave_sum(sq);
+    if (lane == 0) s_sum[wave] = make_double2(sp, sq);
     __syncthreads();
-    if (work && threadIdx.x == 0) {
+    if (threadIdx.x == 0) {
       double tp = 0.0, tq = 0.0;
       for (int k = 0; k < kChainWaves; ++k) {
         tp += s_sum[k].x;
@@ -135,6 +141,45 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
         a.s_part[((int64_t)(level - 1) * a.rs.nP + g) * a.nchunk_c + chunk] = tp;
     }
     __syncthreads();  // the next item reuses the block's LDS
+  };
+
+  if (level == 0) {
+    for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
+      const int64_t g = w / a.nchunk_c;
+      const int chunk = (int)(w - g * a.nchunk_c);
+      const int r = (int)(g / (a.N + 1));
+      const int v = (int)(g - (int64_t)r * (a.N + 1)) - 1;
+      if (threadIdx.x == 0) s_cnt = 0;
+      __syncthreads();
+      int cnt = 0;
+      for (int j = threadIdx.x; j < a.N; j += kThreads) cnt += a.parent[(int64_t)r * a.N + j] == v;
+      if (cnt) atomicAdd(&s_cnt, cnt);
+      __syncthreads();
+      const int m = s_cnt;
+      if (chunk == 0 && threadIdx.x == 0) a.nchild[g] = m;
+      __syncthreads();  // s_cnt is read by every thread before the next item resets it
+      if (m >= 2 && m <= kMaxSampledChildren) do_item(g, chunk);
+    }
+    return;
+  }
+  // items blockIdx.x + k gridDim.x, kThreads at a time: their children counts in one round
+  const int64_t stride = gridDim.x;
+  for (int64_t base = blockIdx.x; base < items; base += stride * kThreads) {
+    if (threadIdx.x == 0) s_cnt = 0;
+    __syncthreads();
+    const int64_t w = base + (int64_t)threadIdx.x * stride;
+    if (w < items) {
+      const int m = a.nchild[w / a.nchunk_c];
+      if (m >= level + 1 && m <= kMaxSampledChildren) s_items[atomicAdd(&s_cnt, 1)] = threadIdx.x;
+    }
+    __syncthreads();
+    const int nit = s_cnt;
+    for (int it = 0; it < nit; ++it) {
+      const int64_t w2 = base + (int64_t)s_items[it] * stride;
+      const int64_t g = w2 / a.nchunk_c;
+      do_item(g, (int)(w2 - g * a.nchunk_c));
+    }
+    __syncthreads();  // s_cnt and s_items are reset by the next round
   }
 }
 
