@@ -189,11 +189,33 @@ __global__ __launch_bounds__(64) void k_tree_chain_final(TreeQArgs a) {
   const int m = a.nchild[g];
   if (m < 1 || m > kMaxSampledChildren) return;
   const int64_t nP = a.rs.nP;
-  double Ep, Eq;
-  if (m >= 2) {
-    Ep = wave_sum_fixed(e_part_of(a, g), a.nchunk_c, 2);
-    Eq = wave_sum_fixed(e_part_of(a, g) + 1, a.nchunk_c, 2);
-  } else {  // one child: the HBM pass's normalisers suffice for its ratio
+  const int lane = threadIdx.x;
+  // the normalisers (two or more children) and S_1 .. S_{m-1}: every array's entries in one round of
+  // loads, then summed in wave_sum_fixed's order (lane l: entries l, l+64, ...; then the butterfly)
+  const double* ep = e_part_of(a, g);
+  double se = 0.0, sq = 0.0, S[kMaxSampledChildren];
+#pragma unroll
+  for (int k = 0; k < kMaxSampledChildren; ++k) S[k] = 0.0;
+  for (int k = lane; k < a.nchunk_c; k += 64) {
+    if (m >= 2) {
+      se += ep[2 * (int64_t)k];
+      sq += ep[2 * (int64_t)k + 1];
+    }
+#pragma unroll
+    for (int j = 1; j < kMaxSampledChildren; ++j)
+      if (j < m) S[j] += s_part_of(a, j, g)[k];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    se += __shfl_xor(se, off, 64);
+    sq += __shfl_xor(sq, off, 64);
+#pragma unroll
+    for (int j = 1; j < kMaxSampledChildren; ++j)
+      if (j < m) S[j] += __shfl_xor(S[j], off, 64);
+  }
+  if (lane != 0) return;
+  double Ep = se, Eq = sq;
+  if (m < 2) {  // one child: the HBM pass's normalisers suffice for its ratio
     Ep = a.rowstat[g].Z;
     Eq = a.rowstat[nP + g].Z;
     if (a.use_topp) {
@@ -201,16 +223,19 @@ __global__ __launch_bounds__(64) void k_tree_chain_final(TreeQArgs a) {
       Eq *= a.topp[nP + g].M;
     }
   }
-  double S[kMaxSampledChildren];
-  for (int k = 1; k < m; ++k) S[k] = wave_sum_fixed(s_part_of(a, k, g), a.nchunk_c, 1);
-  if (threadIdx.x != 0) return;
   NodeChain ch;
   ch.Ep = Ep;
   ch.Eq = Eq;
   ch.c[0] = 0.0;
   ch.S[0] = 1.0;
   ch.stuck = kMaxSampledChildren + 1;
-  for (int k = 1; k <= m; ++k) {
+#pragma unroll
+  for (int k = 1; k <= kMaxSampledChildren; ++k) {
+    if (k > m) {
+      ch.c[k] = 0.0;
+      ch.S[k] = 0.0;
+      continue;
+    }
     if (ch.stuck <= k) {  // a zero residual earlier: the residual stays
       ch.c[k] = ch.c[k - 1];
       ch.S[k] = ch.S[k - 1];
