@@ -72,9 +72,11 @@ __device__ inline RowView row_view(const DrawArgs& a, const DrawDesc& d) {
   return v;
 }
 
-// exp((l - lmax) / T) for a kept token, 0 outside the nucleus (and for l = -inf)
+// exp((l - lmax) / T) for a kept token, 0 outside the nucleus (and for l = -inf): 2^(t/256) with
+// t = l c256 - lmax c256 by one fused multiply-add (c256 and lmax c256 are loop invariants)
 __device__ inline double term(float l, float lmax, float thr, double inv_T, const double* tbl) {
-  const double e = exp_tang(((double)l - (double)lmax) * inv_T, tbl);
+  const double c256 = inv_T * k256Log2e;
+  const double e = exp2_256(fma((double)l, c256, -((double)lmax * c256)), tbl);
   return l >= thr ? e : 0.0;
 }
 

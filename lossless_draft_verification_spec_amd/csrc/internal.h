@@ -161,6 +161,31 @@ __device__ inline double exp_tang(double x, const double* tbl) {
   return x > -745.0 ? v : 0.0;
 }
 
+// 2^(t/256) for t = 256 log2(e) (l - lmax) / T formed by one fused multiply-add,
+// t = l c256 - lmax c256: with r = t - rint(t) (exact, |r| <= 1/2), 2^(t/256) = 2^m 2^(j/256) 2^(r/256)
+// and 2^(r/256) - 1 by its degree-4 Taylor polynomial in r (coefficients (ln 2/256)^i / i!,
+// truncation below 4e-17).  Same table as exp_tang.  Relative error against exp((l - lmax) / T):
+// below 1e-14 for |l - lmax| / T up to 80, 2.2e-13 at 4600 (the rounding of lmax c256 scales with
+// it), as exp_tang's own argument rounding does.  Branch-free; below 2^-1074 the result is 0.
+constexpr double k256Log2e = 369.3299304675746;  // 256 / ln 2
+__device__ inline double exp2_256(double t, const double* tbl) {
+  const double c1 = 0.0027076061740622863;   // ln 2 / 256
+  const double c2 = 3.6655655969101062e-06;  // (ln 2 / 256)^2 / 2
+  const double c3 = 3.3083026805413713e-09;  // (ln 2 / 256)^3 / 6
+  const double c4 = 2.239395190875157e-12;   // (ln 2 / 256)^4 / 24
+  const double tc = fmax(t, -275000.0);
+  const double kf = rint(tc);
+  const int k = (int)kf;
+  const double r = tc - kf;
+  double s = fma(r, c4, c3);
+  s = fma(r, s, c2);
+  s = fma(r, s, c1);
+  const double p = r * s;  // 2^(r/256) - 1
+  const double tj = tbl[k & (kExpTable - 1)];
+  const double v = ldexp(fma(tj, p, tj), k >> 8);
+  return t > -275000.0 ? v : 0.0;
+}
+
 // online softmax accumulation: (m, s) with s = sum exp2((x - m) * c)
 __device__ inline void os_combine(float& m, float& s, float m2, float s2, float c) {
   const float mn = fmaxf(m, m2);
