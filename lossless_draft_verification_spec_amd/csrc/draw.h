@@ -72,11 +72,14 @@ __device__ inline RowView row_view(const DrawArgs& a, const DrawDesc& d) {
   return v;
 }
 
-// exp((l - lmax) / T) for a kept token, 0 outside the nucleus (and for l = -inf): 2^(t/256) with
-// t = l c256 - lmax c256 by one fused multiply-add (c256 and lmax c256 are loop invariants)
+// exp((l - lmax) / T) for a kept token, 0 outside the nucleus (and for l = -inf or NaN): 2^(t/256)
+// with t = l c256 - lmax c256 by one fused multiply-add (c256 and lmax c256 are loop invariants).
+// kTopp = false skips the nucleus test (thr = -inf keeps every finite logit).
+template <bool kTopp = true>
 __device__ inline double term(float l, float lmax, float thr, double inv_T, const double* tbl) {
   const double c256 = inv_T * k256Log2e;
   const double e = exp2_256(fma((double)l, c256, -((double)lmax * c256)), tbl);
+  if constexpr (!kTopp) return e;
   return l >= thr ? e : 0.0;
 }
 
@@ -101,7 +104,7 @@ __device__ inline double rho_estimate(const DrawArgs& a, const DrawDesc& d) {
 }
 
 // Draw chunk c of request r (every thread of a kThreads block calls it).
-template <typename T>
+template <typename T, bool kTopp>
 __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_ok) {
   __shared__ double tbl[kExpTable];
   __shared__ int s_excl[1024];
@@ -134,8 +137,8 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
       // four tokens' fp64 chains at a time: 110 instead of 149 VGPRs, 4 waves per SIMD
 #pragma unroll 4
       for (int e = 0; e < kPerLane; ++e) {
-        const double ep = term(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl);
-        const double eq = term(fq[e], v.lmax_q, v.thr_q, a.inv_T, tbl);
+        const double ep = term<kTopp>(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl);
+        const double eq = term<kTopp>(fq[e], v.lmax_q, v.thr_q, a.inv_T, tbl);
         Ep += ep;
         Eq += eq;
         const double diff = ep - rho * eq, band = kBand * (ep + rho * eq);
@@ -166,8 +169,8 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
           // the few uncertain tokens re-read their logits (cached): no register copy of the run
           for (uint32_t m = umask; m; m &= m - 1) {
             const int x = x0 + __builtin_ctz(m);
-            *dst++ = make_double2(term(to_f32(prow[x]), v.lmax_p, v.thr_p, a.inv_T, tbl),
-                                  term(to_f32(qrow[x]), v.lmax_q, v.thr_q, a.inv_T, tbl));
+            *dst++ = make_double2(term<kTopp>(to_f32(prow[x]), v.lmax_p, v.thr_p, a.inv_T, tbl),
+                                  term<kTopp>(to_f32(qrow[x]), v.lmax_q, v.thr_q, a.inv_T, tbl));
           }
         }
       }
@@ -175,7 +178,7 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
     } else {
 #pragma unroll
       for (int e = 0; e < kPerLane; ++e) {
-        double ep = term(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl);
+        double ep = term<kTopp>(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl);
         if (nexcl && excluded(x0 + e, s_excl, nexcl)) ep = 0.0;
         Ap += ep;
       }

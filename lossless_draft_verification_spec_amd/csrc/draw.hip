@@ -34,18 +34,18 @@
 namespace psispec {
 namespace {
 
-template <typename T>
+template <typename T, bool kTopp>
 __global__ __launch_bounds__(kThreads) void k_draw_pass(DrawArgs a, int vec_ok) {
   if (!a.list) {
     const int r = blockIdx.x / a.nchunk_draw;
-    draw_pass_task<T>(a, r, blockIdx.x - r * a.nchunk_draw, vec_ok);
+    draw_pass_task<T, kTopp>(a, r, blockIdx.x - r * a.nchunk_draw, vec_ok);
     return;
   }
   // listed draws only: the grid loops over (list entry, chunk) pairs
   const int n = *a.count * a.nchunk_draw;
   for (int w = blockIdx.x; w < n; w += gridDim.x) {
     const int e = w / a.nchunk_draw;
-    draw_pass_task<T>(a, a.list[e], w - e * a.nchunk_draw, vec_ok);
+    draw_pass_task<T, kTopp>(a, a.list[e], w - e * a.nchunk_draw, vec_ok);
     __syncthreads();  // the next task refills the block's LDS
   }
 }
@@ -82,10 +82,21 @@ hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t strea
                      ((size_t)a.rs.pstride * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
                      ((uintptr_t)a.rs.q % 16) == 0;
   timing_begin("draw_pass", stream);
-  if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL(k_draw_pass<bf16_t>, dim3(grid), dim3(kThreads), 0, stream, a, vec_ok);
-  else
-    hipLaunchKernelGGL(k_draw_pass<float>, dim3(grid), dim3(kThreads), 0, stream, a, vec_ok);
+  if (dtype == PSISPEC_BF16) {
+    if (a.use_topp)
+      hipLaunchKernelGGL((k_draw_pass<bf16_t, true>), dim3(grid), dim3(kThreads), 0, stream, a,
+                         vec_ok);
+    else
+      hipLaunchKernelGGL((k_draw_pass<bf16_t, false>), dim3(grid), dim3(kThreads), 0, stream, a,
+                         vec_ok);
+  } else {
+    if (a.use_topp)
+      hipLaunchKernelGGL((k_draw_pass<float, true>), dim3(grid), dim3(kThreads), 0, stream, a,
+                         vec_ok);
+    else
+      hipLaunchKernelGGL((k_draw_pass<float, false>), dim3(grid), dim3(kThreads), 0, stream, a,
+                         vec_ok);
+  }
   timing_end("draw_pass", stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
