@@ -119,37 +119,74 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
                     ? node_prob<T>(a, row0 + v + 1, s_lmax[v + 1], s_Z[v + 1], tj)
                     : 0.0;
   }
-  // first[s]: no earlier sibling of s carries s's token (each distinct removed token counts once)
-  for (int j = t; j < N; j += 64) {
-    const int v = s_par[j], tj = s_tok[j];
-    int first = 1;
-#pragma unroll 8
-    for (int s2 = 0; s2 < N; ++s2) first &= !(s2 < j && s_par[s2] == v && s_tok[s2] == tj);
-    s_first[j] = first;
-  }
+  // first[s]: no earlier sibling of s carries s's token (each distinct removed token counts once).
+  // With N <= 64, node s sits in lane s and the loops over the earlier siblings read its parent,
+  // token, flag and probability from that lane (v_readlane, wave-uniform index: scalar values, no
+  // LDS round trips); larger trees read LDS.  Either way R takes the same subtractions in index
+  // order.
   __syncthreads();
-  for (int j = t; j < N; j += 64) {
-    const int v = s_par[j];
-    double ratio = 0.0;
-    const int tj = s_tok[j];
-    if (tj < 0 || tj >= V) {
-      st |= PSISPEC_ST_BAD_TOKEN;
-    } else if (v >= -1 && v < j) {
-      double res = s_pown[j];
-      double R = 1.0;
-#pragma unroll 8
-      for (int s = 0; s < N; ++s) {  // earlier siblings, in index order
-        const int ts = s_tok[s];
-        if (s >= j || s_par[s] != v || ts < 0 || ts >= V) continue;
-        if (ts == tj)
-          res = 0.0;  // same token rejected earlier: already removed from the residual
-        else if (s_first[s])
-          R -= s_pown[s];
-      }
-      ratio = R > 0.0 ? fmin(1.0, res / R) : 0.0;
+  if (N <= 64) {
+    const int pj = t < N ? s_par[t] : -2, tj = t < N ? s_tok[t] : -1;
+    const double pown = t < N ? s_pown[t] : 0.0;
+    const int pown_lo = __double2loint(pown), pown_hi = __double2hiint(pown);
+    int first = 1;
+    for (int s2 = 0; s2 < N; ++s2) {
+      const int ps = __builtin_amdgcn_readlane(pj, s2), ts = __builtin_amdgcn_readlane(tj, s2);
+      first &= !(s2 < t && ps == pj && ts == tj);
     }
-    s_ratio[j] = ratio;
-    if (a.node_ratios) a.node_ratios[(int64_t)r * N + j] = (float)ratio;
+    double ratio = 0.0;
+    if (t < N) {
+      if (tj < 0 || tj >= V) st |= PSISPEC_ST_BAD_TOKEN;
+    }
+    double res = pown, R = 1.0;
+    for (int s2 = 0; s2 < N; ++s2) {  // earlier siblings, in index order
+      const int ps = __builtin_amdgcn_readlane(pj, s2), ts = __builtin_amdgcn_readlane(tj, s2);
+      const int fs = __builtin_amdgcn_readlane(first, s2);
+      const double ws = __hiloint2double(__builtin_amdgcn_readlane(pown_hi, s2),
+                                         __builtin_amdgcn_readlane(pown_lo, s2));
+      if (s2 >= t || ps != pj || ts < 0 || ts >= V) continue;
+      if (ts == tj)
+        res = 0.0;  // same token rejected earlier: already removed from the residual
+      else if (fs)
+        R -= ws;
+    }
+    if (t < N) {
+      if (tj >= 0 && tj < V && pj >= -1 && pj < t) ratio = R > 0.0 ? fmin(1.0, res / R) : 0.0;
+      s_ratio[t] = ratio;
+      if (a.node_ratios) a.node_ratios[(int64_t)r * N + t] = (float)ratio;
+    }
+  } else {
+    for (int j = t; j < N; j += 64) {
+      const int v = s_par[j], tj = s_tok[j];
+      int first = 1;
+#pragma unroll 8
+      for (int s2 = 0; s2 < N; ++s2) first &= !(s2 < j && s_par[s2] == v && s_tok[s2] == tj);
+      s_first[j] = first;
+    }
+    __syncthreads();
+    for (int j = t; j < N; j += 64) {
+      const int v = s_par[j];
+      double ratio = 0.0;
+      const int tj = s_tok[j];
+      if (tj < 0 || tj >= V) {
+        st |= PSISPEC_ST_BAD_TOKEN;
+      } else if (v >= -1 && v < j) {
+        double res = s_pown[j];
+        double R = 1.0;
+#pragma unroll 8
+        for (int s2 = 0; s2 < N; ++s2) {  // earlier siblings, in index order
+          const int ts = s_tok[s2];
+          if (s2 >= j || s_par[s2] != v || ts < 0 || ts >= V) continue;
+          if (ts == tj)
+            res = 0.0;  // same token rejected earlier: already removed from the residual
+          else if (s_first[s2])
+            R -= s_pown[s2];
+        }
+        ratio = R > 0.0 ? fmin(1.0, res / R) : 0.0;
+      }
+      s_ratio[j] = ratio;
+      if (a.node_ratios) a.node_ratios[(int64_t)r * N + j] = (float)ratio;
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) st |= __shfl_xor(st, off, 64);
