@@ -110,7 +110,7 @@ bool fuse_topp(psispec_dtype dtype, int64_t rows, int V, double top_p) {
 // the chain passes' partial sums and its residual chain.
 struct TreeQPlan {
   Plan pl;
-  size_t off_nchild, off_epart, off_spart, off_chain, total;
+  size_t off_nchild, off_epart, off_spart, off_band, off_fb, off_chain, total;
 };
 
 TreeQPlan make_treeq_plan(int batch, int N, int V, size_t es) {
@@ -125,6 +125,10 @@ TreeQPlan make_treeq_plan(int batch, int N, int V, size_t es) {
   off = align_up(off + sizeof(double2) * (size_t)nP * nc);
   tp.off_spart = off;
   off = align_up(off + sizeof(double) * (size_t)(kMaxSampledChildren - 1) * (size_t)nP * nc);
+  tp.off_band = off;
+  off = align_up(off + sizeof(BandPart) * (size_t)nP * nc);
+  tp.off_fb = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)nP * nc);
   tp.off_chain = off;
   off = align_up(off + sizeof(NodeChain) * (size_t)nP);
   tp.total = off;
@@ -288,6 +292,8 @@ psispec_status verify_tree_sampled(const void* p_logits, const void* q_logits, p
   ta.nchild = carve<int32_t>(workspace, tp.off_nchild);
   ta.e_part = carve<double2>(workspace, tp.off_epart);
   ta.s_part = carve<double>(workspace, tp.off_spart);
+  ta.band = carve<BandPart>(workspace, tp.off_band);
+  ta.fb = carve<int32_t>(workspace, tp.off_fb);
   ta.chain = carve<NodeChain>(workspace, tp.off_chain);
   ta.desc = desc;
   ta.ucount = carve<int32_t>(workspace, pl.off_ucount);
@@ -295,8 +301,11 @@ psispec_status verify_tree_sampled(const void* p_logits, const void* q_logits, p
   ta.accept_nodes = accept_nodes;
   ta.out_tokens = out_tokens;
   ta.node_ratios = node_ratios;
-  for (int level = 0; level < kMaxSampledChildren; ++level)
+  if (launch_tree_children(ta, stream) != hipSuccess) return PSISPEC_EHIP;
+  for (int level = 0; level < kMaxSampledChildren; ++level) {
+    if (level == 1 && launch_tree_resolve(ta, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
     if (launch_tree_chain_pass(ta, level, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
+  }
   if (launch_decide_tree_sampled(ta, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
 
   DrawArgs da{};

@@ -120,6 +120,13 @@ struct NodeChain {
   double c[kMaxSampledChildren + 1];
   int stuck;
 };
+// Level 0's split of one chunk's terms of S_1 = sum_x max(0, p'(x) - q'(x)) (see k_tree_chain)
+constexpr int kBandSlots = 8;  // in-between tokens kept per chunk
+struct BandPart {
+  double pa, qa;            // sums of e_p and e_q over the chunk's tokens surely in the support
+  int32_t n;                // in-between tokens seen (more than kBandSlots: the chunk is redone)
+  int32_t x[kBandSlots];    // their indices (the first kBandSlots seen, in no fixed order)
+};
 struct TreeQArgs {
   RowSet rs;                // p rows [0, nP), q rows [nP, 2 nP), nP = batch (N+1)
   const int32_t* parent;
@@ -135,6 +142,8 @@ struct TreeQArgs {
   int32_t* nchild;          // [nP] children per node row (written by the level-0 pass)
   double2* e_part;          // [nP][nchunk_c] (sum e_p, sum e_q) over the kept tokens
   double* s_part;           // [kMaxSampledChildren - 1][nP][nchunk_c] residual masses
+  BandPart* band;           // [nP][nchunk_c] level 0's split of S_1
+  int32_t* fb;              // [nP][nchunk_c] 1: the level-1 pass recomputes the chunk
   NodeChain* chain;         // [nP]
   DrawDesc* desc;
   int32_t* ucount;
@@ -143,8 +152,10 @@ struct TreeQArgs {
   int32_t* out_tokens;
   float* node_ratios;
 };
+hipError_t launch_tree_children(const TreeQArgs& a, hipStream_t stream);
 hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype dtype,
                                   hipStream_t stream);
+hipError_t launch_tree_resolve(const TreeQArgs& a, psispec_dtype dtype, hipStream_t stream);
 hipError_t launch_decide_tree_sampled(const TreeQArgs& a, psispec_dtype dtype, hipStream_t stream);
 
 // draw.hip -- the fp64 inverse-CDF draw shared by the verify entry points and the drafting step

@@ -10,7 +10,8 @@
 // c_{i+1} = c_i + S_i and S_i = sum_x max(0, p'(x) - c_i q'(x)): by induction, where p' > c_i q' the
 // next subtraction leaves p' - (c_i + S_i) q', and elsewhere both sides are 0.  So a node with m
 // children needs its exact normalisers and S_1 .. S_{m-1}, one fp64 pass over its p and q rows per
-// level (k_tree_chain; level 0 gives the normalisers), then its chain (k_tree_chain_final).  The
+// level (k_tree_chain; level 0 gives the normalisers and, from the row pass's estimate of their
+// ratio, most of S_1, which k_tree_resolve completes), then its chain (k_tree_chain_final).  The
 // accept tests need one gathered token per child (k_decide_tree_sampled), and the final draw is the
 // residual draw of the linear rule with q weighted by c_m (or, at a leaf, the draw from p').
 #include "launch.h"
@@ -47,17 +48,49 @@ __device__ inline const double* s_part_of(const TreeQArgs& a, int level, int64_t
   return a.s_part + ((int64_t)(level - 1) * a.rs.nP + g) * a.nchunk_c;
 }
 
+// Children per node row: one block per request counts the parents (entries outside -1 .. N-1 are
+// counted for no row; the decide rejects them).
+__global__ __launch_bounds__(256) void k_tree_children(TreeQArgs a) {
+  __shared__ int s_cnt[1025];
+  const int r = blockIdx.x, N = a.N;
+  for (int j = threadIdx.x; j <= N; j += 256) s_cnt[j] = 0;
+  __syncthreads();
+  for (int j = threadIdx.x; j < N; j += 256) {
+    const int v = a.parent[(int64_t)r * N + j];
+    if (v >= -1 && v < N) atomicAdd(&s_cnt[v + 1], 1);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j <= N; j += 256) a.nchild[(int64_t)r * (N + 1) + j] = s_cnt[j];
+}
+
+// kappa = E_p / E_q estimated from the row pass (its fp32 sums, times the nucleus masses).  Level 0
+// classifies a token as surely inside the support of max(0, p' - q') when e_p > kappa (1 + d) e_q,
+// surely outside when e_p <= kappa (1 - d) e_q (the tests on the fp64 terms themselves: 0 and 0, as
+// past a row's end, is outside), and keeps the indices of the few in between; the resolve accepts
+// the split only when the exact ratio lies well inside the band (within d / 4), so a wrong estimate
+// costs a recomputation, never a wrong sum.
+constexpr double kBandRel = 1.0 / 65536.0;
+__device__ inline double kappa_est(const TreeQArgs& a, int64_t g) {
+  double zp = a.rowstat[g].Z, zq = a.rowstat[a.rs.nP + g].Z;
+  if (a.use_topp) {
+    zp *= a.topp[g].M;
+    zq *= a.topp[a.rs.nP + g].M;
+  }
+  return zp / zq;
+}
+
 // Work item (g, chunk) of a level: node row g = r (N+1) + v + 1, 4096 tokens of its p and q rows.
-// Level 0: children count (chunk 0 stores it) and, for nodes with >= 2 children, the chunk's sums
-// of e_p and e_q.  Level i >= 1: for nodes with >= i+1 children, the chunk's sum of
-// max(0, p' - c_i q').  A fixed grid loops over the items; from level 1 on, a block first looks up
-// the children counts of up to kThreads of its items in one round of loads and then works through
-// the items that have work only, so levels without work cost a launch and one load.
-template <typename T>
+// Level 0, nodes with >= 2 children: the chunk's sums of e_p and e_q, and the split of S_1's terms
+// above (BandPart).  Level 1: only the chunks whose split the resolve did not accept, the chunk's
+// sum of max(0, p' - q').  Level i >= 2, nodes with >= i+1 children: the chunk's sum of
+// max(0, p' - c_i q').  A fixed grid loops over the items: a block looks up the children counts of
+// up to kThreads of its items in one round of loads and then works through the items that have
+// work only, so levels without work cost a launch and one load.
+template <typename T, bool kFirst>
 __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level, int vec_ok) {
   __shared__ double tbl[kExpTable];
-  __shared__ int s_cnt;
-  __shared__ double2 s_sum[kChainWaves];
+  __shared__ int s_cnt, s_nband;
+  __shared__ double s_sum[kChainWaves][4];
   __shared__ double s_inv[2], s_c;
   __shared__ int s_items[kThreads];
   exp_table_fill(tbl);
@@ -66,7 +99,22 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
 
   // the item's pass over its 4096 tokens (every thread of the block; block barriers inside)
   auto do_item = [&](int64_t g, int chunk) {
-    if (level > 0 && wave == 0) {
+    const int64_t prow = g, qrow = a.rs.nP + g, item = g * a.nchunk_c + chunk;
+    // the item's loads first (tokens, row statistics), in flight while wave 0 sums the node's parts
+    const int x0 = chunk * a.chunk_elems_c + wave * kSub + lane * kPerLane;
+    float fp[kPerLane], fq[kPerLane];
+    load_run<T, kPerLane>(row_ptr<T>(a.rs, prow), x0, a.V, vec_ok, fp);
+    load_run<T, kPerLane>(row_ptr<T>(a.rs, qrow), x0, a.V, vec_ok, fq);
+    const float lmp = a.rowstat[prow].lmax, lmq = a.rowstat[qrow].lmax;
+    const float thp = a.use_topp ? a.topp[prow].thr : -__builtin_huge_valf();
+    const float thq = a.use_topp ? a.topp[qrow].thr : -__builtin_huge_valf();
+    double klo = 0.0, khi = 0.0;
+    if constexpr (kFirst) {
+      const double k = kappa_est(a, g);
+      klo = k * (1.0 - kBandRel);
+      khi = k * (1.0 + kBandRel);
+      if (threadIdx.x == 0) s_nband = 0;
+    } else if (wave == 0) {
       // the node's normalisers and c_level = 1 + S_1 + ... + S_{level-1}: every array's entries
       // loaded in one round, then summed in wave_sum_fixed's order (lane l: entries l, l+64, ...;
       // then the butterfly)
@@ -100,69 +148,69 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
       }
     }
     __syncthreads();
-    const int64_t prow = g, qrow = a.rs.nP + g;
-    const T* pr = row_ptr<T>(a.rs, prow);
-    const T* qr = row_ptr<T>(a.rs, qrow);
-    const float lmp = a.rowstat[prow].lmax, lmq = a.rowstat[qrow].lmax;
-    const float thp = a.use_topp ? a.topp[prow].thr : -__builtin_huge_valf();
-    const float thq = a.use_topp ? a.topp[qrow].thr : -__builtin_huge_valf();
-    const double invEp = level > 0 ? s_inv[0] : 0.0, invEq = level > 0 ? s_inv[1] : 0.0;
-    const double ci = level > 0 ? s_c : 0.0;
-    const int x0 = chunk * a.chunk_elems_c + wave * kSub + lane * kPerLane;
-    float fp[kPerLane], fq[kPerLane];
-    load_run<T, kPerLane>(pr, x0, a.V, vec_ok, fp);
-    load_run<T, kPerLane>(qr, x0, a.V, vec_ok, fq);
-    double sp = 0.0, sq = 0.0;
+    const double invEp = kFirst ? 0.0 : s_inv[0], invEq = kFirst ? 0.0 : s_inv[1];
+    const double ci = kFirst ? 0.0 : s_c;
+    double sp = 0.0, sq = 0.0, pa = 0.0, qa = 0.0;
+    if constexpr (kFirst) {
 #pragma unroll
-    for (int e = 0; e < kPerLane; ++e) {
-      const double ep = term(fp[e], lmp, thp, a.inv_T, tbl);
-      const double eq = term(fq[e], lmq, thq, a.inv_T, tbl);
-      if (level == 0) {
+      for (int e = 0; e < kPerLane; ++e) {
+        const double ep = term(fp[e], lmp, thp, a.inv_T, tbl);
+        const double eq = term(fq[e], lmq, thq, a.inv_T, tbl);
         sp += ep;
         sq += eq;
-      } else {
+        if (ep > khi * eq) {
+          pa += ep;
+          qa += eq;
+        } else if (!(ep <= klo * eq)) {  // rare: an in-between token (or a NaN term)
+          const int k = atomicAdd(&s_nband, 1);
+          if (k < kBandSlots) a.band[item].x[k] = x0 + e;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e) {
+        const double ep = term(fp[e], lmp, thp, a.inv_T, tbl);
+        const double eq = term(fq[e], lmq, thq, a.inv_T, tbl);
         const double x = sub_products(ep, invEp, ci, eq * invEq);
         sp += x > 0.0 ? x : 0.0;
       }
     }
     sp = wave_sum(sp);
     sq = wave_sum(sq);
-    if (lane == 0) s_sum[wave] = make_double2(sp, sq);
+    if constexpr (kFirst) {
+      pa = wave_sum(pa);
+      qa = wave_sum(qa);
+    }
+    if (lane == 0) {
+      s_sum[wave][0] = sp;
+      s_sum[wave][1] = sq;
+      s_sum[wave][2] = pa;
+      s_sum[wave][3] = qa;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-      double tp = 0.0, tq = 0.0;
+      double tp = 0.0, tq = 0.0, ta = 0.0, tb = 0.0;
       for (int k = 0; k < kChainWaves; ++k) {
-        tp += s_sum[k].x;
-        tq += s_sum[k].y;
+        tp += s_sum[k][0];
+        tq += s_sum[k][1];
+        ta += s_sum[k][2];
+        tb += s_sum[k][3];
       }
-      if (level == 0)
-        a.e_part[g * a.nchunk_c + chunk] = make_double2(tp, tq);
-      else
+      if constexpr (kFirst) {
+        a.e_part[item] = make_double2(tp, tq);
+        a.band[item].pa = ta;
+        a.band[item].qa = tb;
+        a.band[item].n = s_nband;
+      } else {
         a.s_part[((int64_t)(level - 1) * a.rs.nP + g) * a.nchunk_c + chunk] = tp;
+      }
     }
     __syncthreads();  // the next item reuses the block's LDS
   };
 
-  if (level == 0) {
-    for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
-      const int64_t g = w / a.nchunk_c;
-      const int chunk = (int)(w - g * a.nchunk_c);
-      const int r = (int)(g / (a.N + 1));
-      const int v = (int)(g - (int64_t)r * (a.N + 1)) - 1;
-      if (threadIdx.x == 0) s_cnt = 0;
-      __syncthreads();
-      int cnt = 0;
-      for (int j = threadIdx.x; j < a.N; j += kThreads) cnt += a.parent[(int64_t)r * a.N + j] == v;
-      if (cnt) atomicAdd(&s_cnt, cnt);
-      __syncthreads();
-      const int m = s_cnt;
-      if (chunk == 0 && threadIdx.x == 0) a.nchild[g] = m;
-      __syncthreads();  // s_cnt is read by every thread before the next item resets it
-      if (m >= 2 && m <= kMaxSampledChildren) do_item(g, chunk);
-    }
-    return;
-  }
-  // items blockIdx.x + k gridDim.x, kThreads at a time: their children counts in one round
+  // items blockIdx.x + k gridDim.x, kThreads at a time: their children counts (and at level 1 the
+  // resolve's flags) in one round
+  const int mmin = level < 2 ? 2 : level + 1;
   const int64_t stride = gridDim.x;
   for (int64_t base = blockIdx.x; base < items; base += stride * kThreads) {
     if (threadIdx.x == 0) s_cnt = 0;
@@ -170,7 +218,8 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
     const int64_t w = base + (int64_t)threadIdx.x * stride;
     if (w < items) {
       const int m = a.nchild[w / a.nchunk_c];
-      if (m >= level + 1 && m <= kMaxSampledChildren) s_items[atomicAdd(&s_cnt, 1)] = threadIdx.x;
+      const int redo = level == 1 ? a.fb[w] : 1;  // read for every item; used where m >= 2 only
+      if (m >= mmin && m <= kMaxSampledChildren && redo) s_items[atomicAdd(&s_cnt, 1)] = threadIdx.x;
     }
     __syncthreads();
     const int nit = s_cnt;
@@ -180,6 +229,76 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
       do_item(g, (int)(w2 - g * a.nchunk_c));
     }
     __syncthreads();  // s_cnt and s_items are reset by the next round
+  }
+}
+
+// One wave per node row with two or more children: its exact normalisers (wave_sum_fixed's order),
+// then per chunk S_1's part from level 0's split: the sure terms' sums scaled, plus the kept
+// in-between tokens (their e_p and e_q recomputed as level 0 computes them) in index order.  A
+// chunk whose split cannot be used (ratio outside the checked band, or more in-between tokens than
+// were kept) is flagged for the full level-1 pass.
+template <typename T>
+__global__ __launch_bounds__(64) void k_tree_resolve(TreeQArgs a) {
+  __shared__ double tbl[kExpTable];
+  exp_table_fill(tbl);
+  const int64_t g = blockIdx.x;
+  const int m = a.nchild[g];
+  if (m < 2 || m > kMaxSampledChildren) return;
+  const int lane = threadIdx.x;
+  const int64_t prow = g, qrow = a.rs.nP + g;
+  const T* pr = row_ptr<T>(a.rs, prow);
+  const T* qr = row_ptr<T>(a.rs, qrow);
+  const float lmp = a.rowstat[prow].lmax, lmq = a.rowstat[qrow].lmax;
+  const float thp = a.use_topp ? a.topp[prow].thr : -__builtin_huge_valf();
+  const float thq = a.use_topp ? a.topp[qrow].thr : -__builtin_huge_valf();
+  const double* ep = e_part_of(a, g);
+  double se = 0.0, sq = 0.0;
+  for (int k = lane; k < a.nchunk_c; k += 64) {
+    se += ep[2 * (int64_t)k];
+    sq += ep[2 * (int64_t)k + 1];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    se += __shfl_xor(se, off, 64);
+    sq += __shfl_xor(sq, off, 64);
+  }
+  const double invEp = 1.0 / se, invEq = 1.0 / sq;
+  const double kt = kappa_est(a, g), kappa = se / sq;
+  const bool ok = kappa > kt * (1.0 - 0.25 * kBandRel) && kappa < kt * (1.0 + 0.25 * kBandRel);
+  double* s1 = a.s_part + g * a.nchunk_c;
+  for (int k = lane; k < a.nchunk_c; k += 64) {
+    const int64_t item = g * a.nchunk_c + k;
+    const BandPart& b = a.band[item];
+    const int n = b.n;
+    int redo = 1;
+    if (ok && n <= kBandSlots) {
+      double s = sub_products(b.pa, invEp, 1.0, b.qa * invEq);
+      s = s > 0.0 ? s : 0.0;
+      int xs[kBandSlots];
+#pragma unroll
+      for (int j = 0; j < kBandSlots; ++j) xs[j] = j < n ? b.x[j] : 0x7fffffff;
+      // index order (the atomic slots are taken in no fixed order): a sorting network
+#pragma unroll
+      for (int i = 0; i < kBandSlots; ++i)
+#pragma unroll
+        for (int j = (i & 1); j + 1 < kBandSlots; j += 2) {
+          const int lo = min(xs[j], xs[j + 1]), hi = max(xs[j], xs[j + 1]);
+          xs[j] = lo;
+          xs[j + 1] = hi;
+        }
+#pragma unroll
+      for (int j = 0; j < kBandSlots; ++j) {
+        if (j < n) {
+          const double ep = term(to_f32(pr[xs[j]]), lmp, thp, a.inv_T, tbl);
+          const double eq = term(to_f32(qr[xs[j]]), lmq, thq, a.inv_T, tbl);
+          const double x = sub_products(ep, invEp, 1.0, eq * invEq);
+          s += x > 0.0 ? x : 0.0;
+        }
+      }
+      s1[k] = s;
+      redo = 0;
+    }
+    a.fb[item] = redo;
   }
 }
 
@@ -402,6 +521,25 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
 
 }  // namespace
 
+hipError_t launch_tree_children(const TreeQArgs& a, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  timing_begin("tree_children", stream);
+  hipLaunchKernelGGL(k_tree_children, dim3((unsigned)a.batch), dim3(256), 0, stream, a);
+  timing_end("tree_children", stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_resolve(const TreeQArgs& a, psispec_dtype dtype, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  timing_begin("tree_resolve", stream);
+  if (dtype == PSISPEC_BF16)
+    hipLaunchKernelGGL(k_tree_resolve<bf16_t>, dim3((unsigned)a.rs.nP), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_tree_resolve<float>, dim3((unsigned)a.rs.nP), dim3(64), 0, stream, a);
+  timing_end("tree_resolve", stream);
+  return hipGetLastError();
+}
+
 hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype dtype,
                                   hipStream_t stream) {
   int64_t blocks = a.rs.nP * (int64_t)a.nchunk_c;
@@ -411,12 +549,9 @@ hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype d
   const int vec_ok = ((size_t)a.V * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
                      ((uintptr_t)a.rs.q % 16) == 0;
   timing_begin("tree_chain", stream);
-  if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL(k_tree_chain<bf16_t>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a,
-                       level, vec_ok);
-  else
-    hipLaunchKernelGGL(k_tree_chain<float>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a,
-                       level, vec_ok);
+  auto kern = dtype == PSISPEC_BF16 ? (level == 0 ? k_tree_chain<bf16_t, true> : k_tree_chain<bf16_t, false>)
+                                    : (level == 0 ? k_tree_chain<float, true> : k_tree_chain<float, false>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, level, vec_ok);
   timing_end("tree_chain", stream);
   return hipGetLastError();
 }

@@ -97,3 +97,41 @@ def test_full_size_sampled_tree():
     t = _compare(tin, steps=range(2), rows=[0, 3, 7])
     print(t)
     t.check()
+
+
+def _ratio_band_tokens(tin, picks):
+    """fp32 rows in which chosen tokens of a node's draft row have p'(x) / q'(x) equal to 1 up to
+    the logits' fp32 rounding (their q logit set from the exact normalisers, a few fixed-point
+    rounds): the tokens where the sign of p' - q' is closest to undecided.  picks: (request, node
+    row, token indices)."""
+    q = tin.q.detach().cpu().double().clone()
+    p = tin.p.detach().cpu().double()
+    for r, row, xs in picks:
+        lp, lq = p[r, row], q[r, row]
+        xs = torch.as_tensor(xs)
+        for _ in range(4):
+            Ep = torch.exp(lp - lp.max()).sum()
+            Eq = torch.exp(lq - lq.max()).sum()
+            lq[xs] = lp[xs] - lp.max() + lq.max() - torch.log(Ep / Eq)
+        q[r, row] = lq
+    return q.to(torch.float32).to(DEV)
+
+
+def test_ratio_band_tokens():
+    """Tokens whose ratio p'/q' sits at 1 within the logits' rounding: a few per chunk (the level-0
+    split keeps them and the resolve settles them in index order) and many in one chunk (that chunk
+    is recomputed in full, the others keep the split)."""
+    tin = workloads.make_tree_sampled("c4s", device=DEV, batch=3, V=40000, N=20)
+    p = tin.p.detach().cpu()
+    picks = []
+    for r in range(3):
+        low = torch.argsort(p[r, 0])[:400].sort().values  # low target logits: q stays below its max
+        few = [int(x) for x in low[::57][:6]]
+        chunk0 = [int(x) for x in low if x < 4096][:14]  # more than a chunk keeps
+        picks.append((r, 0, few + chunk0 if r == 1 else few))
+        low1 = torch.argsort(p[r, 1])[:50]
+        picks.append((r, 1, [int(x) for x in low1[:3]]))
+    q = _ratio_band_tokens(tin, picks)
+    t = _compare(tin, steps=range(3), q=q)
+    print(t)
+    t.check()
