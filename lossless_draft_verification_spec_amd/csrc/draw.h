@@ -134,7 +134,7 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
     uint32_t umask = 0;
     if (has_q) {
       load_run<T, kPerLane>(qrow, x0, a.V, vec_ok, fq);
-      // four tokens' fp64 chains at a time: 110 instead of 149 VGPRs, 4 waves per SIMD
+      // four tokens' fp64 chains at a time: fewer VGPRs than a full unroll, more waves per SIMD
 #pragma unroll 4
       for (int e = 0; e < kPerLane; ++e) {
         const double ep = term<kTopp>(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl);

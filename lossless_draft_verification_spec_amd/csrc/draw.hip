@@ -34,9 +34,11 @@
 namespace psispec {
 namespace {
 
-template <typename T, bool kTopp>
+// kList: the draws are a device-side list (the grid loops over its entries); a separate
+// instantiation, since the loop keeps registers live that the one-task-per-block form does not need
+template <typename T, bool kTopp, bool kList>
 __global__ __launch_bounds__(kThreads) void k_draw_pass(DrawArgs a, int vec_ok) {
-  if (!a.list) {
+  if constexpr (!kList) {
     const int r = blockIdx.x / a.nchunk_draw;
     draw_pass_task<T, kTopp>(a, r, blockIdx.x - r * a.nchunk_draw, vec_ok);
     return;
@@ -82,21 +84,12 @@ hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t strea
                      ((size_t)a.rs.pstride * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
                      ((uintptr_t)a.rs.q % 16) == 0;
   timing_begin("draw_pass", stream);
-  if (dtype == PSISPEC_BF16) {
-    if (a.use_topp)
-      hipLaunchKernelGGL((k_draw_pass<bf16_t, true>), dim3(grid), dim3(kThreads), 0, stream, a,
-                         vec_ok);
-    else
-      hipLaunchKernelGGL((k_draw_pass<bf16_t, false>), dim3(grid), dim3(kThreads), 0, stream, a,
-                         vec_ok);
-  } else {
-    if (a.use_topp)
-      hipLaunchKernelGGL((k_draw_pass<float, true>), dim3(grid), dim3(kThreads), 0, stream, a,
-                         vec_ok);
-    else
-      hipLaunchKernelGGL((k_draw_pass<float, false>), dim3(grid), dim3(kThreads), 0, stream, a,
-                         vec_ok);
-  }
+  const bool bf = dtype == PSISPEC_BF16, tp = a.use_topp, li = a.list != nullptr;
+  auto kern = bf ? (tp ? (li ? k_draw_pass<bf16_t, true, true> : k_draw_pass<bf16_t, true, false>)
+                       : (li ? k_draw_pass<bf16_t, false, true> : k_draw_pass<bf16_t, false, false>))
+                 : (tp ? (li ? k_draw_pass<float, true, true> : k_draw_pass<float, true, false>)
+                       : (li ? k_draw_pass<float, false, true> : k_draw_pass<float, false, false>));
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, a, vec_ok);
   timing_end("draw_pass", stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
