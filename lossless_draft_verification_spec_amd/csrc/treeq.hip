@@ -93,7 +93,6 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
   __shared__ double s_sum[kChainWaves][4];
   __shared__ double s_inv[2], s_c;
   __shared__ int s_items[kThreads];
-  exp_table_fill(tbl);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t items = a.rs.nP * (int64_t)a.nchunk_c;
 
@@ -208,6 +207,16 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
     __syncthreads();  // the next item reuses the block's LDS
   };
 
+  if constexpr (kFirst) {  // one item per block (no loop: 95 instead of 111 VGPRs, 5 waves/SIMD)
+    const int64_t w = blockIdx.x;
+    const int64_t g = w / a.nchunk_c;
+    const int m = a.nchild[g];
+    if (m < 2 || m > kMaxSampledChildren) return;
+    exp_table_fill(tbl);  // read after do_item's first barrier
+    do_item(g, (int)(w - g * a.nchunk_c));
+    return;
+  }
+  exp_table_fill(tbl);
   // items blockIdx.x + k gridDim.x, kThreads at a time: their children counts (and at level 1 the
   // resolve's flags) in one round
   const int mmin = level < 2 ? 2 : level + 1;
@@ -544,7 +553,7 @@ hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype d
                                   hipStream_t stream) {
   int64_t blocks = a.rs.nP * (int64_t)a.nchunk_c;
   if (blocks == 0) return hipSuccess;
-  if (blocks > 2048) blocks = 2048;  // a fixed grid loops over the work items
+  if (level > 0 && blocks > 2048) blocks = 2048;  // a fixed grid loops over the work items
   const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
   const int vec_ok = ((size_t)a.V * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
                      ((uintptr_t)a.rs.q % 16) == 0;
