@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
     do_item(g, (int)(w - g * a.nchunk_c));
     return;
   }
-  exp_table_fill(tbl);
+  bool filled = false;  // the exp table, filled once the block has an item (empty levels skip it)
   // items blockIdx.x + k gridDim.x, kThreads at a time: their children counts (and at level 1 the
   // resolve's flags) in one round
   const int mmin = level < 2 ? 2 : level + 1;
@@ -232,6 +232,10 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
     }
     __syncthreads();
     const int nit = s_cnt;
+    if (nit > 0 && !filled) {  // read after do_item's first barrier
+      exp_table_fill(tbl);
+      filled = true;
+    }
     for (int it = 0; it < nit; ++it) {
       const int64_t w2 = base + (int64_t)s_items[it] * stride;
       const int64_t g = w2 / a.nchunk_c;
