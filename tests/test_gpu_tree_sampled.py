@@ -36,12 +36,25 @@ def _compare(tin, T=1.0, top_p=1.0, steps=(0,), rows=None, seed=None, q=None):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("batch,N,V,branching", [
     (4, 10, 64, (3, 2, 1)), (3, 32, 5003, (4, 2, 2, 1, 1, 1, 1, 1)), (2, 1, 100, (1,)),
-    (5, 40, 999, (8, 2, 1, 1)), (2, 7, 4097, (1, 1, 1, 1, 1, 1, 1))])
+    (5, 40, 999, (8, 2, 1, 1)), (2, 7, 4097, (1, 1, 1, 1, 1, 1, 1)),
+    (2, 100, 3001, (8, 3, 2, 1, 1))])
 def test_sampled_tree_small(dtype, batch, N, V, branching):
     from dataclasses import replace
     pr = replace(workloads.PRESETS["c4s"], dtype=dtype, depth=8)
     tin = workloads.make_tree_sampled(pr, device=DEV, batch=batch, V=V, N=N, branching=branching)
     t = _compare(tin, steps=range(5))
+    print(t)
+    t.check()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_sampled_tree_max_nodes(dtype):
+    """1024 nodes, eight children for every node down to depth 4 (the largest tree and fan-out the
+    entry point takes)."""
+    from dataclasses import replace
+    pr = replace(workloads.PRESETS["c4s"], dtype=dtype, depth=8)
+    tin = workloads.make_tree_sampled(pr, device=DEV, batch=2, V=257, N=1024, branching=(8, 8, 8, 8))
+    t = _compare(tin, steps=range(3))
     print(t)
     t.check()
 
