@@ -224,10 +224,14 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
   for (int64_t base = blockIdx.x; base < items; base += stride * kThreads) {
     if (threadIdx.x == 0) s_cnt = 0;
     __syncthreads();
-    const int64_t w = base + (int64_t)threadIdx.x * stride;
-    if (w < items) {
-      const int m = a.nchild[w / a.nchunk_c];
-      const int redo = level == 1 ? a.fb[w] : 1;  // read for every item; used where m >= 2 only
+    // index j runs chunk-major (node row j mod nP, chunk j / nP), so that one node's chunks land
+    // in different blocks whatever the grid size
+    const int64_t j = base + (int64_t)threadIdx.x * stride;
+    if (j < items) {
+      const int64_t g = j % a.rs.nP;
+      const int m = a.nchild[g];
+      // the resolve's flag, read for every item; used where m >= 2 only
+      const int redo = level == 1 ? a.fb[g * a.nchunk_c + j / a.rs.nP] : 1;
       if (m >= mmin && m <= kMaxSampledChildren && redo) s_items[atomicAdd(&s_cnt, 1)] = threadIdx.x;
     }
     __syncthreads();
@@ -237,9 +241,8 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
       filled = true;
     }
     for (int it = 0; it < nit; ++it) {
-      const int64_t w2 = base + (int64_t)s_items[it] * stride;
-      const int64_t g = w2 / a.nchunk_c;
-      do_item(g, (int)(w2 - g * a.nchunk_c));
+      const int64_t j2 = base + (int64_t)s_items[it] * stride;
+      do_item(j2 % a.rs.nP, (int)(j2 / a.rs.nP));
     }
     __syncthreads();  // s_cnt and s_items are reset by the next round
   }
@@ -557,7 +560,10 @@ hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype d
                                   hipStream_t stream) {
   int64_t blocks = a.rs.nP * (int64_t)a.nchunk_c;
   if (blocks == 0) return hipSuccess;
-  if (level > 0 && blocks > 2048) blocks = 2048;  // a fixed grid loops over the work items
+  // a fixed grid loops over the work items; levels from 4 on (nodes with five or more children,
+  // rare) get a small one, which makes a launch without work cheaper
+  if (level > 0 && blocks > 2048) blocks = 2048;
+  if (level >= 4 && blocks > 509) blocks = 509;
   const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
   const int vec_ok = ((size_t)a.V * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
                      ((uintptr_t)a.rs.q % 16) == 0;
