@@ -560,10 +560,11 @@ hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype d
                                   hipStream_t stream) {
   int64_t blocks = a.rs.nP * (int64_t)a.nchunk_c;
   if (blocks == 0) return hipSuccess;
-  // a fixed grid loops over the work items; levels from 4 on (nodes with five or more children,
-  // rare) get a small one, which makes a launch without work cheaper
+  // a fixed grid loops over the work items: 2048 blocks at level 1 (every chunk of every node with
+  // two or more children when the level-0 split is refused), 509 from level 2 on (nodes with three
+  // or more children: fewer items, and a launch without work is cheaper)
   if (level > 0 && blocks > 2048) blocks = 2048;
-  if (level >= 4 && blocks > 509) blocks = 509;
+  if (level >= 2 && blocks > 509) blocks = 509;
   const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
   const int vec_ok = ((size_t)a.V * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
                      ((uintptr_t)a.rs.q % 16) == 0;
