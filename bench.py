@@ -429,8 +429,7 @@ def run_lmhead(steps, warmup, torch, pkg, workloads):
     torch.cuda.synchronize()
     log(f"c5: generated inputs in {time.time() - t0:.1f}s")
     b, B, H, V, r = preset.batch, preset.B, preset.H, preset.V, preset.r
-    ws = torch.empty(pkg.lmhead_workspace_bytes(b, B, H, V, r, True), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(pkg.lmhead_workspace_bytes(b, B, H, V, r), dtype=torch.uint8, device="cuda")
     out = dict(accept_len=torch.empty(b, dtype=torch.int32, device="cuda"),
                out_tokens=torch.empty(b, B + 1, dtype=torch.int32, device="cuda"),
                ratios=torch.empty(b, B, dtype=torch.float32, device="cuda"),
@@ -439,8 +438,8 @@ def run_lmhead(steps, warmup, torch, pkg, workloads):
     acc = torch.zeros(b, dtype=torch.int64, device="cuda")
 
     def step(s):
-        pkg.psispec_lmhead_verify(inp.h_ar, inp.h_draft, inp.w_t, inp.drafts[s % len(inp.drafts)],
-                                  inp.a_t, inp.b_t, preset.lora_scale, temperature=preset.T,
+        pkg.psispec_lmhead_verify(inp.h_ar, inp.h_draft, inp.W, inp.drafts[s % len(inp.drafts)],
+                                  inp.A, inp.Bl, preset.lora_scale, temperature=preset.T,
                                   seed=inp.seed, step=s, workspace=ws, out=out)
 
     for s in range(warmup):

@@ -219,32 +219,38 @@ psispec_status psispec_kv_commit(void* kv, int64_t line_stride, int64_t row_byte
  * AR path scores the block).  Computes, on the bf16 matrix cores with fp32 accumulation,
  *   p logits (AR rows)    = h_ar . W
  *   q logits (draft rows) = h_draft . W + lora_scale (h_draft . A) . B
- * and runs psispec_verify_linear on them (same sampling, outputs, statuses and Philox keys).
+ * and runs the linear verify on them (same sampling, outputs, statuses and Philox keys as
+ * psispec_verify_linear on those fp32 logits).  The logits are not written to memory: the matrix
+ * product's epilogue hands the verify each row's softmax statistics and the logit at each draft
+ * token, and the one or two rows that the final draw reads (p_k and q_k at the first rejection k,
+ * or the block-end row p_B) are recomputed, bit-identical, into the workspace.
  *
  *   h_ar      bf16 [batch][B+1][H]  final hidden states of the AR rows (row B = block end)
  *   h_draft   bf16 [batch][B][H]    final hidden states of the draft rows
- *   w_t       bf16 [V][H]           W[H][V] stored one vocabulary row at a time
- *   lora_a_t  bf16 [r][H]           A[H][r] stored one rank row at a time; NULL when r = 0
- *   lora_b_t  bf16 [V][r]           B[r][V] stored one vocabulary row at a time; NULL when r = 0
- *   H         multiple of 64, at most 2^20;  0 <= r <= 64;  B 1..64
- *   logits    fp32 [batch*(2B+1)][V] or NULL: where the logits are written (rows 0..batch(B+1)-1
- *             the AR rows request-major, then the draft rows); NULL keeps them in the workspace
- *             (size from psispec_lmhead_verify_workspace with logits_in_workspace = 1)
- * h_ar, h_draft, w_t, lora_a_t and logits must be 16-byte aligned (PSISPEC_EINVAL otherwise).  All
- * inputs are read-only and caller-owned; the call is asynchronous on `stream`.
+ *   W         bf16 [H][V]           the LM-head weight (V contiguous)
+ *   lora_A    bf16 [H][r]           the LoRA down-projection; NULL when r = 0
+ *   lora_B    bf16 [r][V]           the LoRA up-projection (V contiguous); NULL when r = 0
+ *   H         multiple of 64, at most 2^20;  V multiple of 8;  0 <= r <= 64;  B 1..64
+ *   p_logits_dbg, q_logits_dbg
+ *             fp32 [batch][B+1][V] and [batch][B][V], or both NULL (the logits are never
+ *             materialised).  When given, the logits are also stored there and the final draw
+ *             reads them instead of recomputing its rows.  With top_p < 1 both are required (the
+ *             nucleus needs every row's values a second time): PSISPEC_EUNSUPPORTED otherwise.
+ * h_ar, h_draft, W, lora_B and the logit buffers must be 16-byte aligned (PSISPEC_EINVAL
+ * otherwise).  All inputs are read-only and caller-owned; the call is asynchronous on `stream`.
  * The product h_draft . A is formed in fp64 and enters the matrix product as a bf16 pair
  * (hi + lo, relative error 2^-17).
  */
-size_t psispec_lmhead_verify_workspace(int32_t batch, int32_t B, int32_t H, int32_t V, int32_t r,
-                                       int32_t logits_in_workspace);
+size_t psispec_lmhead_verify_workspace(int32_t batch, int32_t B, int32_t H, int32_t V, int32_t r);
 
-psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, const void* w_t,
-                                     const void* lora_a_t, const void* lora_b_t, float lora_scale,
+psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, const void* W,
+                                     const void* lora_A, const void* lora_B, float lora_scale,
                                      int32_t batch, int32_t B, int32_t H, int32_t V, int32_t r,
                                      const int32_t* draft_tokens, const psispec_sampling* s,
                                      int32_t* accept_len, int32_t* out_tokens, float* ratios,
-                                     uint64_t* accept_mask, int32_t* status, float* logits,
-                                     void* workspace, size_t workspace_bytes, void* stream);
+                                     uint64_t* accept_mask, int32_t* status, float* p_logits_dbg,
+                                     float* q_logits_dbg, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /* Message for a return code (static string). */
 const char* psispec_strerror(psispec_status code);

@@ -59,10 +59,10 @@ def lib():
         L.psispec_verify_tree.argtypes = [P, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P,
                                           sz, P]
         L.psispec_verify_tree.restype = i32
-        L.psispec_lmhead_verify_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.psispec_lmhead_verify_workspace.argtypes = [i32, i32, i32, i32, i32]
         L.psispec_lmhead_verify_workspace.restype = sz
         L.psispec_lmhead_verify.argtypes = ([P, P, P, P, P, ctypes.c_float, i32, i32, i32, i32, i32,
-                                             P, P, P, P, P, P, P, P, P, sz, P])
+                                             P, P, P, P, P, P, P, P, P, P, sz, P])
         L.psispec_lmhead_verify.restype = i32
         L.psispec_sample_drafts_workspace.argtypes = [i32, i32, i32, i32]
         L.psispec_sample_drafts_workspace.restype = sz
@@ -101,6 +101,48 @@ def _dev(t: torch.Tensor, name: str) -> int:
     if not t.is_contiguous():
         raise PsispecError(f"{name} must be contiguous")
     return t.data_ptr()
+
+
+def _same_dev(t: torch.Tensor, dev, name: str):
+    if t.device != dev:
+        raise PsispecError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _out_check(t: torch.Tensor | None, shape, dtype, dev, name: str, exact: bool = True):
+    """A caller-supplied output: a contiguous GPU tensor on `dev` of `dtype` holding `shape`
+    (exactly, or at least that many elements): the library writes through its raw pointer."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
+        raise PsispecError(f"{name} must be a GPU tensor on {dev}")
+    if not t.is_contiguous():
+        raise PsispecError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise PsispecError(f"{name} must be {dtype}, got {t.dtype}")
+    need = 1
+    for n in shape:
+        need *= int(n)
+    if (exact and tuple(t.shape) != tuple(shape)) or t.numel() < need:
+        raise PsispecError(f"{name} must hold {tuple(shape)} elements, got {tuple(t.shape)}")
+
+
+def _check_out(out: dict, spec: dict, dev):
+    """spec: name -> (shape, dtype, required)."""
+    for name, (shape, dtype, required) in spec.items():
+        t = out.get(name)
+        if t is None:
+            if required:
+                raise PsispecError(f"out[{name!r}] is required")
+            continue
+        _out_check(t, shape, dtype, dev, f"out[{name!r}]", exact=False)
+
+
+def _check_linear_out(out: dict, batch: int, B: int, dev):
+    _check_out(out, {"accept_len": ((batch,), torch.int32, True),
+                     "out_tokens": ((batch, B + 1), torch.int32, True),
+                     "ratios": ((batch, B), torch.float32, False),
+                     "accept_mask": ((batch,), torch.int64, False),
+                     "status": ((batch,), torch.int32, False)}, dev)
 
 
 def _ptr(t):
@@ -153,6 +195,8 @@ def psispec_verify_linear(p_logits: torch.Tensor, q_logits: torch.Tensor, draft_
                    ratios=torch.empty(batch, B, dtype=torch.float32, device=dev),
                    accept_mask=torch.empty(batch, dtype=torch.int64, device=dev),
                    status=torch.empty(batch, dtype=torch.int32, device=dev))
+    else:
+        _check_linear_out(out, batch, B, dev)
     need = linear_workspace_bytes(batch, B, V, dt)
     if need == 0:
         raise PsispecError("unsupported sizes (B must be 1..64)")
@@ -183,23 +227,31 @@ def psispec_verify_tree(p_logits: torch.Tensor, parent: torch.Tensor, node_token
         raise PsispecError("p_logits must be [batch][N+1][V]")
     batch, Np1, V = p_logits.shape
     N = Np1 - 1
+    dt = _dtype_code(p_logits)
+    dev = p_logits.device
+    _dev(p_logits, "p_logits")
     for name, t in (("parent", parent), ("node_tokens", node_tokens)):
         if tuple(t.shape) != (batch, N) or t.dtype != torch.int32:
             raise PsispecError(f"{name} must be int32 [batch][N]")
         _dev(t, name)
-    dt = _dtype_code(p_logits)
-    dev = p_logits.device
-    _dev(p_logits, "p_logits")
+        _same_dev(t, dev, name)
     if q_logits is not None:
         if tuple(q_logits.shape) != tuple(p_logits.shape) or q_logits.dtype != p_logits.dtype:
             raise PsispecError("q_logits must be [batch][N+1][V] with the dtype of p_logits")
         _dev(q_logits, "q_logits")
+        _same_dev(q_logits, dev, "q_logits")
     if out is None:
         out = dict(accept_len=torch.empty(batch, dtype=torch.int32, device=dev),
                    accept_nodes=torch.empty(batch, max_depth, dtype=torch.int32, device=dev),
                    out_tokens=torch.empty(batch, max_depth + 1, dtype=torch.int32, device=dev),
                    node_ratios=torch.empty(batch, N, dtype=torch.float32, device=dev),
                    status=torch.empty(batch, dtype=torch.int32, device=dev))
+    else:
+        _check_out(out, {"accept_len": ((batch,), torch.int32, True),
+                         "accept_nodes": ((batch, max_depth), torch.int32, True),
+                         "out_tokens": ((batch, max_depth + 1), torch.int32, True),
+                         "node_ratios": ((batch, N), torch.float32, False),
+                         "status": ((batch,), torch.int32, False)}, dev)
     need = tree_workspace_bytes(batch, N, V, dt)
     if need == 0:
         raise PsispecError("unsupported sizes (N must be 1..1024)")
@@ -215,66 +267,80 @@ def psispec_verify_tree(p_logits: torch.Tensor, parent: torch.Tensor, node_token
     return out
 
 
-def lmhead_workspace_bytes(batch, B, H, V, r, logits_in_workspace=True) -> int:
-    return int(lib().psispec_lmhead_verify_workspace(batch, B, H, V, r, 1 if logits_in_workspace else 0))
+def lmhead_workspace_bytes(batch, B, H, V, r) -> int:
+    return int(lib().psispec_lmhead_verify_workspace(batch, B, H, V, r))
 
 
-def psispec_lmhead_verify(h_ar: torch.Tensor, h_draft: torch.Tensor, w_t: torch.Tensor,
-                          draft_tokens: torch.Tensor, lora_a_t: torch.Tensor | None = None,
-                          lora_b_t: torch.Tensor | None = None, lora_scale: float = 1.0,
-                          temperature: float = 1.0, top_p: float = 1.0, seed: int = 0, step: int = 0,
-                          request_base: int = 0, flags: int = 0, logits: torch.Tensor | None = None,
+def psispec_lmhead_verify(h_ar: torch.Tensor, h_draft: torch.Tensor, W: torch.Tensor,
+                          draft_tokens: torch.Tensor, lora_A: torch.Tensor | None = None,
+                          lora_B: torch.Tensor | None = None, lora_scale: float = 1.0,
+                          temperature: float = 1.0, top_p: float = 1.0, seed: int = 0,
+                          step: int = 0, request_base: int = 0, flags: int = 0,
+                          p_logits_dbg: torch.Tensor | None = None,
+                          q_logits_dbg: torch.Tensor | None = None,
                           workspace: torch.Tensor | None = None, out: dict | None = None,
                           stream=None) -> dict:
-    """LM head + linear verify.  h_ar [batch][B+1][H], h_draft [batch][B][H], w_t [V][H] (the
-    weight stored one vocabulary row at a time), lora_a_t [r][H], lora_b_t [V][r], all bf16 on one
-    GPU; draft_tokens int32 [batch][B].  `logits`, if given, is an fp32 [batch*(2B+1)][V] tensor
-    that receives the logits (AR rows first).  Returns the outputs of psispec_verify_linear."""
-    if h_ar.dim() != 3 or h_draft.dim() != 3 or w_t.dim() != 2:
-        raise PsispecError("h_ar [batch][B+1][H], h_draft [batch][B][H], w_t [V][H]")
+    """LM head + linear verify.  h_ar bf16 [batch][B+1][H], h_draft bf16 [batch][B][H], W bf16
+    [H][V], LoRA lora_A bf16 [H][r] and lora_B bf16 [r][V] (or None), draft_tokens int32
+    [batch][B].  The logits are never materialised unless p_logits_dbg [batch][B+1][V] and
+    q_logits_dbg [batch][B][V] (fp32) are given (required with top_p < 1).  Returns the outputs of
+    psispec_verify_linear."""
+    if h_ar.dim() != 3 or h_draft.dim() != 3 or W.dim() != 2:
+        raise PsispecError("h_ar must be [batch][B+1][H], h_draft [batch][B][H] and W [H][V]")
     batch, Bp1, H = h_ar.shape
     B = Bp1 - 1
-    V = w_t.shape[0]
-    if tuple(h_draft.shape) != (batch, B, H) or w_t.shape[1] != H:
-        raise PsispecError("h_draft must be [batch][B][H] and w_t [V][H]")
-    for name, t in (("h_ar", h_ar), ("h_draft", h_draft), ("w_t", w_t)):
+    V = W.shape[1]
+    if tuple(h_draft.shape) != (batch, B, H) or W.shape[0] != H:
+        raise PsispecError("h_draft must be [batch][B][H] and W [H][V]")
+    dev = h_ar.device
+    for name, t in (("h_ar", h_ar), ("h_draft", h_draft), ("W", W)):
         if t.dtype != torch.bfloat16:
             raise PsispecError(f"{name} must be bfloat16")
         _dev(t, name)
+        _same_dev(t, dev, name)
     r = 0
-    if lora_a_t is not None and lora_a_t.numel():
-        r = lora_a_t.shape[0]
-        if tuple(lora_a_t.shape) != (r, H) or lora_b_t is None or tuple(lora_b_t.shape) != (V, r):
-            raise PsispecError("lora_a_t must be [r][H] and lora_b_t [V][r]")
-        _dev(lora_a_t, "lora_a_t")
-        _dev(lora_b_t, "lora_b_t")
+    if lora_A is not None and lora_A.numel():
+        r = lora_A.shape[1]
+        if (lora_A.dim() != 2 or lora_A.shape[0] != H or lora_B is None
+                or tuple(lora_B.shape) != (r, V)):
+            raise PsispecError("lora_A must be [H][r] and lora_B [r][V]")
+        for name, t in (("lora_A", lora_A), ("lora_B", lora_B)):
+            if t.dtype != torch.bfloat16:
+                raise PsispecError(f"{name} must be bfloat16")
+            _dev(t, name)
+            _same_dev(t, dev, name)
     else:
-        lora_a_t = lora_b_t = None
+        lora_A = lora_B = None
     if tuple(draft_tokens.shape) != (batch, B) or draft_tokens.dtype != torch.int32:
         raise PsispecError("draft_tokens must be int32 [batch][B]")
     _dev(draft_tokens, "draft_tokens")
-    dev = h_ar.device
-    if logits is not None:
-        if tuple(logits.shape) != (batch * (2 * B + 1), V) or logits.dtype != torch.float32:
-            raise PsispecError("logits must be float32 [batch*(2B+1)][V]")
-        _dev(logits, "logits")
+    _same_dev(draft_tokens, dev, "draft_tokens")
+    if (p_logits_dbg is None) != (q_logits_dbg is None):
+        raise PsispecError("p_logits_dbg and q_logits_dbg go together")
+    if p_logits_dbg is not None:
+        _out_check(p_logits_dbg, (batch, B + 1, V), torch.float32, dev, "p_logits_dbg")
+        _out_check(q_logits_dbg, (batch, B, V), torch.float32, dev, "q_logits_dbg")
     if out is None:
         out = dict(accept_len=torch.empty(batch, dtype=torch.int32, device=dev),
                    out_tokens=torch.empty(batch, B + 1, dtype=torch.int32, device=dev),
                    ratios=torch.empty(batch, B, dtype=torch.float32, device=dev),
                    accept_mask=torch.empty(batch, dtype=torch.int64, device=dev),
                    status=torch.empty(batch, dtype=torch.int32, device=dev))
-    need = lmhead_workspace_bytes(batch, B, H, V, r, logits is None)
+    else:
+        _check_linear_out(out, batch, B, dev)
+    need = lmhead_workspace_bytes(batch, B, H, V, r)
     if need == 0:
-        raise PsispecError("unsupported sizes (H a multiple of 64, r <= 64, B 1..64)")
+        raise PsispecError("unsupported sizes (H a multiple of 64, V a multiple of 8, r <= 64, "
+                           "B 1..64)")
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     s = _sampling(temperature, top_p, seed, step, request_base, flags)
     rc = lib().psispec_lmhead_verify(
-        _ptr(h_ar), _ptr(h_draft), _ptr(w_t), _ptr(lora_a_t), _ptr(lora_b_t), float(lora_scale),
+        _ptr(h_ar), _ptr(h_draft), _ptr(W), _ptr(lora_A), _ptr(lora_B), float(lora_scale),
         batch, B, H, V, r, _ptr(draft_tokens), ctypes.byref(s), _ptr(out["accept_len"]),
         _ptr(out["out_tokens"]), _ptr(out.get("ratios")), _ptr(out.get("accept_mask")),
-        _ptr(out.get("status")), _ptr(logits), _ptr(workspace), workspace.numel(), _stream(stream))
+        _ptr(out.get("status")), _ptr(p_logits_dbg), _ptr(q_logits_dbg), _ptr(workspace),
+        workspace.numel(), _stream(stream))
     _check(rc, "psispec_lmhead_verify")
     return out
 
@@ -327,6 +393,9 @@ def psispec_sample_drafts(q_logits: torch.Tensor | None, ar_logits: torch.Tensor
     if out is None:
         out = dict(draft_tokens=torch.empty(batch, B, dtype=torch.int32, device=dev),
                    status=torch.empty(batch, B, dtype=torch.int32, device=dev))
+    else:
+        _check_out(out, {"draft_tokens": ((batch, B), torch.int32, True),
+                         "status": ((batch, B), torch.int32, False)}, dev)
     need = drafts_workspace_bytes(batch, B, V, dt)
     if need == 0:
         raise PsispecError("unsupported sizes (B must be 1..64)")
@@ -360,14 +429,15 @@ def psispec_kv_commit(kv: torch.Tensor, blk: int, n_keep: torch.Tensor, length: 
         if tuple(t.shape) != (batch,) or t.dtype != torch.int32:
             raise PsispecError(f"{name} must be int32 [batch]")
         _dev(t, name)
+        _same_dev(t, kv.device, name)
     ks = 0
     if keep is not None:
         if keep.dim() != 2 or keep.shape[0] != batch or keep.dtype != torch.int32:
             raise PsispecError("keep must be int32 [batch][k]")
         _dev(keep, "keep")
+        _same_dev(keep, kv.device, "keep")
         ks = keep.shape[1]
-    if status is not None:
-        _dev(status, "status")
+    _out_check(status, (batch,), torch.int32, kv.device, "status", exact=False)
     rc = lib().psispec_kv_commit(_ptr(kv), kv.stride(0) * es, row_bytes, Lmax, int(blk), _ptr(keep),
                                  ks, _ptr(n_keep), _ptr(length), _ptr(status), batch,
                                  _stream(stream))

@@ -743,99 +743,112 @@ psispec_status psispec_kv_commit(void* kv, int64_t line_stride, int64_t row_byte
 // ---------------------------------------------------------------------------------------------
 namespace {
 
+// Workspace of the LM-head verify: the linear verify's plan over the M = batch (2B+1) rows (one
+// row pair per column tile), the logit at each row's draft token, the staged A operand (reused
+// by the stopping-row pass once the main pass is done), and for the final draw the recomputed
+// stopping rows with their descriptors and statistics.
 struct LMPlan {
   Plan pl;
-  size_t off_logits, off_aaug, off_baug, total;
-  int ntiles, mtiles, kx;
+  size_t off_gath, off_ablk, off_desc2, off_rowstat2, off_rows, total;
+  int ntiles;
 };
 
-LMPlan make_lm_plan(int batch, int B, int H, int V, int r, bool own_logits) {
+LMPlan make_lm_plan(int batch, int B, int H, int V, int r) {
   LMPlan lp{};
   const int nP = batch * (B + 1), nQ = batch * B, M = nP + nQ;
   lp.ntiles = (V + lmhead_tile_n() - 1) / lmhead_tile_n();
-  lp.mtiles = (M + lmhead_tile_m() - 1) / lmhead_tile_m();
   lp.pl = make_plan((int64_t)M, batch, V, 4, 0, lp.ntiles);
   size_t off = lp.pl.total;
-  lp.off_logits = off;
-  if (own_logits) off = align_up(off + sizeof(float) * (size_t)M * (size_t)V);
-  lp.kx = r > 0 ? (2 * r + 63) / 64 * 64 : 0;
-  lp.off_aaug = off;
-  off = align_up(off + sizeof(uint16_t) * (size_t)M * (size_t)(H + lp.kx));
-  lp.off_baug = off;
-  off = align_up(off + sizeof(uint16_t) * (size_t)V * (size_t)lp.kx);
+  lp.off_gath = off;
+  off = align_up(off + sizeof(float) * (size_t)M);
+  lp.off_ablk = off;
+  const size_t a_main = lmhead_ablk_bytes(M, H, r), a_rows = lmhead_ablk_bytes(2 * batch, H, r);
+  off = align_up(off + (a_main > a_rows ? a_main : a_rows));
+  lp.off_desc2 = off;
+  off = align_up(off + sizeof(DrawDesc) * (size_t)batch);
+  lp.off_rowstat2 = off;
+  off = align_up(off + sizeof(RowStat) * (size_t)(2 * batch));
+  lp.off_rows = off;
+  off = align_up(off + sizeof(float) * (size_t)(2 * batch) * (size_t)V);
   lp.total = off + kAlign;
   return lp;
+}
+
+bool lm_shape_ok(int32_t batch, int32_t B, int32_t H, int32_t V, int32_t r) {
+  if (batch < 0 || B < 1 || B > 64 || V < 8 || V % 8 || H < 64 || H % 64 || H > (1 << 20) ||
+      r < 0 || r > 64)
+    return false;
+  // 32-bit offsets: rows of the staged operand, a K step of W, the per-call row count
+  const int64_t M = (int64_t)batch * (2 * B + 1);
+  if (M > (1 << 24) || (int64_t)V * 64 > INT32_MAX || M * (H + 128) * 2 > INT32_MAX) return false;
+  return true;
 }
 
 }  // namespace
 
 extern "C" {
 
-size_t psispec_lmhead_verify_workspace(int32_t batch, int32_t B, int32_t H, int32_t V, int32_t r,
-                                       int32_t logits_in_workspace) {
-  if (batch < 0 || B < 1 || B > 64 || V < 1 || H < 64 || H % 64 || H > (1 << 20) || r < 0 || r > 64)
-    return 0;
-  return make_lm_plan(batch, B, H, V, r, logits_in_workspace != 0).total;
+size_t psispec_lmhead_verify_workspace(int32_t batch, int32_t B, int32_t H, int32_t V, int32_t r) {
+  if (!lm_shape_ok(batch, B, H, V, r)) return 0;
+  return make_lm_plan(batch, B, H, V, r).total;
 }
 
-psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, const void* w_t,
-                                     const void* lora_a_t, const void* lora_b_t, float lora_scale,
+psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, const void* W,
+                                     const void* lora_A, const void* lora_B, float lora_scale,
                                      int32_t batch, int32_t B, int32_t H, int32_t V, int32_t r,
                                      const int32_t* draft_tokens, const psispec_sampling* s,
                                      int32_t* accept_len, int32_t* out_tokens, float* ratios,
-                                     uint64_t* accept_mask, int32_t* status, float* logits,
-                                     void* workspace, size_t workspace_bytes, void* stream_ptr) {
-  if (batch < 0 || B < 1 || B > 64 || V < 1 || H < 64 || H % 64 || H > (1 << 20) || r < 0 || r > 64)
-    return PSISPEC_EINVAL;
+                                     uint64_t* accept_mask, int32_t* status, float* p_logits_dbg,
+                                     float* q_logits_dbg, void* workspace, size_t workspace_bytes,
+                                     void* stream_ptr) {
+  if (!lm_shape_ok(batch, B, H, V, r)) return PSISPEC_EINVAL;
   if (!sampling_ok(s) || !isfinite(lora_scale)) return PSISPEC_EINVAL;
   if (batch == 0) return PSISPEC_OK;
-  if (!h_ar || !h_draft || !w_t || !draft_tokens || !accept_len || !out_tokens) return PSISPEC_EINVAL;
-  if (r > 0 && (!lora_a_t || !lora_b_t)) return PSISPEC_EINVAL;
-  if (((uintptr_t)h_ar | (uintptr_t)h_draft | (uintptr_t)w_t | (uintptr_t)lora_a_t |
-       (uintptr_t)logits) % 16)
+  if (!h_ar || !h_draft || !W || !draft_tokens || !accept_len || !out_tokens) return PSISPEC_EINVAL;
+  if (r > 0 && (!lora_A || !lora_B)) return PSISPEC_EINVAL;
+  if ((p_logits_dbg == nullptr) != (q_logits_dbg == nullptr)) return PSISPEC_EINVAL;
+  if (((uintptr_t)h_ar | (uintptr_t)h_draft | (uintptr_t)W | (uintptr_t)lora_B |
+       (uintptr_t)p_logits_dbg | (uintptr_t)q_logits_dbg) % 16)
     return PSISPEC_EINVAL;
-  const LMPlan lp = make_lm_plan(batch, B, H, V, r, logits == nullptr);
+  const bool use_topp = s->top_p < 1.0;
+  const bool materialise = p_logits_dbg != nullptr;
+  if (use_topp && !materialise) return PSISPEC_EUNSUPPORTED;
+  const LMPlan lp = make_lm_plan(batch, B, H, V, r);
   if (!workspace || workspace_bytes < lp.total || ((uintptr_t)workspace % kAlign) != 0)
     return PSISPEC_EWORKSPACE;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const double T = s->temperature;
   const float c = (float)(1.4426950408889634074 / T);
-  const bool use_topp = s->top_p < 1.0;
-  const int nP = batch * (B + 1), nQ = batch * B, M = nP + nQ;
-  float* L = logits ? logits : carve<float>(workspace, lp.off_logits);
+  const int nP = batch * (B + 1), nQ = batch * B;
   const Plan& pl = lp.pl;
   float2* part = carve<float2>(workspace, pl.off_part);
+  float* gath = carve<float>(workspace, lp.off_gath);
+  uint16_t* ablk = carve<uint16_t>(workspace, lp.off_ablk);
 
   LMHeadArgs ha{};
   ha.h_ar = static_cast<const uint16_t*>(h_ar);
   ha.h_dr = static_cast<const uint16_t*>(h_draft);
-  ha.w_t = static_cast<const uint16_t*>(w_t);
-  ha.lora_at = static_cast<const uint16_t*>(lora_a_t);
-  ha.lora_bt = static_cast<const uint16_t*>(lora_b_t);
-  ha.aaug = carve<uint16_t>(workspace, lp.off_aaug);
-  ha.baug = carve<uint16_t>(workspace, lp.off_baug);
-  ha.kx = lp.kx;
+  ha.w = static_cast<const uint16_t*>(W);
+  ha.lora_a = static_cast<const uint16_t*>(lora_A);
+  ha.lora_b = static_cast<const uint16_t*>(lora_B);
   ha.lora_scale = lora_scale;
   ha.nP = nP;
   ha.nQ = nQ;
-  ha.M = M;
   ha.N = V;
   ha.K = H;
   ha.r = r;
-  ha.mtiles = lp.mtiles;
-  ha.ntiles = lp.ntiles;
   ha.c = c;
-  ha.logits = L;
-  ha.part = part;
-  if (launch_lmhead(ha, stream) != hipSuccess) return PSISPEC_EHIP;
+  if (launch_lmhead_main(ha, ablk, draft_tokens, B, part, gath, p_logits_dbg, q_logits_dbg,
+                         stream) != hipSuccess)
+    return PSISPEC_EHIP;
 
-  // the verify itself, on the fp32 logits, with the epilogue's row pairs (one per column tile)
-  RowSet rs{L, L + (int64_t)nP * V, nP, nQ, V, B, (s->flags & PSISPEC_FIRST_FROM_TARGET) ? 1 : 0,
-            V};
+  // the accept test on the epilogue's row pairs (one per column tile) and gathered logits; the rows
+  // themselves are read only when the caller materialised them (the nucleus, the final draw)
+  RowSet rs{p_logits_dbg, q_logits_dbg, nP, nQ, V, B,
+            (s->flags & PSISPEC_FIRST_FROM_TARGET) ? 1 : 0, V};
   RowStat* rowstat = carve<RowStat>(workspace, pl.off_rowstat);
   ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
   DrawDesc* desc = carve<DrawDesc>(workspace, pl.off_desc);
-  // one pair per column tile: combine every row's pairs once, one wave per row
   if (launch_combine_rows(rs, part, pl.nchunk, c, rowstat, stream) != hipSuccess)
     return PSISPEC_EHIP;
   if (use_topp && launch_topp(rs, PSISPEC_F32, pl.nchunk, c, s->top_p, part, topp, stream,
@@ -859,6 +872,7 @@ psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, cons
   la.topp = topp;
   la.rowstat = rowstat;
   la.rowstat_ready = 1;
+  la.gath = gath;
   la.desc = desc;
   la.ucount = carve<int32_t>(workspace, pl.off_ucount);
   la.accept_len = accept_len;
@@ -866,6 +880,7 @@ psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, cons
   la.ratios = ratios;
   la.accept_mask = accept_mask;
   if (launch_decide_linear(la, PSISPEC_F32, stream) != hipSuccess) return PSISPEC_EHIP;
+
   DrawArgs da{};
   da.rs = rs;
   da.batch = batch;
@@ -881,6 +896,18 @@ psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, cons
   da.rowstat = rowstat;
   da.topp = topp;
   da.desc = desc;
+  if (!materialise) {
+    // recompute the stopping rows: p_k and q_k of request r become rows 2r and 2r + 1
+    float* rows = carve<float>(workspace, lp.off_rows);
+    DrawDesc* desc2 = carve<DrawDesc>(workspace, lp.off_desc2);
+    RowStat* rowstat2 = carve<RowStat>(workspace, lp.off_rowstat2);
+    if (launch_lmhead_rows(ha, ablk, batch, desc, rowstat, desc2, rowstat2, rows, stream) !=
+        hipSuccess)
+      return PSISPEC_EHIP;
+    da.rs = RowSet{rows, rows, 2 * (int64_t)batch, 0, V, 1, 0, V};
+    da.rowstat = rowstat2;
+    da.desc = desc2;
+  }
   da.excl = nullptr;
   da.excl_stride = 0;
   da.esum = carve<double2>(workspace, pl.off_esum);

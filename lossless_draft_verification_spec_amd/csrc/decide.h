@@ -136,10 +136,14 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
     } else if (bad_tok) {
       ratio = 0.0;
     } else {
-      const T* prow = row_ptr<T>(a.rs, prow0 + t);
-      const T* qrow = row_ptr<T>(a.rs, qrow0 + t);
-      const float lp = to_f32(prow[d]);
-      const float lq = to_f32(qrow[d]);
+      float lp, lq;
+      if (a.gath) {
+        lp = a.gath[prow0 + t];
+        lq = a.gath[qrow0 + t];
+      } else {
+        lp = to_f32(row_ptr<T>(a.rs, prow0 + t)[d]);
+        lq = to_f32(row_ptr<T>(a.rs, qrow0 + t)[d]);
+      }
       double pa = exp(((double)lp - (double)s_lmax[t]) * a.inv_T) / s_Z[t];
       double qb = exp(((double)lq - (double)s_lmax[Bp1 + t]) * a.inv_T) / s_Z[Bp1 + t];
       if (a.use_topp) {

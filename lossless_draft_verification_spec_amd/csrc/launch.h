@@ -38,6 +38,7 @@ struct LinearArgs {
   const ToppStat* topp;
   RowStat* rowstat;
   int rowstat_ready;  // rowstat already holds every row's statistics (launch_combine_rows)
+  const float* gath;  // logit at each row's draft token (LM-head epilogue), or null: read the rows
   DrawDesc* desc;
   int32_t* ucount;
   int32_t* accept_len;
@@ -205,23 +206,29 @@ hipError_t launch_kv_commit(const KvArgs& a, hipStream_t stream);
 
 // lmhead.hip -- LM head on MFMA feeding the linear verify
 struct LMHeadArgs {
-  const uint16_t* h_ar;     // bf16 [nP][K]
-  const uint16_t* h_dr;     // bf16 [nQ][K]
-  const uint16_t* w_t;      // bf16 [N][K]
-  const uint16_t* lora_at;  // bf16 [r][K] or null
-  const uint16_t* lora_bt;  // bf16 [N][r] or null
-  uint16_t* aaug;           // bf16 [M][K+kx] scratch: h row, then zeros (AR) / [t_hi | t_lo | 0] (draft)
-  uint16_t* baug;           // bf16 [N][kx] scratch: [B_t | B_t | 0]
+  const uint16_t* h_ar;    // bf16 [nP][K]
+  const uint16_t* h_dr;    // bf16 [nQ][K]
+  const uint16_t* w;       // bf16 [K][N]
+  const uint16_t* lora_a;  // bf16 [K][r] or null
+  const uint16_t* lora_b;  // bf16 [r][N] or null
   float lora_scale;
-  int nP, nQ, M, N, K, r;
-  int kx;                   // extra contraction columns (2r rounded up to 64; 0 without LoRA)
-  int mtiles, ntiles;
-  float c;                  // log2(e) / T for the epilogue's row pairs
-  float* logits;            // fp32 [M][N]
-  float2* part;             // [M][ntiles] online (max, sum exp) pairs
+  int nP, nQ, N, K, r;
+  float c;                 // log2(e) / T for the epilogue's row pairs
 };
 int lmhead_tile_n();
-int lmhead_tile_m();
-hipError_t launch_lmhead(const LMHeadArgs& a, hipStream_t stream);
+int lmhead_kx(int r);  // extra contraction columns of the LoRA delta (2r rounded up to 32)
+// bytes of the staged A operand for `rows` rows
+size_t lmhead_ablk_bytes(int rows, int K, int r);
+// Every row: per (row, column tile) online (max, sum exp) pairs [nP + nQ][ntiles], the logit at
+// each row's draft token (gath [nP + nQ]; p row B of a request has none) and, when out_p is not
+// null, the logits (p rows to out_p [nP][N], q rows to out_q [nQ][N]).
+hipError_t launch_lmhead_main(const LMHeadArgs& a, uint16_t* ablk, const int32_t* draft, int B,
+                              float2* part, float* gath, float* out_p, float* out_q,
+                              hipStream_t stream);
+// The stopping rows of every draw: row 2r = desc[r].prow, 2r + 1 = desc[r].qrow (if any), logits
+// to out [2 batch][N]; desc2 / rowstat2 describe the draws over those rows.
+hipError_t launch_lmhead_rows(const LMHeadArgs& a, uint16_t* ablk, int batch, const DrawDesc* desc,
+                              const RowStat* rowstat, DrawDesc* desc2, RowStat* rowstat2,
+                              float* out, hipStream_t stream);
 
 }  // namespace psispec

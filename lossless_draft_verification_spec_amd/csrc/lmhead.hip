@@ -1,36 +1,53 @@
-// lmhead.hip -- the LM head feeding the verify: logits = H W (+ LoRA on the draft rows) on MFMA.
+// lmhead.hip -- the LM head feeding the verify: logits = h W (+ LoRA on the draft rows) on MFMA.
 //
 // [lanes] §"헤드냐, LoRA냐": the draft path is the frozen AR weights plus a low-rank LoRA delta, the
 // verify path the frozen AR weights alone; [alphalab] walkthrough step 2 (draft rows through the
 // LoRA path) and step 3 (the AR scores the block).  Only the output projection is built here:
-//   p rows (AR):    logits[m]  = h_ar[m] . W
-//   q rows (draft): logits[m]  = h_dr[m] . W + s (h_dr[m] . A) . B
-// The product is the one dense contraction of the verify step, so it runs on the bf16 matrix cores
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  The weight is taken in its usual storage, one
-// contiguous row of H values per token (W_t[V][H]), so both MFMA operands are contiguous along the
-// contraction and go to LDS without a transpose.
+//   p rows (AR):    logits[m] = h_ar[m] . W
+//   q rows (draft): logits[m] = h_dr[m] . W + s (h_dr[m] . A) . B
+// with W [H][V], A [H][r], B [r][V] (bf16, V contiguous in W and B).  The product is the one dense
+// contraction of the verify step, so it runs on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation).
 //
-// Tiling: a 256x256 output tile per 256-thread workgroup (four wave64s, 128x128 each = 4x4 MFMA
-// tiles), K steps of 64 double-buffered in LDS (144 KB), 16-byte global loads staged through
-// registers.  Tiles are ordered so that the workgroups of one XCD sweep the M tiles of the same
-// W column block together, so each W block comes from HBM once and is reused through that XCD's L2.
-// The LoRA delta rides in the same MFMA loop as extra contraction columns: t = s (h_dr . A) is
-// computed in fp64 and split into two bf16 parts t_hi + t_lo (relative error 2^-17, far below the
-// fp32 accumulation error of the H-long product), and the extra steps multiply [t_hi | t_lo] by
-// [B | B] (zeros for the AR rows and the padding).  The epilogue writes the fp32 logits and emits
-// per (row, column tile) the online softmax pair (max, sum exp) that the verify's decide and draw
-// kernels consume in place of the HBM row pass.
+// Operands.  The A operand (hidden states plus LoRA columns) is staged by k_build_a in a K-step
+// blocked layout, [K/32][Mpad][32]: the 32 contraction columns of one K step of a whole M tile are
+// one contiguous block, so every load of it fills whole cache lines.  The LoRA delta rides in the
+// same MFMA loop as extra contraction columns: t = s (h_dr . A) is summed in fp64, rounded to fp32
+// and split into bf16 t_hi + t_lo (relative error 2^-17, far below the fp32 accumulation error of
+// the H-long product); the extra K steps multiply [t_hi | t_lo | 0] by the rows [B | B | 0]
+// (zeros for the AR rows).  W and B are read in place, V contiguous: each K step of a tile is 32
+// rows of BN contiguous columns.  The MFMA wants eight consecutive contraction values of one
+// column per lane, so the B fragments come out of LDS through gfx950's transposing read
+// (ds_read_b64_tr_b16: a 16-lane group reads a 4 x 16 block and each lane receives one column's
+// four values).
+//
+// Tiling.  A BM x BN output tile per 256-thread workgroup (four wave64s, 128 x 128 each = 4 x 4
+// MFMA tiles of 32 x 32), K steps of 32 through NSTAGE LDS stages filled by 16-byte
+// direct-to-LDS buffer loads NSTAGE-1 steps ahead (no register staging), one barrier per step.
+// Workgroup ids are dealt round-robin to the 8 XCDs; each XCD takes a contiguous range of column
+// tiles with the M tiles fastest, so the workgroups that share a W column block run on one XCD
+// at the same time and share it through that XCD's L2.
+//
+// Epilogue.  The logits are not stored.  Per (row, column tile) it emits the online softmax pair
+// (max, sum exp2((x - max) log2e / T)) that the verify combines in place of an HBM row pass, and
+// the logit at the row's draft token (its one column tile writes it), which the accept test
+// needs.  Storing the logits is an option, used for the stopping rows that the final draw reads
+// (recomputed by a second launch over just those rows: the same kernel and K order give the same
+// bits) and for a caller who asks for them.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace psispec {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
-constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per LDS stage: A tile then B tile (32 KB)
-constexpr int kDma = BM * BK * 2 / 1024 / 4;  // 1 KB direct-to-LDS blocks per wave per operand
+constexpr int BK = 32;                  // contraction columns per K step
 constexpr int kXcd = 8;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer resource: 32-bit data, no swizzle
 
@@ -39,32 +56,75 @@ __device__ inline uint16_t bf16_rne(float f) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// Row m of the augmented A operand (grid over all M rows), KX = K + kx columns: the hidden state
-// (h_ar row m for m < nP, h_dr row m - nP after), then the extra contraction columns: zeros for the
-// AR rows; for draft row i = m - nP, t_j = s sum_h h_dr[i][h] A_t[j][h] (fp64 sum) stored as bf16
-// t_hi (columns K..K+r-1) and t_lo = t - t_hi (columns K+r..K+2r-1), zero up to KX.
-__global__ __launch_bounds__(kThreads) void k_build_a(const uint16_t* __restrict__ har,
-                                                      const uint16_t* __restrict__ hd,
-                                                      const uint16_t* __restrict__ at, int nP,
-                                                      int K, int r, int kx, float scale,
-                                                      uint16_t* __restrict__ aaug) {
+// The transposing LDS read.  The restrict-qualified (inlined) parameter gives the access an alias
+// scope, so the compiler does not add a wait for every direct-to-LDS load in flight before it: the
+// kernel orders those loads and the reads itself (explicit vmcnt waits and a barrier per K step).
+__device__ __attribute__((always_inline)) inline bf16x4 tr_read(const lds_bf16x4* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+__device__ inline float bf16_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Row m of the staged A operand ([KTX][Mpad][32], KTX = (K + kx) / 32): the hidden state of source
+// row src (h_ar row src for src < nP, h_dr row src - nP after; zeros for src < 0), then the extra
+// contraction columns: zeros for the AR rows; for a draft row, t_j = s sum_h h[h] A[h][j] (fp64
+// sum) stored as bf16 t_hi (columns K..K+r-1) and t_lo = t - t_hi (columns K+r..K+2r-1), zero up to
+// K + kx.  Source rows: m itself (m < nP + nQ), or with a draw list the stopping rows of request
+// m / 2 (row 2r = p row of the draw, 2r + 1 = its q row); that form also rewrites the draw's
+// descriptor and row statistics for the recomputed rows (row index 2r and 2r + 1).
+struct BuildArgs {
+  const uint16_t* h_ar;
+  const uint16_t* h_dr;
+  const uint16_t* lora_a;  // [K][r]
+  float lora_scale;
+  int nP, nQ, K, r, kx, Mpad;
+  int nrows;               // rows with a source (the rest of Mpad is zero)
+  const DrawDesc* desc;    // null: identity rows
+  const RowStat* rowstat;
+  DrawDesc* desc2;
+  RowStat* rowstat2;
+  uint16_t* ablk;
+};
+
+__global__ __launch_bounds__(kThreads) void k_build_a(BuildArgs a) {
   const int m = blockIdx.x;
-  const int KX = K + kx;
-  uint16_t* row = aaug + (int64_t)m * KX;
-  const uint16_t* x = m < nP ? har + (int64_t)m * K : hd + (int64_t)(m - nP) * K;
-  const int nc = K >> 3;  // K is a multiple of 64: whole 16-byte chunks
-  for (int c = threadIdx.x; c < nc; c += kThreads)
-    *reinterpret_cast<u32x4*>(row + 8 * c) = *reinterpret_cast<const u32x4*>(x + 8 * c);
-  uint16_t* out = row + K;
-  if (m < nP) {
-    for (int j = threadIdx.x; j < kx; j += kThreads) out[j] = 0;
-    return;
+  int src = -1;
+  if (m < a.nrows) {
+    if (!a.desc) {
+      src = m;
+    } else {
+      const DrawDesc d = a.desc[m >> 1];
+      src = (m & 1) ? d.qrow : d.prow;
+      if (threadIdx.x == 0) {
+        if (src >= 0) a.rowstat2[m] = a.rowstat[src];
+        if ((m & 1) == 0) {
+          DrawDesc d2 = d;
+          d2.prow = m;
+          d2.qrow = d.qrow >= 0 ? m + 1 : -1;
+          a.desc2[m >> 1] = d2;
+        }
+      }
+    }
   }
-  for (int j = threadIdx.x + 2 * r; j < kx; j += kThreads) out[j] = 0;
-  // all ranks in one pass over h: each thread owns 8-element chunks of h and keeps up to 16 fp64
-  // partial sums per round
-  for (int j0 = 0; j0 < r; j0 += 16) {
-    const int nj = min(16, r - j0);
+  const int64_t kstride = (int64_t)a.Mpad * BK;  // elements from one K step's block to the next
+  uint16_t* dst = a.ablk + (int64_t)m * BK;
+  const int nc = a.K >> 3;  // 16-byte chunks of the hidden state
+  const uint16_t* x = src < 0 ? nullptr
+                    : src < a.nP ? a.h_ar + (int64_t)src * a.K
+                                 : a.h_dr + (int64_t)(src - a.nP) * a.K;
+  for (int c = threadIdx.x; c < nc; c += kThreads) {
+    const u32x4 v = x ? *reinterpret_cast<const u32x4*>(x + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(dst + (c >> 2) * kstride + 8 * (c & 3)) = v;
+  }
+  if (a.kx == 0) return;
+  uint16_t* ext = dst + (a.K / BK) * kstride;  // the extra columns: one or more K steps
+  auto put = [&](int j, uint16_t v) { ext[(j / BK) * kstride + (j % BK)] = v; };
+  const bool draft_row = src >= a.nP;
+  for (int j = threadIdx.x + (draft_row ? 2 * a.r : 0); j < a.kx; j += kThreads) put(j, 0);
+  if (!draft_row) return;
+  __shared__ double s_acc[kThreads / 64][16];
+  for (int j0 = 0; j0 < a.r; j0 += 16) {
+    const int nj = min(16, a.r - j0);
     double acc[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.0;
@@ -77,15 +137,11 @@ __global__ __launch_bounds__(kThreads) void k_build_a(const uint16_t* __restrict
         xv[2 * e + 1] = (double)__uint_as_float(xw[e] & 0xffff0000u);
       }
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        if (q < nj) {
-          const u32x4 aw = *reinterpret_cast<const u32x4*>(at + (int64_t)(j0 + q) * K + 8 * c);
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t* arow = a.lora_a + (int64_t)(8 * c + e) * a.r + j0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[q] += xv[2 * e] * (double)__uint_as_float(aw[e] << 16);
-            acc[q] += xv[2 * e + 1] * (double)__uint_as_float(aw[e] & 0xffff0000u);
-          }
-        }
+        for (int q = 0; q < 16; ++q)
+          if (q < nj) acc[q] += xv[e] * (double)bf16_f(arow[q]);
       }
     }
 #pragma unroll
@@ -93,7 +149,6 @@ __global__ __launch_bounds__(kThreads) void k_build_a(const uint16_t* __restrict
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) acc[q] += __shfl_xor(acc[q], off, 64);
     }
-    __shared__ double s_acc[kThreads / 64][16];
     if ((threadIdx.x & 63) == 0) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) s_acc[threadIdx.x >> 6][q] = acc[q];
@@ -103,100 +158,130 @@ __global__ __launch_bounds__(kThreads) void k_build_a(const uint16_t* __restrict
       double tot = 0.0;
       for (int w = 0; w < kThreads / 64; ++w) tot += s_acc[w][threadIdx.x];
       const int j = j0 + threadIdx.x;
-      const float tf = (float)(tot * (double)scale);
+      const float tf = (float)(tot * (double)a.lora_scale);
       const uint16_t hi = bf16_rne(tf);
-      out[j] = hi;
-      out[r + j] = bf16_rne(tf - __uint_as_float((uint32_t)hi << 16));
+      put(j, hi);
+      put(a.r + j, bf16_rne(tf - bf16_f(hi)));
     }
     __syncthreads();
   }
 }
 
-// Extra contraction columns of vocab column n: [B_t[n][0..r) | B_t[n][0..r) | 0 ...] up to kx.
-__global__ __launch_bounds__(kThreads) void k_lora_aug_cols(const uint16_t* __restrict__ bt, int N,
-                                                            int r, int kx,
-                                                            uint16_t* __restrict__ baug) {
-  // one thread per 8-column chunk of an augmented row (kx is a multiple of 64)
-  const int cpr = kx >> 3;
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (int64_t)N * cpr) return;
-  const int n = (int)(idx / cpr);
-  const int j0 = 8 * (int)(idx - (int64_t)n * cpr);
-  const uint16_t* src = bt + (int64_t)n * r;
-  uint32_t w[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    uint32_t v2[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int j = j0 + 2 * e + k;
-      v2[k] = j < r ? src[j] : (j < 2 * r ? src[j - r] : 0u);
-    }
-    w[e] = v2[0] | (v2[1] << 16);
-  }
-  *reinterpret_cast<u32x4*>(baug + (int64_t)n * kx + j0) = u32x4{w[0], w[1], w[2], w[3]};
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
+struct GemmArgs {
+  const uint16_t* ablk;    // [KTX][Mpad][32]
+  const uint16_t* w;       // [K][N]
+  const uint16_t* lora_b;  // [r][N] or null
+  int M, Mpad, N, K, r, KT, KTX, mtiles, ntiles;
+  float c;                 // log2(e) / T for the row pairs
+  float2* part;            // [M][ntiles] row pairs, or null
+  const int32_t* draft;    // gather: draft token of each row (linear layout), or null
+  int B, nP;
+  float* gath;             // [M] logit at the row's draft token
+  float* out0;             // logit store, or null: row m < split -> out0 + m N,
+  float* out1;             //                        else out1 + (m - split) N
+  int split;
+};
 
 // s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory operations are in
 // flight, leaving the LDS and export counters unconstrained.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-__global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(LMHeadArgs a) {
+constexpr int BM = 256, BN = 256, NSTAGE = 4;  // output tile and LDS stages
+
+__global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(GemmArgs a) {
+  constexpr int WN = BN / 128, WM = BM / 128;
+  static_assert(WM * WN == 4, "four 128 x 128 wave tiles per workgroup");
+  constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per LDS stage: A block, then B block
+  constexpr int nA = BM / 64;            // 1 KB direct-to-LDS loads per wave per step (A)
+  constexpr int nB = BN / 64;            // idem (B)
+  constexpr int D = nA + nB;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NSTAGE * STAGE];
-  // XCD-aware tile order: workgroup ids are dealt round-robin to the 8 XCDs; give each XCD a
-  // contiguous range of tiles, M tiles fastest, so the XCD's workgroups share W column blocks.
+
   const int ntile = a.mtiles * a.ntiles;
-  const int per_xcd = (int)((gridDim.x + kXcd - 1) / kXcd);
+  const int per_xcd = (int)(gridDim.x / kXcd);
   const int tile = (int)(blockIdx.x % kXcd) * per_xcd + (int)(blockIdx.x / kXcd);
   if (tile >= ntile) return;
   const int tm = tile % a.mtiles, tn = tile / a.mtiles;
   const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: LDS bases go to M0
-  const int wm = wave >> 1, wn = wave & 1;
-  const int K = a.K;
+  const int wm = wave / WN, wn = wave % WN;
 
-  // Operands stream HBM -> LDS with 16-byte direct-to-LDS buffer loads, NSTAGE-1 K steps ahead of
-  // the MFMAs.  Each load instruction fills one 1 KB block: 16 rows of 32 bf16, lane l writing row
-  // l/4, 16-byte slot l%4.  Slot s of row r holds the row's K chunk s ^ f(r), f(r) = r2 | (r1^r3)<<1
-  // (r_k = bit k of r): the 16-byte fragment reads then hit distinct banks both within each group
-  // of 8 rows on 32 banks and within each group of 16 rows on 64 banks.  The buffer resources
-  // cover only this tile's valid rows: rows past M or N, and the steps past the end (a zero-length
-  // resource), land as zeros.  A is the augmented [M][K + kx] matrix; B is W_t for the first K/32
-  // steps and the augmented LoRA columns [N][kx] after.
-  const int KX = K + a.kx;
-  const int rows_a = min(BM, a.M - m0), rows_b = min(BN, a.N - n0);
+  // ---- loads ---------------------------------------------------------------------------------
+  // A: one load fills 16 rows x 64 B (lane l: row l/4, 16-byte slot l%4).  Slot s of row r holds
+  // the row's chunk s ^ f(r), f(r) = r2 | (r1 ^ r3) << 1 (r_k = bit k of r), which keeps the
+  // 16-byte fragment reads conflict-free.  The whole K step of the tile is one contiguous block.
+  // B: one load fills 512 contiguous columns of the step's 32 rows (BN = 256: two rows).  Slot s
+  // of row k holds the row's 8-column chunk s ^ ((k & 3) << 2): the transposing reads of four
+  // consecutive rows then fall on distinct banks.  W and the LoRA rows are read through buffer
+  // resources whose range ends with the matrix: rows past the end read as zeros (the padding of a
+  // last partial K step); columns past N of a last column tile read neighbouring data that only
+  // feeds the discarded output columns.
   const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.aaug + (int64_t)m0 * KX), (short)0, rows_a * KX * 2, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.w_t + (int64_t)n0 * K), (short)0, rows_b * K * 2, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.baug + (int64_t)n0 * a.kx), (short)0, rows_b * a.kx * 2, kRsrcWord3);
+      (void*)a.ablk, (short)0, (int)((uint32_t)a.KTX * (uint32_t)a.Mpad * 64u), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_0 =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a.w_t, (short)0, 0, kRsrcWord3);
-  const int drow = wave * kDma * 16 + (lane >> 2);  // + 16 i
-  const int gch = (lane & 3) ^ (((lane >> 4) & 1) | ((((lane >> 3) ^ (lane >> 5)) & 1) << 1));
-  const int va = drow * KX * 2 + 16 * gch;
-  const int vw = drow * K * 2 + 16 * gch;
-  const int vx = drow * a.kx * 2 + 16 * gch;
-  const int KT = K / BK, KTX = KT + a.kx / BK;
-  auto dma = [&](int kt) {
-    uint16_t* As = smem + (kt % NSTAGE) * STAGE + wave * kDma * 512;
-    uint16_t* Bs = As + BM * BK;
-    const bool live = kt < KTX, main = kt < KT;
-    const __amdgpu_buffer_rsrc_t ra = live ? rs_a : rs_0;
-    const __amdgpu_buffer_rsrc_t rb = live ? (main ? rs_w : rs_x) : rs_0;
-    const int oa = va + kt * (BK * 2);
-    const int ob = main ? vw + kt * (BK * 2) : vx + (kt - KT) * (BK * 2);
-    const int sa = 16 * KX * 2, sb = 16 * (main ? K : a.kx) * 2;
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.ablk, (short)0, 0, kRsrcWord3);
+  const int arow = lane >> 2;
+  const int ach = (lane & 3) ^ (((arow >> 2) & 1) | ((((arow >> 1) ^ (arow >> 3)) & 1) << 1));
+  const int va = (wave * nA * 16 + arow) * 64 + 16 * ach;  // + 1024 i
+  int vb[nB], cbo[nB], lrow[nB];
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(As + i * 512), 16, oa + i * sa, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(Bs + i * 512), 16, ob + i * sb, 0, 0, 0);
+  for (int i = 0; i < nB; ++i) {
+    const int e = (wave * nB + i) * 512 + lane * 8;  // element within the step's B block
+    const int kr = e / BN, s = (e % BN) >> 3;
+    cbo[i] = (s ^ ((kr & 3) << 2)) * 16;
+    vb[i] = kr * a.N * 2 + cbo[i];
+    lrow[i] = kr;
+  }
+  const int64_t wtotal = (int64_t)a.K * a.N;
+  const int64_t lleft = a.lora_b ? 2 * ((int64_t)a.r * a.N - n0) : 0;
+  const int nrow2 = a.N * 2;
+  // A K step's loads.  kW: a step of W (no branch, so that the loads interleave with the MFMAs of
+  // one basic block); otherwise any step: W, a LoRA step, or past the end (zero-length resource).
+  auto dma = [&](int kt, auto kW) {
+    uint16_t* As = smem + (kt % NSTAGE) * STAGE + wave * nA * 512;
+    uint16_t* Bs = smem + (kt % NSTAGE) * STAGE + BM * BK + wave * nB * 512;
+    const bool live = decltype(kW)::value || kt < a.KTX;
+    const __amdgpu_buffer_rsrc_t ra = live ? rs_a : rs_0;
+    const int soa = live ? (kt * a.Mpad + m0) * 64 : 0;
+#pragma unroll
+    for (int i = 0; i < nA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(As + i * 512), 16, va + i * 1024,
+                                               soa, 0, 0);
+    const int64_t wbase = (int64_t)kt * BK * a.N + n0;
+    const int64_t wleft = 2 * (wtotal - wbase);
+    const auto w_rsrc = [&]() {
+      return __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.w + wbase), (short)0,
+          (int)(uint32_t)(wleft > 0xffffffffll ? 0xffffffffll : wleft), kRsrcWord3);
+    };
+    if constexpr (decltype(kW)::value) {
+      const __amdgpu_buffer_rsrc_t rb = w_rsrc();
+#pragma unroll
+      for (int i = 0; i < nB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(Bs + i * 512), 16, vb[i], 0, 0, 0);
+    } else if (kt < a.KT) {
+      const __amdgpu_buffer_rsrc_t rb = w_rsrc();
+#pragma unroll
+      for (int i = 0; i < nB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(Bs + i * 512), 16, vb[i], 0, 0, 0);
+    } else {
+      const int64_t left = live ? lleft : 0;
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.lora_b ? a.lora_b + n0 : a.w), (short)0, (int)(uint32_t)left, kRsrcWord3);
+      const int jb = (kt - a.KT) * BK;
+#pragma unroll
+      for (int i = 0; i < nB; ++i) {
+        // extra column j of a LoRA step: LoRA row j (t_hi), j - r (t_lo), none past 2r
+        const int j = jb + lrow[i];
+        const int lr = j < a.r ? j : j - a.r;
+        const int off = j < 2 * a.r ? lr * nrow2 + cbo[i] : (int)left;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(Bs + i * 512), 16, off, 0, 0, 0);
+      }
     }
   };
+  using kWStep = std::integral_constant<bool, true>;
+  using kAnyStep = std::integral_constant<bool, false>;
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -206,18 +291,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(LMHeadArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // fragment of MFMA row/column l%32, K chunk 2 ks + l/32 (8 bf16), through the slot swizzle
+  // ---- fragments -----------------------------------------------------------------------------
+  // A: MFMA row l%32, contraction chunk 2 ks + l/32 (8 values), through the slot swizzle.
   const int xr = ((lane >> 2) & 1) | ((((lane >> 1) ^ (lane >> 3)) & 1) << 1);
   const int fofs0 = (lane & 31) * BK + 8 * ((lane >> 5) ^ xr);
   const int fofs1 = (lane & 31) * BK + 8 * ((2 + (lane >> 5)) ^ xr);
+  // B: lane l of 16-lane group g reads 8 bytes at contraction row 8 (g / 2) + 4 h + (l % 16) / 4,
+  // columns 16 (g % 2) + 4 (l % 4) .. +3 of the MFMA column block; it receives column
+  // 16 (g % 2) + l % 16 at four consecutive contraction rows.  Byte offsets within the stage's B
+  // block, per column block j (h and ks are immediate offsets).
+  const int g = lane >> 4, q = lane & 15;
+  int bofs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int k = 8 * (g >> 1) + (q >> 2);
+    const int chunk = wn * 16 + 4 * (j ^ (q >> 2)) + 2 * (g & 1) + ((q & 3) >> 1);
+    bofs[j] = k * BN * 2 + chunk * 16 + (q & 1) * 8;
+  }
   bf16x8 fa[2][4], fb[2][4];
   auto fread = [&](int kt, int ks, bf16x8(&ra)[4], bf16x8(&rb)[4]) {
     const uint16_t* As = smem + (kt % NSTAGE) * STAGE + (wm * 128) * BK + (ks ? fofs1 : fofs0);
-    const uint16_t* Bs = As + BM * BK + (wn - wm) * 128 * BK;
+    const char* Bs = reinterpret_cast<const char*>(smem + (kt % NSTAGE) * STAGE + BM * BK) +
+                     ks * 16 * BN * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * BK);
-      rb[i] = *reinterpret_cast<const bf16x8*>(Bs + i * 32 * BK);
+    for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * BK);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x4 lo = tr_read((const lds_bf16x4*)(Bs + bofs[j]));
+      const bf16x4 hi = tr_read((const lds_bf16x4*)(Bs + bofs[j] + 4 * BN * 2));
+      rb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
   auto mfma16 = [&](const bf16x8(&ra)[4], const bf16x8(&rb)[4]) {
@@ -228,54 +330,62 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(LMHeadArgs a) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i], rb[j], acc[i][j], 0, 0, 0);
   };
 
+  const int KTX = a.KTX;
 #pragma unroll
-  for (int k = 0; k < NSTAGE - 1; ++k) dma(k);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSTAGE - 2) * 2 * kDma));  // step 0 landed
+  for (int k = 0; k < NSTAGE - 1; ++k) dma(k, kAnyStep{});
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSTAGE - 2) * D));  // step 0 landed
   __builtin_amdgcn_s_barrier();
   fread(0, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < KTX; ++kt) {
+  auto step = [&](int kt, auto kW) {
     // One barrier per step.  Past it, step kt+1 has landed for every wave (each waited for its own
     // loads of it) and every wave is done with step kt-1, whose stage the loads of step
     // kt+NSTAGE-1 then overwrite.  Everything else in the step is free to overlap the MFMAs.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSTAGE - 3) * 2 * kDma));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSTAGE - 3) * D));
     __builtin_amdgcn_s_barrier();
     fread(kt, 1, fa[1], fb[1]);
-    dma(kt + NSTAGE - 1);
+    dma(kt + NSTAGE - 1, kW);
     mfma16(fa[0], fb[0]);
     fread(kt + 1, 0, fa[0], fb[0]);
     mfma16(fa[1], fb[1]);
-    // issue order: one fragment read after each of the first 8 MFMAs, one DMA load after each of
-    // the next 8, then the reads of step kt+1 between the first 8 MFMAs of substep 1
+    // issue order: the 12 fragment reads of substep 1 after the first 12 MFMAs, the step's loads
+    // after the next 4, then the reads of step kt+1 between the MFMAs of substep 1
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int k = 0; k < 12; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (direct-to-LDS)
+    for (int k = 0; k < 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, D / 4, 0);  // VMEM read (direct-to-LDS)
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int k = 0; k < 12; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-  }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+  // steps whose look-ahead loads are W steps, then the last NSTAGE-1 steps of W and the LoRA steps
+  const int kt_w = a.KT - (NSTAGE - 1);
+  int kt = 0;
+  for (; kt < kt_w; ++kt) step(kt, kWStep{});
+  for (; kt < KTX; ++kt) step(kt, kAnyStep{});
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the zero-filling tail loads also write LDS
   __syncthreads();
 
   // ---- epilogue -------------------------------------------------------------------------------
   // Element (i, j, v) of this lane sits at row m0 + wm*128 + i*32 + 8*(v/4) + 4*(lane/32) + v%4,
-  // column n0 + wn*128 + j*32 + lane%32.  One 64-row slice (i fixed) at a time goes through LDS:
-  // then 4 threads per row reduce 64 columns each to the segment's (max, sum exp2((x - max) c)),
-  // combined over the row's 4 segments, and each wave stores 16 of the slice's rows, one row of
-  // 256 columns per 1 KB coalesced instruction.
+  // column n0 + wn*128 + j*32 + lane%32.  One slice (i fixed: WM*32 rows) at a time goes through
+  // LDS; then TPR threads per row reduce 64 columns each to the segment's
+  // (max, sum exp2((x - max) c)), combined over the row's segments in a fixed order.
+  constexpr int SR = WM * 32;        // rows per slice
+  constexpr int TPR = kThreads / SR;  // threads per row (4 or 8); each takes 64 columns
   constexpr int SROW = BN + 4;
-  float* S = reinterpret_cast<float*>(smem);  // [64][SROW]
+  float* S = reinterpret_cast<float*>(smem);  // [SR][SROW]
   const float c = a.c;
-  const int lr = t >> 2, qq = t & 3;
+  const int lr = t / TPR, qq = t % TPR;
+  const int ncol = min(BN, a.N - n0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -286,87 +396,186 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(LMHeadArgs a) {
         S[rr * SROW + wn * 128 + j * 32 + (lane & 31)] = acc[i][j][v];
       }
     __syncthreads();
-    const int m = m0 + (lr < 32 ? i * 32 + lr : 128 + i * 32 + (lr - 32));
-    const int nvalid = a.N - (n0 + qq * 64);  // columns of this segment inside the row (may be <= 0)
+    auto slice_row = [&](int sr) { return m0 + (sr >> 5) * 128 + i * 32 + (sr & 31); };
+    const int m = slice_row(lr);
+    const int nvalid = ncol - qq * 64;  // columns of this segment inside the row (may be <= 0)
     const float* src = S + lr * SROW + qq * 64;
     float4 buf[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) buf[k] = *reinterpret_cast<const float4*>(src + 4 * k);
-    // segment max and sum, four independent chains each (a finite floor: a segment past the row's
-    // end gives (floor, 0)); the chains are combined in a fixed order
-    float mq[4] = {kNegBig, kNegBig, kNegBig, kNegBig};
+    if (a.part) {
+      // segment max and sum, four independent chains each (a finite floor: a segment past the
+      // row's end gives (floor, 0)); the chains are combined in a fixed order
+      float mq[4] = {kNegBig, kNegBig, kNegBig, kNegBig};
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float x[4] = {buf[k].x, buf[k].y, buf[k].z, buf[k].w};
+      for (int k = 0; k < 16; ++k) {
+        const float x[4] = {buf[k].x, buf[k].y, buf[k].z, buf[k].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * k + e < nvalid) mq[e] = fmaxf(mq[e], x[e]);
-    }
-    const float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-    float sq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float x[4] = {buf[k].x, buf[k].y, buf[k].z, buf[k].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * k + e < nvalid) sq[e] += __builtin_amdgcn_exp2f((x[e] - mx) * c);
-    }
-    float sm = (sq[0] + sq[1]) + (sq[2] + sq[3]);
-    float mxc = mx;
-#pragma unroll
-    for (int off = 1; off <= 2; off <<= 1) {
-      const float m2 = __shfl_xor(mxc, off, 64);
-      const float s2 = __shfl_xor(sm, off, 64);
-      os_combine(mxc, sm, m2, s2, c);
-    }
-    if (qq == 0 && m < a.M) a.part[(int64_t)m * a.ntiles + tn] = make_float2(mxc, sm);
-    // logits: one wave writes one row's 256 columns per instruction (16 rows per wave)
-    const int ncol = min(BN, a.N - n0);
-#pragma unroll 4
-    for (int q = 0; q < 16; ++q) {
-      const int sr = wave * 16 + q;  // slice row
-      const int mr = m0 + (sr < 32 ? i * 32 + sr : 128 + i * 32 + (sr - 32));
-      if (mr >= a.M) continue;
-      const float4 v4 = *reinterpret_cast<const float4*>(S + sr * SROW + 4 * lane);
-      float* dst = a.logits + (int64_t)mr * a.N + n0 + 4 * lane;
-      if (4 * lane + 4 <= ncol && (a.N & 3) == 0) {
-        *reinterpret_cast<float4*>(dst) = v4;
-      } else {
-        const float e4[4] = {v4.x, v4.y, v4.z, v4.w};
         for (int e = 0; e < 4; ++e)
-          if (4 * lane + e < ncol) dst[e] = e4[e];
+          if (4 * k + e < nvalid) mq[e] = fmaxf(mq[e], x[e]);
+      }
+      const float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+      float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float x[4] = {buf[k].x, buf[k].y, buf[k].z, buf[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * k + e < nvalid) sq[e] += __builtin_amdgcn_exp2f((x[e] - mx) * c);
+      }
+      float sm = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+      float mxc = mx;
+#pragma unroll
+      for (int off = 1; off < TPR; off <<= 1) {
+        const float m2 = __shfl_xor(mxc, off, 64);
+        const float s2 = __shfl_xor(sm, off, 64);
+        os_combine(mxc, sm, m2, s2, c);
+      }
+      if (qq == 0 && m < a.M) a.part[(int64_t)m * a.ntiles + tn] = make_float2(mxc, sm);
+    }
+    if (a.gath && m < a.M) {
+      // the logit at this row's draft token, by the thread whose segment holds it
+      int d = -1;
+      if (m < a.nP) {
+        const int rq = m / (a.B + 1), pos = m - rq * (a.B + 1);
+        if (pos < a.B) d = a.draft[(int64_t)rq * a.B + pos];
+      } else {
+        d = a.draft[m - a.nP];
+      }
+      const int o = d - (n0 + qq * 64);
+      if (d >= 0 && d < a.N && o >= 0 && o < 64) a.gath[m] = src[o];
+    }
+    if (a.out0) {
+      // logits: each wave stores SR/4 rows of the slice, 256 columns per instruction
+      for (int k = 0; k < SR / 4; ++k) {
+        const int sr = wave * (SR / 4) + k;
+        const int mr = slice_row(sr);
+        if (mr >= a.M) continue;
+        float* dst = mr < a.split ? a.out0 + (int64_t)mr * a.N : a.out1 + (int64_t)(mr - a.split) * a.N;
+#pragma unroll
+        for (int cb = 0; cb < BN; cb += 256) {
+          const int col = cb + 4 * lane;
+          const float4 v4 = *reinterpret_cast<const float4*>(S + sr * SROW + col);
+          if (col + 4 <= ncol) {
+            *reinterpret_cast<float4*>(dst + n0 + col) = v4;
+          } else {
+            const float e4[4] = {v4.x, v4.y, v4.z, v4.w};
+            for (int e = 0; e < 4; ++e)
+              if (col + e < ncol) dst[n0 + col + e] = e4[e];
+          }
+        }
       }
     }
     __syncthreads();
   }
 }
 
+constexpr int kBM = BM, kBN = BN;
+
+int lmhead_mpad(int rows) { return (rows + kBM - 1) / kBM * kBM; }
+
 }  // namespace
 
-int lmhead_tile_n() { return BN; }
-int lmhead_tile_m() { return BM; }
+int lmhead_tile_n() { return kBN; }
 
-hipError_t launch_lmhead(const LMHeadArgs& a, hipStream_t stream) {
-  if (a.M == 0) return hipSuccess;
-  timing_begin("build_a", stream);
-  hipLaunchKernelGGL(k_build_a, dim3((unsigned)a.M), dim3(kThreads), 0, stream, a.h_ar, a.h_dr,
-                     a.lora_at, a.nP, a.K, a.r, a.kx, a.lora_scale, a.aaug);
-  if (a.kx > 0) {
-    const int64_t n = (int64_t)a.N * (a.kx >> 3);
-    hipLaunchKernelGGL(k_lora_aug_cols, dim3((unsigned)((n + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, a.lora_bt, a.N, a.r, a.kx, a.baug);
-  }
-  timing_end("build_a", stream);
-  {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int ntile = a.mtiles * a.ntiles;
+int lmhead_kx(int r) { return r > 0 ? (2 * r + BK - 1) / BK * BK : 0; }
+
+size_t lmhead_ablk_bytes(int rows, int K, int r) {
+  return (size_t)lmhead_mpad(rows) * (size_t)(K + lmhead_kx(r)) * 2;
+}
+
+namespace {
+
+hipError_t run_gemm(const LMHeadArgs& a, const uint16_t* ablk, int rows, float2* part,
+                    const int32_t* draft, int B, float* gath, float* out0, float* out1, int split,
+                    hipStream_t stream, const char* name) {
+  GemmArgs g{};
+  g.ablk = ablk;
+  g.w = a.w;
+  g.lora_b = a.lora_b;
+  g.M = rows;
+  g.Mpad = lmhead_mpad(rows);
+  g.N = a.N;
+  g.K = a.K;
+  g.r = a.r;
+  g.KT = a.K / BK;
+  g.KTX = (a.K + lmhead_kx(a.r)) / BK;
+  g.mtiles = g.Mpad / kBM;
+  g.ntiles = (a.N + kBN - 1) / kBN;
+  g.c = a.c;
+  g.part = part;
+  g.draft = draft;
+  g.B = B;
+  g.nP = a.nP;
+  g.gath = gath;
+  g.out0 = out0;
+  g.out1 = out1;
+  g.split = split;
+  const int ntile = g.mtiles * g.ntiles;
   const unsigned grid = (unsigned)((ntile + kXcd - 1) / kXcd * kXcd);
-  timing_begin("lmhead_gemm", stream);
-  hipLaunchKernelGGL(k_lmhead_gemm, dim3(grid), dim3(kThreads), 0, stream, a);
-  timing_end("lmhead_gemm", stream);
+  timing_begin(name, stream);
+  hipLaunchKernelGGL(k_lmhead_gemm, dim3(grid), dim3(kThreads), 0, stream, g);
+  timing_end(name, stream);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lmhead_main(const LMHeadArgs& a, uint16_t* ablk, const int32_t* draft, int B,
+                              float2* part, float* gath, float* out_p, float* out_q,
+                              hipStream_t stream) {
+  const int M = a.nP + a.nQ;
+  if (M == 0) return hipSuccess;
+  BuildArgs b{};
+  b.h_ar = a.h_ar;
+  b.h_dr = a.h_dr;
+  b.lora_a = a.lora_a;
+  b.lora_scale = a.lora_scale;
+  b.nP = a.nP;
+  b.nQ = a.nQ;
+  b.K = a.K;
+  b.r = a.r;
+  b.kx = lmhead_kx(a.r);
+  b.Mpad = lmhead_mpad(M);
+  b.nrows = M;
+  b.ablk = ablk;
+  timing_begin("build_a", stream);
+  hipLaunchKernelGGL(k_build_a, dim3((unsigned)b.Mpad), dim3(kThreads), 0, stream, b);
+  timing_end("build_a", stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return run_gemm(a, ablk, M, part, draft, B, gath, out_p, out_q, a.nP, stream, "lmhead_gemm");
+}
+
+hipError_t launch_lmhead_rows(const LMHeadArgs& a, uint16_t* ablk, int batch, const DrawDesc* desc,
+                              const RowStat* rowstat, DrawDesc* desc2, RowStat* rowstat2,
+                              float* out, hipStream_t stream) {
+  const int rows = 2 * batch;
+  if (rows == 0) return hipSuccess;
+  BuildArgs b{};
+  b.h_ar = a.h_ar;
+  b.h_dr = a.h_dr;
+  b.lora_a = a.lora_a;
+  b.lora_scale = a.lora_scale;
+  b.nP = a.nP;
+  b.nQ = a.nQ;
+  b.K = a.K;
+  b.r = a.r;
+  b.kx = lmhead_kx(a.r);
+  b.Mpad = lmhead_mpad(rows);
+  b.nrows = rows;
+  b.desc = desc;
+  b.rowstat = rowstat;
+  b.desc2 = desc2;
+  b.rowstat2 = rowstat2;
+  b.ablk = ablk;
+  timing_begin("build_rows", stream);
+  hipLaunchKernelGGL(k_build_a, dim3((unsigned)b.Mpad), dim3(kThreads), 0, stream, b);
+  timing_end("build_rows", stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return run_gemm(a, ablk, rows, nullptr, nullptr, 0, nullptr, out, out, rows, stream,
+                  "lmhead_rows");
 }
 
 }  // namespace psispec

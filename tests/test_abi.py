@@ -119,3 +119,26 @@ def test_kv_commit_host_checks(libpsispec):
     assert L.psispec_kv_commit(fake, 320, 32, 10, 4, fake, 0, fake, fake, None, 2, None) == -1
     # an empty batch launches nothing
     assert L.psispec_kv_commit(None, 320, 32, 10, 4, None, 0, None, None, None, 0, None) == 0
+
+
+def test_lmhead_host_checks(libpsispec):
+    """The LM-head call's shape rules and its top-p / debug-buffer rules are checked on the host,
+    before anything is launched (pointers here are never dereferenced)."""
+    import lossless_draft_verification_spec_amd as pkg
+    L = libpsispec
+    assert pkg.lmhead_workspace_bytes(128, 8, 4096, 151936, 16) > 0
+    assert pkg.lmhead_workspace_bytes(128, 8, 4096, 151937, 16) == 0  # V not a multiple of 8
+    assert pkg.lmhead_workspace_bytes(128, 8, 4000, 151936, 16) == 0  # H not a multiple of 64
+    assert pkg.lmhead_workspace_bytes(128, 8, 4096, 151936, 65) == 0  # r > 64
+    P = ctypes.c_void_p(256)
+    big = ctypes.c_size_t(1 << 40)
+
+    def call(top_p, pdbg, qdbg):
+        s = pkg.psispec_sampling(1.0, top_p, 0, 0, 0, 0, 0)
+        return L.psispec_lmhead_verify(P, P, P, None, None, 1.0, 2, 2, 64, 256, 0, P,
+                                       ctypes.byref(s), P, P, None, None, None, pdbg, qdbg, P,
+                                       big, None)
+
+    assert call(0.9, None, None) == -5  # top-p needs the logits in memory: unsupported
+    assert call(1.0, P, None) == -1     # debug buffers go together
+    assert call(1.0, None, ctypes.c_void_p(8)) == -1

@@ -23,15 +23,21 @@ def test_lmhead_logits_match_numpy(orc, M, H, V, r):
     assert np.allclose(half - base, 0.5 * (lora - base), rtol=1e-12, atol=1e-15)
 
 
-def test_lmhead_rows_helper_matches_plain_oracle(orc):
-    """The numpy-product helper used at full size agrees with the plain loops (weights stored one
-    output row at a time)."""
-    rng = np.random.default_rng(7)
-    M, H, V, r = 4, 96, 53, 3
+@pytest.mark.parametrize("M,H,V,r", [(4, 96, 53, 3), (3, 1024, 40, 16), (2, 4096, 24, 16)])
+def test_lmhead_rows_helper_matches_plain_oracle(orc, M, H, V, r):
+    """The numpy-product helper used at full size agrees with the plain loops, also at a
+    contraction length that matters (H up to 4096) with a rank-16 LoRA delta, so the helper's
+    operand layout (W[H][V], A[H][r], B[r][V]) is checked where a transposed index would show."""
+    rng = np.random.default_rng(7 + H)
     h = bf16_round(rng.standard_normal((M, H)))
     W = bf16_round(rng.standard_normal((H, V)) * 0.02)
     A = bf16_round(rng.standard_normal((H, r)) * 0.01)
     Bl = bf16_round(rng.standard_normal((r, V)) * 0.01)
     plain = orc.lmhead_logits(h, W, A, Bl, scale=1.0)
-    helper = orc.lmhead_logits_rows(h, W.T.copy(), A.T.copy(), Bl.T.copy(), 1.0)
-    assert np.allclose(plain, helper, rtol=1e-13, atol=1e-15)
+    helper = orc.lmhead_logits_rows(h, W, A, Bl, 1.0)
+    assert np.allclose(plain, helper, rtol=1e-12, atol=1e-14)
+    wide = orc.lmhead_logits_rows(h, orc.widen_bf16(W), orc.widen_bf16(A), orc.widen_bf16(Bl), 1.0)
+    assert np.array_equal(wide, helper)
+    # the check can fail: W with its columns reversed does not agree
+    if V >= 2 and H >= 2:
+        assert not np.allclose(plain, orc.lmhead_logits_rows(h, W[:, ::-1].copy(), A, Bl, 1.0))
