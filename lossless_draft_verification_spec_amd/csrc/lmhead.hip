@@ -171,7 +171,16 @@ struct GemmArgs {
   const uint16_t* ablk;    // [KTX][Mpad][32]
   const uint16_t* w;       // [K][N]
   const uint16_t* lora_b;  // [r][N] or null
-  int M, Mpad, N, K, r, KT, KTX, mtiles, ntiles;
+  int M, Mpad, N, K, r, KT, KTX;
+  // Tiles: full 256-row bands of 256 x 256 tiles; a last band of at most 128 rows takes 128 x 512
+  // tiles instead (no MFMA work on padding rows).  Tiles are numbered by column group (256 columns,
+  // or 512 with such a band), bands fastest within a group, the 128 x 512 tile last.
+  int fbands;              // full bands (256 x 256 tiles)
+  int tailB;               // 1: a last band of 128 x 512 tiles
+  int gcols;               // columns per group: 256, or 512 with tailB
+  int per_group;           // tiles per group: fbands (x2 with tailB) + tailB
+  int ngroups;
+  int ntiles;              // 256-column tiles of a row (row pairs per row)
   float c;                 // log2(e) / T for the row pairs
   float2* part;            // [M][ntiles] row pairs, or null
   const int32_t* draft;    // gather: draft token of each row (linear layout), or null
@@ -186,23 +195,32 @@ struct GemmArgs {
 // flight, leaving the LDS and export counters unconstrained.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-constexpr int BM = 256, BN = 256, NSTAGE = 4;  // output tile and LDS stages
+constexpr int NSTAGE = 4;            // LDS stages
+constexpr int kGT = 512;             // threads per workgroup: two waves per SIMD
+constexpr int WTM = 128, WTN = 64;   // output tile of one wave
+template <int BM_, int BN_>
+struct TileShape {
+  static constexpr int BM = BM_, BN = BN_;
+};
+using ShapeFull = TileShape<256, 256>;  // full bands
+using ShapeTail = TileShape<128, 512>;  // a last band of at most 128 rows
+constexpr int kStageMax = (128 + 512) * BK;  // bf16 elements of the larger stage
 
-__global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(GemmArgs a) {
-  constexpr int WN = BN / 128, WM = BM / 128;
-  static_assert(WM * WN == 4, "four 128 x 128 wave tiles per workgroup");
-  constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per LDS stage: A block, then B block
-  constexpr int nA = BM / 64;            // 1 KB direct-to-LDS loads per wave per step (A)
-  constexpr int nB = BN / 64;            // idem (B)
+// One output tile of shape Shp at (m0, n0).
+template <class Shp>
+__device__ __attribute__((always_inline)) inline void gemm_tile(const GemmArgs& a, Shp, int m0,
+                                                                int n0, uint16_t* smem) {
+  constexpr int BM = Shp::BM, BN = Shp::BN;
+  constexpr int kWaves = kGT / 64;
+  constexpr int WN = BN / WTN, WM = BM / WTM;
+  static_assert(WM * WN == kWaves, "the wave tiles cover the output tile");
+  constexpr int NI = WTM / 32, NJ = WTN / 32;  // 32 x 32 MFMA blocks of a wave tile
+  constexpr int STAGE = kStageMax;             // bf16 elements per LDS stage: A block, then B block
+  static_assert((BM + BN) * BK <= STAGE, "a stage holds the tile's K step");
+  constexpr int nA = BM / 16 / kWaves;         // 1 KB direct-to-LDS loads per wave per step (A)
+  constexpr int nB = BN / 16 / kWaves;         // idem (B)
   constexpr int D = nA + nB;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[NSTAGE * STAGE];
-
-  const int ntile = a.mtiles * a.ntiles;
-  const int per_xcd = (int)(gridDim.x / kXcd);
-  const int tile = (int)(blockIdx.x % kXcd) * per_xcd + (int)(blockIdx.x / kXcd);
-  if (tile >= ntile) return;
-  const int tm = tile % a.mtiles, tn = tile / a.mtiles;
-  const int m0 = tm * BM, n0 = tn * BN;
+  constexpr int R = NI + 2 * NJ;               // fragment reads per wave per substep
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: LDS bases go to M0
   const int wm = wave / WN, wn = wave % WN;
@@ -283,11 +301,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(GemmArgs a) {
   using kWStep = std::integral_constant<bool, true>;
   using kAnyStep = std::integral_constant<bool, false>;
 
-  f32x16 acc[4][4];
+  f32x16 acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -301,32 +319,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(GemmArgs a) {
   // 16 (g % 2) + l % 16 at four consecutive contraction rows.  Byte offsets within the stage's B
   // block, per column block j (h and ks are immediate offsets).
   const int g = lane >> 4, q = lane & 15;
-  int bofs[4];
+  int bofs[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int k = 8 * (g >> 1) + (q >> 2);
-    const int chunk = wn * 16 + 4 * (j ^ (q >> 2)) + 2 * (g & 1) + ((q & 3) >> 1);
-    bofs[j] = k * BN * 2 + chunk * 16 + (q & 1) * 8;
+    const int n = wn * WTN + 32 * j + 16 * (g & 1) + 4 * (q & 3);
+    const int chunk = (n >> 3) ^ ((k & 3) << 2);
+    bofs[j] = k * BN * 2 + chunk * 16 + (n & 7) * 2;
   }
-  bf16x8 fa[2][4], fb[2][4];
-  auto fread = [&](int kt, int ks, bf16x8(&ra)[4], bf16x8(&rb)[4]) {
-    const uint16_t* As = smem + (kt % NSTAGE) * STAGE + (wm * 128) * BK + (ks ? fofs1 : fofs0);
+  bf16x8 fa[2][NI], fb[2][NJ];
+  auto fread = [&](int kt, int ks, bf16x8(&ra)[NI], bf16x8(&rb)[NJ]) {
+    const uint16_t* As = smem + (kt % NSTAGE) * STAGE + (wm * WTM) * BK + (ks ? fofs1 : fofs0);
     const char* Bs = reinterpret_cast<const char*>(smem + (kt % NSTAGE) * STAGE + BM * BK) +
                      ks * 16 * BN * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * BK);
+    for (int i = 0; i < NI; ++i) ra[i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * BK);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const bf16x4 lo = tr_read((const lds_bf16x4*)(Bs + bofs[j]));
       const bf16x4 hi = tr_read((const lds_bf16x4*)(Bs + bofs[j] + 4 * BN * 2));
       rb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
-  auto mfma16 = [&](const bf16x8(&ra)[4], const bf16x8(&rb)[4]) {
+  auto mfma_sub = [&](const bf16x8(&ra)[NI], const bf16x8(&rb)[NJ]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i], rb[j], acc[i][j], 0, 0, 0);
   };
 
@@ -344,27 +363,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(GemmArgs a) {
     __builtin_amdgcn_s_barrier();
     fread(kt, 1, fa[1], fb[1]);
     dma(kt + NSTAGE - 1, kW);
-    mfma16(fa[0], fb[0]);
+    mfma_sub(fa[0], fb[0]);
     fread(kt + 1, 0, fa[0], fb[0]);
-    mfma16(fa[1], fb[1]);
-    // issue order: the 12 fragment reads of substep 1 after the first 12 MFMAs, the step's loads
-    // after the next 4, then the reads of step kt+1 between the MFMAs of substep 1
+    mfma_sub(fa[1], fb[1]);
+    // issue order: the fragment reads of substep 1 between the MFMAs of substep 0; the step's
+    // loads and the reads of step kt+1 between the MFMAs of substep 1
 #pragma unroll
-    for (int k = 0; k < 12; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    for (int k = 0; k < NI * NJ; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+      if (k < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, D / 4, 0);  // VMEM read (direct-to-LDS)
+    for (int k = 0; k < NI * NJ; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+      if (k < D) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM read (to LDS)
+      if (k < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
     }
-#pragma unroll
-    for (int k = 0; k < 12; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   // steps whose look-ahead loads are W steps, then the last NSTAGE-1 steps of W and the LoRA steps
   const int kt_w = a.KT - (NSTAGE - 1);
@@ -375,40 +389,43 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(GemmArgs a) {
   __syncthreads();
 
   // ---- epilogue -------------------------------------------------------------------------------
-  // Element (i, j, v) of this lane sits at row m0 + wm*128 + i*32 + 8*(v/4) + 4*(lane/32) + v%4,
-  // column n0 + wn*128 + j*32 + lane%32.  One slice (i fixed: WM*32 rows) at a time goes through
-  // LDS; then TPR threads per row reduce 64 columns each to the segment's
+  // Element (i, j, v) of this lane sits at row m0 + wm*WTM + i*32 + 8*(v/4) + 4*(lane/32) + v%4,
+  // column n0 + wn*WTN + j*32 + lane%32.  One slice (i fixed: WM*32 rows) at a time goes through
+  // LDS; then TPR threads per row reduce COLS columns each to the segment's
   // (max, sum exp2((x - max) c)), combined over the row's segments in a fixed order.
-  constexpr int SR = WM * 32;        // rows per slice
-  constexpr int TPR = kThreads / SR;  // threads per row (4 or 8); each takes 64 columns
+  constexpr int SR = WM * 32;         // rows per slice
+  constexpr int TPR = kGT / SR;       // threads per row
+  constexpr int COLS = BN / TPR;      // columns per thread
   constexpr int SROW = BN + 4;
+  static_assert(SR * SROW * sizeof(float) <= NSTAGE * STAGE * sizeof(uint16_t),
+                "a slice fits in the stages' LDS");
   float* S = reinterpret_cast<float*>(smem);  // [SR][SROW]
   const float c = a.c;
   const int lr = t / TPR, qq = t % TPR;
   const int ncol = min(BN, a.N - n0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int rr = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        S[rr * SROW + wn * 128 + j * 32 + (lane & 31)] = acc[i][j][v];
+        S[rr * SROW + wn * WTN + j * 32 + (lane & 31)] = acc[i][j][v];
       }
     __syncthreads();
-    auto slice_row = [&](int sr) { return m0 + (sr >> 5) * 128 + i * 32 + (sr & 31); };
+    auto slice_row = [&](int sr) { return m0 + (sr >> 5) * WTM + i * 32 + (sr & 31); };
     const int m = slice_row(lr);
-    const int nvalid = ncol - qq * 64;  // columns of this segment inside the row (may be <= 0)
-    const float* src = S + lr * SROW + qq * 64;
-    float4 buf[16];
+    const int nvalid = ncol - qq * COLS;  // columns of this segment inside the row (may be <= 0)
+    const float* src = S + lr * SROW + qq * COLS;
+    float4 buf[COLS / 4];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) buf[k] = *reinterpret_cast<const float4*>(src + 4 * k);
+    for (int k = 0; k < COLS / 4; ++k) buf[k] = *reinterpret_cast<const float4*>(src + 4 * k);
     if (a.part) {
       // segment max and sum, four independent chains each (a finite floor: a segment past the
       // row's end gives (floor, 0)); the chains are combined in a fixed order
       float mq[4] = {kNegBig, kNegBig, kNegBig, kNegBig};
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < COLS / 4; ++k) {
         const float x[4] = {buf[k].x, buf[k].y, buf[k].z, buf[k].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -417,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(GemmArgs a) {
       const float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
       float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < COLS / 4; ++k) {
         const float x[4] = {buf[k].x, buf[k].y, buf[k].z, buf[k].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -425,13 +442,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(GemmArgs a) {
       }
       float sm = (sq[0] + sq[1]) + (sq[2] + sq[3]);
       float mxc = mx;
+      // one pair per 256 columns (the threads of one 256-column segment, fixed order)
+      constexpr int TPS = 256 / COLS;
 #pragma unroll
-      for (int off = 1; off < TPR; off <<= 1) {
+      for (int off = 1; off < TPS; off <<= 1) {
         const float m2 = __shfl_xor(mxc, off, 64);
         const float s2 = __shfl_xor(sm, off, 64);
         os_combine(mxc, sm, m2, s2, c);
       }
-      if (qq == 0 && m < a.M) a.part[(int64_t)m * a.ntiles + tn] = make_float2(mxc, sm);
+      const int seg = n0 / 256 + qq / TPS;
+      if (qq % TPS == 0 && m < a.M && seg < a.ntiles)
+        a.part[(int64_t)m * a.ntiles + seg] = make_float2(mxc, sm);
     }
     if (a.gath && m < a.M) {
       // the logit at this row's draft token, by the thread whose segment holds it
@@ -442,13 +463,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(GemmArgs a) {
       } else {
         d = a.draft[m - a.nP];
       }
-      const int o = d - (n0 + qq * 64);
-      if (d >= 0 && d < a.N && o >= 0 && o < 64) a.gath[m] = src[o];
+      const int o = d - (n0 + qq * COLS);
+      if (d >= 0 && d < a.N && o >= 0 && o < COLS) a.gath[m] = src[o];
     }
     if (a.out0) {
-      // logits: each wave stores SR/4 rows of the slice, 256 columns per instruction
-      for (int k = 0; k < SR / 4; ++k) {
-        const int sr = wave * (SR / 4) + k;
+      // logits: each wave stores SR / kWaves rows of the slice, 256 columns per instruction
+      for (int k = 0; k < SR / kWaves; ++k) {
+        const int sr = wave * (SR / kWaves) + k;
         const int mr = slice_row(sr);
         if (mr >= a.M) continue;
         float* dst = mr < a.split ? a.out0 + (int64_t)mr * a.N : a.out1 + (int64_t)(mr - a.split) * a.N;
@@ -470,7 +491,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_lmhead_gemm(GemmArgs a) {
   }
 }
 
-constexpr int kBM = BM, kBN = BN;
+
+__global__ __launch_bounds__(kGT, 1) void k_lmhead_gemm(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NSTAGE * kStageMax];
+  const int per_xcd = (int)(gridDim.x / kXcd);
+  const int tile = (int)(blockIdx.x % kXcd) * per_xcd + (int)(blockIdx.x / kXcd);
+  if (tile >= a.ngroups * a.per_group) return;
+  const int grp = tile / a.per_group, idx = tile - grp * a.per_group;
+  const bool tail = a.tailB && idx == a.per_group - 1;
+  int m0, n0;
+  if (tail) {
+    m0 = a.fbands * 256;
+    n0 = grp * a.gcols;
+  } else {
+    m0 = (idx % a.fbands) * 256;
+    n0 = grp * a.gcols + (idx / a.fbands) * 256;
+  }
+  if (n0 >= a.N) return;
+  if (tail)
+    gemm_tile(a, ShapeTail{}, m0, n0, smem);
+  else
+    gemm_tile(a, ShapeFull{}, m0, n0, smem);
+}
+
+constexpr int kBM = 256, kBN = 256;
 
 int lmhead_mpad(int rows) { return (rows + kBM - 1) / kBM * kBM; }
 
@@ -500,7 +544,13 @@ hipError_t run_gemm(const LMHeadArgs& a, const uint16_t* ablk, int rows, float2*
   g.r = a.r;
   g.KT = a.K / BK;
   g.KTX = (a.K + lmhead_kx(a.r)) / BK;
-  g.mtiles = g.Mpad / kBM;
+  g.fbands = rows / 256;
+  const int rem = rows - 256 * g.fbands;
+  g.tailB = rem > 0 && rem <= 128;
+  if (rem > 128) g.fbands += 1;  // a last band of more than 128 rows: a padded full band
+  g.gcols = g.tailB ? 512 : 256;
+  g.per_group = g.tailB ? 2 * g.fbands + 1 : g.fbands;
+  g.ngroups = (a.N + g.gcols - 1) / g.gcols;
   g.ntiles = (a.N + kBN - 1) / kBN;
   g.c = a.c;
   g.part = part;
@@ -511,10 +561,10 @@ hipError_t run_gemm(const LMHeadArgs& a, const uint16_t* ablk, int rows, float2*
   g.out0 = out0;
   g.out1 = out1;
   g.split = split;
-  const int ntile = g.mtiles * g.ntiles;
+  const int ntile = g.ngroups * g.per_group;
   const unsigned grid = (unsigned)((ntile + kXcd - 1) / kXcd * kXcd);
   timing_begin(name, stream);
-  hipLaunchKernelGGL(k_lmhead_gemm, dim3(grid), dim3(kThreads), 0, stream, g);
+  hipLaunchKernelGGL(k_lmhead_gemm, dim3(grid), dim3(kGT), 0, stream, g);
   timing_end(name, stream);
   return hipGetLastError();
 }
