@@ -54,7 +54,8 @@ typedef enum {
   PSISPEC_EDTYPE = -2,       /* unsupported element type */
   PSISPEC_EWORKSPACE = -3,   /* workspace missing, too small or misaligned */
   PSISPEC_EHIP = -4,         /* a HIP call or kernel launch failed */
-  PSISPEC_EUNSUPPORTED = -5  /* a mode that is not implemented */
+  PSISPEC_EUNSUPPORTED = -5, /* a mode that is not implemented */
+  PSISPEC_ESCRATCH = -6      /* sizes beyond the fixed scratch of the no-allocation entry point */
 } psispec_status;
 
 typedef enum { PSISPEC_F32 = 0, PSISPEC_BF16 = 1 } psispec_dtype;
@@ -108,6 +109,25 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
                                      int32_t* out_tokens, float* ratios, uint64_t* accept_mask,
                                      int32_t* status, void* workspace, size_t workspace_bytes,
                                      void* stream);
+
+/*
+ * Linear verify for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): psispec_verify_linear with the same
+ * arguments, outputs, determinism and errors, but no workspace argument.  Its scratch is a fixed
+ * 64 MiB array in device memory that the library holds on every GPU it runs on until the process
+ * ends; the call allocates nothing.  Sizes whose workspace (psispec_verify_linear_workspace)
+ * exceeds 64 MiB return PSISPEC_ESCRATCH and launch nothing (batch 256 fits at any B up to 64
+ * and V up to 262,144; batch 512 at B = 8, V = 151,936 does not).  Every call on one GPU uses the
+ * same array: calls that overlap on one GPU (two streams, two host threads) race and must be
+ * ordered by the caller.  Nothing in the array needs to start at zero; it keeps the last call's
+ * contents.  (While psispec_timing_enable is on, the library's timing hooks create HIP events.)
+ */
+psispec_status psispec_verify_linear_noalloc(const void* p_logits, const void* q_logits,
+                                             psispec_dtype dtype, const int32_t* draft_tokens,
+                                             int32_t batch, int32_t B, int32_t V,
+                                             const psispec_sampling* s, int32_t* accept_len,
+                                             int32_t* out_tokens, float* ratios,
+                                             uint64_t* accept_mask, int32_t* status, void* stream);
 
 /*
  * Tree verify ([alphalab] §"Linear 與 Tree sampler": several likely candidates per position,

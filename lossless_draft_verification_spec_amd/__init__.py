@@ -21,6 +21,7 @@ ST_NONFINITE, ST_BAD_TOKEN, ST_Q_ZERO, ST_RESID_ZERO, ST_BAD_PARENT = 1, 2, 4, 8
 ST_BAD_KEEP = 32
 
 EXPORTS = ("psispec_verify_linear_workspace", "psispec_verify_linear",
+           "psispec_verify_linear_noalloc",
            "psispec_verify_tree_workspace", "psispec_verify_tree", "psispec_lmhead_verify_workspace",
            "psispec_lmhead_verify", "psispec_sample_drafts_workspace", "psispec_sample_drafts",
            "psispec_kv_commit", "psispec_strerror", "psispec_timing_enable",
@@ -54,6 +55,9 @@ def lib():
         L.psispec_verify_linear_workspace.restype = sz
         L.psispec_verify_linear.argtypes = [P, P, i32, P, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
         L.psispec_verify_linear.restype = i32
+        L.psispec_verify_linear_noalloc.argtypes = [P, P, i32, P, i32, i32, i32, P, P, P, P, P, P,
+                                                    P]
+        L.psispec_verify_linear_noalloc.restype = i32
         L.psispec_verify_tree_workspace.argtypes = [i32, i32, i32, i32]
         L.psispec_verify_tree_workspace.restype = sz
         L.psispec_verify_tree.argtypes = [P, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P,
@@ -209,6 +213,36 @@ def psispec_verify_linear(p_logits: torch.Tensor, q_logits: torch.Tensor, draft_
         _ptr(out.get("accept_mask")), _ptr(out.get("status")), _ptr(workspace),
         workspace.numel(), _stream(stream))
     _check(rc, "psispec_verify_linear")
+    return out
+
+
+def psispec_verify_linear_noalloc(p_logits: torch.Tensor, q_logits: torch.Tensor,
+                                  draft_tokens: torch.Tensor, out: dict, temperature: float = 1.0,
+                                  top_p: float = 1.0, seed: int = 0, step: int = 0,
+                                  request_base: int = 0, flags: int = 0, stream=None) -> dict:
+    """psispec_verify_linear through the entry point that allocates nothing (its scratch is the
+    library's fixed 64 MiB device array): the caller passes the output tensors in `out`
+    (accept_len, out_tokens required; ratios, accept_mask, status optional)."""
+    if p_logits.dim() != 3 or q_logits.dim() != 3:
+        raise PsispecError("p_logits must be [batch][B+1][V] and q_logits [batch][B][V]")
+    batch, Bp1, V = p_logits.shape
+    B = Bp1 - 1
+    if tuple(q_logits.shape) != (batch, B, V) or q_logits.dtype != p_logits.dtype:
+        raise PsispecError("q_logits must be [batch][B][V] with the dtype of p_logits")
+    if tuple(draft_tokens.shape) != (batch, B) or draft_tokens.dtype != torch.int32:
+        raise PsispecError("draft_tokens must be int32 [batch][B]")
+    dt = _dtype_code(p_logits)
+    dev = p_logits.device
+    for name, t in (("p_logits", p_logits), ("q_logits", q_logits), ("draft_tokens", draft_tokens)):
+        _dev(t, name)
+        _same_dev(t, dev, name)
+    _check_linear_out(out, batch, B, dev)
+    s = _sampling(temperature, top_p, seed, step, request_base, flags)
+    rc = lib().psispec_verify_linear_noalloc(
+        _ptr(p_logits), _ptr(q_logits), dt, _ptr(draft_tokens), batch, B, V, ctypes.byref(s),
+        _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out.get("ratios")),
+        _ptr(out.get("accept_mask")), _ptr(out.get("status")), _stream(stream))
+    _check(rc, "psispec_verify_linear_noalloc")
     return out
 
 

@@ -340,6 +340,31 @@ psispec_status verify_tree_sampled(const void* p_logits, const void* q_logits, p
 
 }  // namespace
 
+namespace {
+
+// Scratch of psispec_verify_linear_noalloc: a fixed array in device memory (one copy per GPU
+// the library runs on, held until the process ends).  Host code uses only the device address
+// that hipGetSymbolAddress returns for it, looked up once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+void* noalloc_scratch() {
+  static std::mutex mu;
+  static std::vector<void*> per_device;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  if ((int)per_device.size() <= dev) per_device.resize(dev + 1, nullptr);
+  if (!per_device[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    per_device[dev] = ptr;
+  }
+  return per_device[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* psispec_strerror(psispec_status code) {
@@ -350,6 +375,8 @@ const char* psispec_strerror(psispec_status code) {
     case PSISPEC_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case PSISPEC_EHIP: return "HIP launch or runtime error";
     case PSISPEC_EUNSUPPORTED: return "mode not implemented";
+    case PSISPEC_ESCRATCH:
+      return "sizes need more scratch than the no-allocation entry point's fixed array holds";
   }
   return "unknown status";
 }
@@ -489,6 +516,26 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
   da.status = status;
   if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
   return PSISPEC_OK;
+}
+
+psispec_status psispec_verify_linear_noalloc(const void* p_logits, const void* q_logits,
+                                             psispec_dtype dtype, const int32_t* draft_tokens,
+                                             int32_t batch, int32_t B, int32_t V,
+                                             const psispec_sampling* s, int32_t* accept_len,
+                                             int32_t* out_tokens, float* ratios,
+                                             uint64_t* accept_mask, int32_t* status,
+                                             void* stream) {
+  if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return PSISPEC_EDTYPE;
+  if (batch < 0 || B < 1 || B > 64 || V < 1) return PSISPEC_EINVAL;
+  if (batch == 0) return sampling_ok(s) ? PSISPEC_OK : PSISPEC_EINVAL;
+  const size_t need = psispec_verify_linear_workspace(batch, B, V, dtype);
+  if (need == 0) return PSISPEC_EINVAL;
+  if (need > kNoAllocScratchBytes) return PSISPEC_ESCRATCH;
+  void* ws = noalloc_scratch();
+  if (!ws) return PSISPEC_EHIP;
+  return psispec_verify_linear(p_logits, q_logits, dtype, draft_tokens, batch, B, V, s,
+                               accept_len, out_tokens, ratios, accept_mask, status, ws,
+                               kNoAllocScratchBytes, stream);
 }
 
 psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, psispec_dtype dtype,
