@@ -224,8 +224,9 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
   for (int64_t base = blockIdx.x; base < items; base += stride * kThreads) {
     if (threadIdx.x == 0) s_cnt = 0;
     __syncthreads();
-    // index j runs chunk-major (node row j mod nP, chunk j / nP), so that one node's chunks land
-    // in different blocks whatever the grid size
+    // index j runs chunk-major (node row j mod nP, chunk j / nP): one node's chunks land in
+    // blocks (g + c nP) mod gridDim.x, distinct for all c < gridDim.x when gridDim.x is a prime
+    // that does not divide nP (the launcher picks such a grid)
     const int64_t j = base + (int64_t)threadIdx.x * stride;
     if (j < items) {
       const int64_t g = j % a.rs.nP;
@@ -560,11 +561,21 @@ hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype d
                                   hipStream_t stream) {
   int64_t blocks = a.rs.nP * (int64_t)a.nchunk_c;
   if (blocks == 0) return hipSuccess;
-  // a fixed grid loops over the work items: 2048 blocks at level 1 (every chunk of every node with
-  // two or more children when the level-0 split is refused), 509 from level 2 on (nodes with three
-  // or more children: fewer items, and a launch without work is cheaper)
-  if (level > 0 && blocks > 2048) blocks = 2048;
-  if (level >= 2 && blocks > 509) blocks = 509;
+  // a fixed grid loops over the work items: about 2048 blocks at level 1 (every chunk of every node
+  // with two or more children when the level-0 split is refused), about 509 from level 2 on (nodes
+  // with three or more children: fewer items, and a launch without work is cheaper).  The grid is
+  // a prime that does not divide nP, so that the chunks of one node go to different blocks.
+  if (level > 0) {
+    static const int64_t kGrid1[] = {2039, 2029, 2027}, kGrid2[] = {509, 503, 499};
+    const int64_t* cand = level == 1 ? kGrid1 : kGrid2;
+    int64_t grid = cand[0];
+    for (int i = 0; i < 3; ++i)
+      if (a.rs.nP % cand[i] != 0) {
+        grid = cand[i];
+        break;
+      }
+    if (blocks > grid) blocks = grid;
+  }
   const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
   const int vec_ok = ((size_t)a.V * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
                      ((uintptr_t)a.rs.q % 16) == 0;

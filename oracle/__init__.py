@@ -26,15 +26,22 @@ ST_NONFINITE, ST_BAD_TOKEN, ST_Q_ZERO, ST_RESID_ZERO, ST_BAD_PARENT = 1, 2, 4, 8
 ST_BAD_KEEP = 32
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (no fast-math, no FMA contraction) into an in-tree .so."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
+# A test may point the binding at another build of the same source (the sanitizer build).
+_ALT = os.environ.get("PSISPEC_ORACLE_LIB")
+
+
+def build(force: bool = True, out: str | None = None, checks: tuple = ()) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction) into an in-tree .so, or into
+    `out` with extra instrumentation flags `checks` (e.g. address and undefined-behaviour
+    sanitizers for the host-only test build)."""
+    target = out or _LIB
+    if force or not os.path.exists(target) or os.path.getmtime(target) < os.path.getmtime(_SRC):
+        tmp = target + ".tmp"
         subprocess.check_call(
             ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
-             "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+             "-Wall", "-Wextra", *checks, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, target)
+    return target
 
 
 _lib = None
@@ -43,9 +50,12 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        L = ctypes.CDLL(_LIB)
+        if _ALT:
+            L = ctypes.CDLL(_ALT)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, u32, u64, dbl = ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_double
         L.psispec_oracle_philox.argtypes = [u64, P, P]

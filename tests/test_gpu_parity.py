@@ -268,7 +268,7 @@ def test_c1_histogram_on_gpu():
     assert abs(mean - want) < 5 * se
 
 
-@pytest.mark.parametrize("name,nreq", [("c2", 64), ("ns", 24), ("c3", 12)])
+@pytest.mark.parametrize("name,nreq", [("c2", 64), ("ns", 64), ("c3", 32)])
 def test_full_size_linear(name, nreq):
     inp = workloads.make_linear(name, device=DEV, steps=2)
     pr = inp.preset

@@ -5,6 +5,8 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+
 from lossless_draft_verification_spec_amd import (ST_BAD_PARENT, ST_NONFINITE, psispec_verify_tree,
                                                   workloads)
 from parity import Tally, compare_tree, host_logits, oracle_tree_sampled_requests
@@ -148,3 +150,53 @@ def test_ratio_band_tokens():
     t = _compare(tin, steps=range(3), q=q)
     print(t)
     t.check()
+
+
+def test_chain_passes_over_several_grid_rounds():
+    """A call whose chain passes take more than one round of their fixed grids: 14,336 node rows x
+    38 chunks = 544,768 items (one round covers about 2048 x 256 items at level 1 and 509 x 256 from
+    level 2 on), nodes with 3 to 8 children (levels 1-7 have work), and in a few nodes' draft rows
+    more in-between tokens of the level-0 split than a chunk keeps, all in the row's last chunk, so
+    that level 1 recomputes chunks that only its second round reaches.  Sampled requests against the
+    oracle."""
+    from dataclasses import replace
+    pr = replace(workloads.PRESETS["c4s"], dtype=torch.float32, depth=8)
+    tin = workloads.make_tree_sampled(pr, device=DEV, batch=56, V=151936, N=255,
+                                      branching=(8, 4, 3, 3))
+    par = tin.parent.cpu().numpy()
+    V = tin.p.shape[2]
+    last0 = (V - 1) // 4096 * 4096  # first token of the last 4096-token chunk
+    picks = []
+    for r in (2, 30, 55):
+        kids = np.bincount(par[r] + 1, minlength=par.shape[1] + 1)
+        rows = [int(v) for v in np.nonzero(kids >= 2)[0][:3]]  # node rows with two or more children
+        for row in rows:
+            lp = tin.p[r, row, last0:].cpu()
+            picks.append((r, row, [last0 + int(x) for x in torch.argsort(lp)[:12]]))
+    q = tin.q
+    for r, row, xs in picks:
+        lp = tin.p[r, row].detach().cpu().double()
+        lq = q[r, row].detach().cpu().double().clone()
+        xs = torch.as_tensor(xs)
+        for _ in range(4):
+            Ep = torch.exp(lp - lp.max()).sum()
+            Eq = torch.exp(lq - lq.max()).sum()
+            lq[xs] = lp[xs] - lp.max() + lq.max() - torch.log(Ep / Eq)
+        q[r, row] = lq.to(torch.float32).to(DEV)
+    rows = [2, 30, 55]
+    tally = Tally()
+    for step in range(2):
+        out = psispec_verify_tree(tin.p, tin.parent, tin.node_tokens, 8, seed=tin.seed, step=step,
+                                  q_logits=q)
+        torch.cuda.synchronize()
+        g = {k: v.cpu().numpy() for k, v in out.items()}
+        outs = []
+        for r in rows:
+            outs.append(oracle.verify_tree_sampled(
+                host_logits(tin.p[r:r + 1]), host_logits(q[r:r + 1]), par[r:r + 1],
+                tin.node_tokens[r:r + 1].cpu().numpy(), 8, T=1.0, top_p=1.0, seed=tin.seed,
+                step=step, request_base=r))
+        o = {k: np.concatenate([x[k] for x in outs]) for k in outs[0]}
+        compare_tree(tally, g, o, rows, 1.0)
+    print(tally)
+    tally.check()
