@@ -276,8 +276,24 @@ psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, cons
 const char* psispec_strerror(psispec_status code);
 
 /*
- * Kernel timing (for benchmarks).  While enabled, every kernel launch of the library is bracketed
- * by HIP events recorded on the call's stream.  psispec_timing_read synchronises those events and
+ * Measured ceilings (for benchmarks; not steps of the verify).  psispec_peak_read reads every
+ * 16-byte word of `buf` (device, 16-byte aligned, `bytes` long; make it larger than the 256 MB
+ * last-level cache) once with nontemporal loads, each of `blocks` workgroups of 256 threads
+ * streaming its own contiguous segment, and writes one word per block to out[blocks]:
+ * bytes / kernel time is the sustained read bandwidth.  psispec_peak_mfma runs `iters` rounds of 16 independent v_mfma_f32_32x32x16_bf16 per
+ * wave in `blocks` workgroups of four waves, with no memory traffic, and writes one float per
+ * thread to out[blocks * 256]: blocks * 4 * iters * 16 * 32768 / kernel time is the bf16 matrix-core
+ * issue rate at the clock the chip holds under that load.  Both are asynchronous on `stream`;
+ * the kernels appear in the timing records as "peak_read" and "peak_mfma".
+ */
+psispec_status psispec_peak_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks,
+                                 void* stream);
+psispec_status psispec_peak_mfma(int64_t iters, float* out, int32_t blocks, void* stream);
+
+/*
+ * Kernel timing (for benchmarks).  While enabled, every kernel launch of the library records a
+ * start and a stop event through its own dispatch (hipExtLaunchKernelGGL) on the call's stream:
+ * the events measure the kernel itself, as a profiler's kernel trace does.  psispec_timing_read synchronises those events and
  * returns, per kernel name, the summed device milliseconds and the launch count since the last
  * enable; it returns the number of kernels written (at most max_kernels).  names receives
  * max_kernels fixed slots of 64 bytes (NUL-terminated).

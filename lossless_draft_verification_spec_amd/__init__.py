@@ -25,7 +25,7 @@ EXPORTS = ("psispec_verify_linear_workspace", "psispec_verify_linear",
            "psispec_verify_tree_workspace", "psispec_verify_tree", "psispec_lmhead_verify_workspace",
            "psispec_lmhead_verify", "psispec_sample_drafts_workspace", "psispec_sample_drafts",
            "psispec_kv_commit", "psispec_strerror", "psispec_timing_enable",
-           "psispec_timing_read")
+           "psispec_timing_read", "psispec_peak_read", "psispec_peak_mfma")
 
 
 class PsispecError(RuntimeError):
@@ -80,6 +80,10 @@ def lib():
         L.psispec_strerror.restype = ctypes.c_char_p
         L.psispec_timing_enable.argtypes = [i32]
         L.psispec_timing_enable.restype = i32
+        L.psispec_peak_read.argtypes = [P, sz, P, i32, P]
+        L.psispec_peak_read.restype = i32
+        L.psispec_peak_mfma.argtypes = [ctypes.c_int64, P, i32, P]
+        L.psispec_peak_mfma.restype = i32
         L.psispec_timing_read.argtypes = [P, P, P, i32]
         L.psispec_timing_read.restype = i32
         _lib = L
@@ -477,6 +481,24 @@ def psispec_kv_commit(kv: torch.Tensor, blk: int, n_keep: torch.Tensor, length: 
                                  _stream(stream))
     _check(rc, "psispec_kv_commit")
     return status
+
+
+def peak_read(buf: torch.Tensor, out: torch.Tensor, blocks: int, stream=None):
+    """Read every 16-byte word of `buf` once (measured HBM read ceiling); out: uint32/int32 [blocks]."""
+    _dev(buf, "buf")
+    _dev(out, "out")
+    _check(lib().psispec_peak_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                   int(blocks), _stream(stream)), "psispec_peak_read")
+
+
+def peak_mfma(iters: int, out: torch.Tensor, blocks: int, stream=None):
+    """`iters` rounds of 16 bf16 MFMAs per wave in `blocks` four-wave workgroups (measured MFMA
+    issue ceiling); out: float32 [blocks * 256]."""
+    _dev(out, "out")
+    if out.numel() < blocks * 256 or out.dtype != torch.float32:
+        raise PsispecError("out must be float32 with blocks * 256 elements")
+    _check(lib().psispec_peak_mfma(int(iters), _ptr(out), int(blocks), _stream(stream)),
+           "psispec_peak_mfma")
 
 
 def timing_enable(on: bool = True):

@@ -165,7 +165,6 @@ struct Timing {
   std::vector<std::string> names;
   std::vector<double> total_ms;
   std::vector<int> launches;
-  std::vector<std::pair<std::string, hipEvent_t>> open;  // begun, not yet ended
 };
 
 Timing& timing() {
@@ -208,28 +207,25 @@ void drain(Timing& t) {
 
 }  // namespace
 
-void timing_begin(const char* name, hipStream_t stream) {
+bool timing_take(hipEvent_t* start, hipEvent_t* stop) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
-  if (!t.on) return;
-  hipEvent_t e = take_event(t);
-  if (!e || hipEventRecord(e, stream) != hipSuccess) return;
-  t.open.emplace_back(name, e);
+  if (!t.on) return false;
+  *start = take_event(t);
+  *stop = take_event(t);
+  if (!*start || !*stop) {
+    if (*start) t.pool.push_back(*start);
+    if (*stop) t.pool.push_back(*stop);
+    *start = *stop = nullptr;
+    return false;
+  }
+  return true;
 }
 
-void timing_end(const char* name, hipStream_t stream) {
+void timing_push(const char* name, hipEvent_t start, hipEvent_t stop) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
-  if (!t.on) return;
-  for (size_t i = t.open.size(); i-- > 0;) {
-    if (t.open[i].first == name) {
-      hipEvent_t e = take_event(t);
-      if (e && hipEventRecord(e, stream) == hipSuccess)
-        t.pending.push_back(TimedLaunch{name, t.open[i].second, e});
-      t.open.erase(t.open.begin() + (long)i);
-      break;
-    }
-  }
+  t.pending.push_back(TimedLaunch{name, start, stop});
   if (t.pending.size() > 4096) drain(t);
 }
 
@@ -381,6 +377,21 @@ const char* psispec_strerror(psispec_status code) {
   return "unknown status";
 }
 
+psispec_status psispec_peak_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks,
+                                 void* stream) {
+  if (!buf || !out || blocks < 1 || bytes < 16 || ((uintptr_t)buf % 16) != 0) return PSISPEC_EINVAL;
+  if (launch_peak_read(buf, bytes, out, blocks, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PSISPEC_EHIP;
+  return PSISPEC_OK;
+}
+
+psispec_status psispec_peak_mfma(int64_t iters, float* out, int32_t blocks, void* stream) {
+  if (!out || blocks < 1 || iters < 1) return PSISPEC_EINVAL;
+  if (launch_peak_mfma(iters, out, blocks, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PSISPEC_EHIP;
+  return PSISPEC_OK;
+}
+
 psispec_status psispec_timing_enable(int32_t on) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
@@ -389,7 +400,6 @@ psispec_status psispec_timing_enable(int32_t on) {
   t.names.clear();
   t.total_ms.clear();
   t.launches.clear();
-  t.open.clear();
   return PSISPEC_OK;
 }
 

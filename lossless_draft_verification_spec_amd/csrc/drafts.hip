@@ -280,35 +280,35 @@ hipError_t launch_draft_bounded(const DraftArgs& a, psispec_dtype dtype, hipStre
   const int vec_ok = ((size_t)a.V * es) % 16 == 0 && ((size_t)a.rs.pstride * es) % 16 == 0 &&
                      ((uintptr_t)a.rs.p % 16) == 0 && ((uintptr_t)a.rs.q % 16) == 0;
   const dim3 grid((unsigned)(jobs * nblk)), block(kThreads);
-  timing_begin("draft_bounds", stream);
   if (dtype == PSISPEC_BF16) {
     if (a.use_topp)
-      hipLaunchKernelGGL((k_draft_bounds<bf16_t, true>), grid, block, 0, stream, a, nblk, vec_ok);
+      PSISPEC_LAUNCH("draft_bounds", (k_draft_bounds<bf16_t, true>), grid, block, 0, stream, a,
+                     nblk, vec_ok);
     else
-      hipLaunchKernelGGL((k_draft_bounds<bf16_t, false>), grid, block, 0, stream, a, nblk, vec_ok);
+      PSISPEC_LAUNCH("draft_bounds", (k_draft_bounds<bf16_t, false>), grid, block, 0, stream, a,
+                     nblk, vec_ok);
   } else {
     if (a.use_topp)
-      hipLaunchKernelGGL((k_draft_bounds<float, true>), grid, block, 0, stream, a, nblk, vec_ok);
+      PSISPEC_LAUNCH("draft_bounds", (k_draft_bounds<float, true>), grid, block, 0, stream, a, nblk,
+                     vec_ok);
     else
-      hipLaunchKernelGGL((k_draft_bounds<float, false>), grid, block, 0, stream, a, nblk, vec_ok);
+      PSISPEC_LAUNCH("draft_bounds", (k_draft_bounds<float, false>), grid, block, 0, stream, a,
+                     nblk, vec_ok);
   }
-  timing_end("draft_bounds", stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 sgrid((unsigned)jobs);
-  timing_begin("draft_select", stream);
   if (dtype == PSISPEC_BF16) {
     if (a.use_topp)
-      hipLaunchKernelGGL((k_draft_select<bf16_t, true>), sgrid, block, 0, stream, a);
+      PSISPEC_LAUNCH("draft_select", (k_draft_select<bf16_t, true>), sgrid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((k_draft_select<bf16_t, false>), sgrid, block, 0, stream, a);
+      PSISPEC_LAUNCH("draft_select", (k_draft_select<bf16_t, false>), sgrid, block, 0, stream, a);
   } else {
     if (a.use_topp)
-      hipLaunchKernelGGL((k_draft_select<float, true>), sgrid, block, 0, stream, a);
+      PSISPEC_LAUNCH("draft_select", (k_draft_select<float, true>), sgrid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((k_draft_select<float, false>), sgrid, block, 0, stream, a);
+      PSISPEC_LAUNCH("draft_select", (k_draft_select<float, false>), sgrid, block, 0, stream, a);
   }
-  timing_end("draft_select", stream);
   return hipGetLastError();
 }
 
@@ -317,10 +317,8 @@ hipError_t launch_draft_rows(const RowSet& rs, int batch, int B, int first_from_
                              DrawDesc* desc, hipStream_t stream) {
   const int64_t jobs = (int64_t)batch * B;
   if (jobs == 0) return hipSuccess;
-  timing_begin("draft_rows", stream);
-  hipLaunchKernelGGL(k_draft_rows, dim3((unsigned)jobs), dim3(64), 0, stream, rs, B,
-                     first_from_target, part, nchunk, c, rowstat, desc);
-  timing_end("draft_rows", stream);
+  PSISPEC_LAUNCH("draft_rows", k_draft_rows, dim3((unsigned)jobs), dim3(64), 0, stream, rs, B,
+                 first_from_target, part, nchunk, c, rowstat, desc);
   return hipGetLastError();
 }
 

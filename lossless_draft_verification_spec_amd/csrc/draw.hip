@@ -83,22 +83,18 @@ hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t strea
   const int vec_ok = ((size_t)a.V * es) % 16 == 0 &&
                      ((size_t)a.rs.pstride * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
                      ((uintptr_t)a.rs.q % 16) == 0;
-  timing_begin("draw_pass", stream);
   const bool bf = dtype == PSISPEC_BF16, tp = a.use_topp, li = a.list != nullptr;
   auto kern = bf ? (tp ? (li ? k_draw_pass<bf16_t, true, true> : k_draw_pass<bf16_t, true, false>)
                        : (li ? k_draw_pass<bf16_t, false, true> : k_draw_pass<bf16_t, false, false>))
                  : (tp ? (li ? k_draw_pass<float, true, true> : k_draw_pass<float, true, false>)
                        : (li ? k_draw_pass<float, false, true> : k_draw_pass<float, false, false>));
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, a, vec_ok);
-  timing_end("draw_pass", stream);
+  PSISPEC_LAUNCH("draw_pass", kern, dim3(grid), dim3(kThreads), 0, stream, a, vec_ok);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  timing_begin("draw_select", stream);
   if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL(k_draw_select<bf16_t>, dim3(sgrid), dim3(kThreads), 0, stream, a);
+    PSISPEC_LAUNCH("draw_select", k_draw_select<bf16_t>, dim3(sgrid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_draw_select<float>, dim3(sgrid), dim3(kThreads), 0, stream, a);
-  timing_end("draw_select", stream);
+    PSISPEC_LAUNCH("draw_select", k_draw_select<float>, dim3(sgrid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

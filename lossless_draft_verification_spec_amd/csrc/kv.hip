@@ -103,15 +103,11 @@ __global__ __launch_bounds__(64) void k_kv_len(KvArgs a) {
 hipError_t launch_kv_commit(const KvArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   const int ntiles = (int)((a.row_bytes + kKvTile - 1) / kKvTile);
-  timing_begin("kv_commit", stream);
-  hipLaunchKernelGGL(k_kv_commit, dim3((unsigned)((int64_t)a.batch * ntiles)), dim3(kKvThreads), 0,
-                     stream, a, ntiles);
-  timing_end("kv_commit", stream);
+  PSISPEC_LAUNCH("kv_commit", k_kv_commit, dim3((unsigned)((int64_t)a.batch * ntiles)),
+                 dim3(kKvThreads), 0, stream, a, ntiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  timing_begin("kv_len", stream);
-  hipLaunchKernelGGL(k_kv_len, dim3((unsigned)a.batch), dim3(64), 0, stream, a);
-  timing_end("kv_len", stream);
+  PSISPEC_LAUNCH("kv_len", k_kv_len, dim3((unsigned)a.batch), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // launch.h -- host-side launchers of the kernels (one per .hip translation unit).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -9,9 +10,20 @@
 
 namespace psispec {
 
-// Kernel timing hooks (api.cpp): bracket a launch with events when timing is enabled.
-void timing_begin(const char* name, hipStream_t stream);
-void timing_end(const char* name, hipStream_t stream);
+// Kernel timing (api.hip).  While timing is enabled, timing_take hands out two events and
+// timing_push files them under a kernel name; PSISPEC_LAUNCH launches through
+// hipExtLaunchKernelGGL, whose dispatch records the events at the kernel's own start and end.
+bool timing_take(hipEvent_t* start, hipEvent_t* stop);
+void timing_push(const char* name, hipEvent_t start, hipEvent_t stop);
+
+#define PSISPEC_LAUNCH(name, kernel, grid, block, shm, stream, ...)                           \
+  do {                                                                                         \
+    hipEvent_t psispec_e0_ = nullptr, psispec_e1_ = nullptr;                                   \
+    const bool psispec_on_ = ::psispec::timing_take(&psispec_e0_, &psispec_e1_);              \
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, stream, psispec_e0_, psispec_e1_, 0,       \
+                          __VA_ARGS__);                                                        \
+    if (psispec_on_) ::psispec::timing_push(name, psispec_e0_, psispec_e1_);                   \
+  } while (0)
 
 // rows.hip
 hipError_t launch_rowstats(const RowSet& rs, psispec_dtype dtype, int nchunk, int chunk_elems,
@@ -230,5 +242,10 @@ hipError_t launch_lmhead_main(const LMHeadArgs& a, uint16_t* ablk, const int32_t
 hipError_t launch_lmhead_rows(const LMHeadArgs& a, uint16_t* ablk, int batch, const DrawDesc* desc,
                               const RowStat* rowstat, DrawDesc* desc2, RowStat* rowstat2,
                               float* out, hipStream_t stream);
+
+// peak.hip -- measured ceilings (read bandwidth, bf16 MFMA issue rate)
+hipError_t launch_peak_read(const void* buf, size_t bytes, uint32_t* out, int blocks,
+                            hipStream_t stream);
+hipError_t launch_peak_mfma(int64_t iters, float* out, int blocks, hipStream_t stream);
 
 }  // namespace psispec

@@ -35,21 +35,17 @@ hipError_t launch_combine_rows(const RowSet& rs, const float2* part, int nchunk,
                                RowStat* rowstat, hipStream_t stream) {
   const int64_t rows = rs.nP + rs.nQ;
   if (rows == 0) return hipSuccess;
-  timing_begin("combine_rows", stream);
-  hipLaunchKernelGGL(k_combine_rows, dim3((unsigned)rows), dim3(64), 0, stream, rs, part, nchunk, c,
-                     rowstat);
-  timing_end("combine_rows", stream);
+  PSISPEC_LAUNCH("combine_rows", k_combine_rows, dim3((unsigned)rows), dim3(64), 0, stream, rs,
+                 part, nchunk, c, rowstat);
   return hipGetLastError();
 }
 
 hipError_t launch_decide_linear(const LinearArgs& a, psispec_dtype dtype, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  timing_begin("decide_linear", stream);
   if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL(k_decide_linear<bf16_t>, dim3(a.batch), dim3(64), 0, stream, a);
+    PSISPEC_LAUNCH("decide_linear", k_decide_linear<bf16_t>, dim3(a.batch), dim3(64), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_decide_linear<float>, dim3(a.batch), dim3(64), 0, stream, a);
-  timing_end("decide_linear", stream);
+    PSISPEC_LAUNCH("decide_linear", k_decide_linear<float>, dim3(a.batch), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -68,10 +68,10 @@ __device__ inline float bf16_f(uint16_t b) { return __uint_as_float((uint32_t)b 
 // Row m of the staged A operand ([KTX][Mpad][32], KTX = (K + kx) / 32): the hidden state of source
 // row src (h_ar row src for src < nP, h_dr row src - nP after; zeros for src < 0), then the extra
 // contraction columns: zeros for the AR rows; for a draft row, t_j = s sum_h h[h] A[h][j] (fp64
-// sum) stored as bf16 t_hi (columns K..K+r-1) and t_lo = t - t_hi (columns K+r..K+2r-1), zero up to
-// K + kx.  Source rows: m itself (m < nP + nQ), or with a draw list the stopping rows of request
-// m / 2 (row 2r = p row of the draw, 2r + 1 = its q row); that form also rewrites the draw's
-// descriptor and row statistics for the recomputed rows (row index 2r and 2r + 1).
+// sum, rounded to fp32) stored as bf16 t_hi (columns K..K+r-1) and t_lo = t - t_hi (columns
+// K+r..K+2r-1), zero up to K + kx.  Source rows: m itself (m < nP + nQ), or with a draw list the
+// stopping rows of request m / 2 (row 2r = p row of the draw, 2r + 1 = its q row); that form also
+// rewrites the draw's descriptor and row statistics for the recomputed rows (2r and 2r + 1).
 struct BuildArgs {
   const uint16_t* h_ar;
   const uint16_t* h_dr;
@@ -118,30 +118,72 @@ __global__ __launch_bounds__(kThreads) void k_build_a(BuildArgs a) {
   }
   if (a.kx == 0) return;
   uint16_t* ext = dst + (a.K / BK) * kstride;  // the extra columns: one or more K steps
-  auto put = [&](int j, uint16_t v) { ext[(j / BK) * kstride + (j % BK)] = v; };
   const bool draft_row = src >= a.nP;
-  for (int j = threadIdx.x + (draft_row ? 2 * a.r : 0); j < a.kx; j += kThreads) put(j, 0);
-  if (!draft_row) return;
+  for (int j = threadIdx.x + (draft_row ? 2 * a.r : 0); j < a.kx; j += kThreads)
+    ext[(j / BK) * kstride + (j % BK)] = 0;
+}
+
+// The LoRA columns of the draft rows of the staged A operand (rows as k_build_a takes them; other
+// rows return at once).
+__global__ __launch_bounds__(kThreads) void k_build_lora(BuildArgs a) {
+  const int m = blockIdx.x;
+  if (m >= a.nrows) return;
+  int src = m;
+  if (a.desc) {
+    const DrawDesc d = a.desc[m >> 1];
+    src = (m & 1) ? d.qrow : d.prow;
+  }
+  if (src < a.nP) return;  // an AR row (or none): its extra columns are zero
+  const int64_t kstride = (int64_t)a.Mpad * BK;
+  uint16_t* ext = a.ablk + (int64_t)m * BK + (a.K / BK) * kstride;
+  auto put = [&](int j, uint16_t v) { ext[(j / BK) * kstride + (j % BK)] = v; };
+  const uint16_t* x = a.h_dr + (int64_t)(src - a.nP) * a.K;
+  // t_j = s sum_h x[h] A[h][j], 16 ranks at a time: each thread takes 8 consecutive h per round
+  // (x from one 16-byte word, A's 8 rows loaded together), summed in h order in fp64; the
+  // threads' sums are reduced in a fixed order (wave butterflies, then the 4 waves).
   __shared__ double s_acc[kThreads / 64][16];
+  const bool vec = (a.r % 8) == 0 && ((uintptr_t)a.lora_a % 16) == 0;
   for (int j0 = 0; j0 < a.r; j0 += 16) {
     const int nj = min(16, a.r - j0);
     double acc[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.0;
-    for (int c = threadIdx.x; c < nc; c += kThreads) {
-      const u32x4 xw = *reinterpret_cast<const u32x4*>(x + 8 * c);
-      double xv[8];
+    for (int h0 = 8 * threadIdx.x; h0 < a.K; h0 += 8 * kThreads) {
+      const u32x4 xw = *reinterpret_cast<const u32x4*>(x + h0);
+      u32x4 raw[8][2];
+      if (vec) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xv[2 * e] = (double)__uint_as_float(xw[e] << 16);
-        xv[2 * e + 1] = (double)__uint_as_float(xw[e] & 0xffff0000u);
+        for (int k = 0; k < 8; ++k) {
+          const uint16_t* row = a.lora_a + (int64_t)(h0 + k) * a.r + j0;
+#pragma unroll
+          for (int w = 0; w < 2; ++w)
+            raw[k][w] = 8 * w < nj ? *reinterpret_cast<const u32x4*>(row + 8 * w)
+                                   : u32x4{0u, 0u, 0u, 0u};
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int w = 0; w < 2; ++w)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int q0 = 8 * w + 2 * e;
+              const uint16_t* row = a.lora_a + (int64_t)(h0 + k) * a.r + j0;
+              const uint32_t lo = q0 < nj ? row[q0] : 0u, hi = q0 + 1 < nj ? row[q0 + 1] : 0u;
+              raw[k][w][e] = lo | (hi << 16);
+            }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t* arow = a.lora_a + (int64_t)(8 * c + e) * a.r + j0;
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t xk = xw[k >> 1];
+        const double xd = (double)__uint_as_float((k & 1) ? (xk & 0xffff0000u) : (xk << 16));
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (q < nj) acc[q] += xv[e] * (double)bf16_f(arow[q]);
+        for (int w = 0; w < 2; ++w)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[8 * w + 2 * e] += xd * (double)__uint_as_float(raw[k][w][e] << 16);
+            acc[8 * w + 2 * e + 1] += xd * (double)__uint_as_float(raw[k][w][e] & 0xffff0000u);
+          }
       }
     }
 #pragma unroll
@@ -157,11 +199,11 @@ __global__ __launch_bounds__(kThreads) void k_build_a(BuildArgs a) {
     if (threadIdx.x < nj) {
       double tot = 0.0;
       for (int w = 0; w < kThreads / 64; ++w) tot += s_acc[w][threadIdx.x];
-      const int j = j0 + threadIdx.x;
+      const int jj = j0 + threadIdx.x;
       const float tf = (float)(tot * (double)a.lora_scale);
       const uint16_t hi = bf16_rne(tf);
-      put(j, hi);
-      put(a.r + j, bf16_rne(tf - bf16_f(hi)));
+      put(jj, hi);
+      put(a.r + jj, bf16_rne(tf - bf16_f(hi)));
     }
     __syncthreads();
   }
@@ -563,9 +605,7 @@ hipError_t run_gemm(const LMHeadArgs& a, const uint16_t* ablk, int rows, float2*
   g.split = split;
   const int ntile = g.ngroups * g.per_group;
   const unsigned grid = (unsigned)((ntile + kXcd - 1) / kXcd * kXcd);
-  timing_begin(name, stream);
-  hipLaunchKernelGGL(k_lmhead_gemm, dim3(grid), dim3(kGT), 0, stream, g);
-  timing_end(name, stream);
+  PSISPEC_LAUNCH(name, k_lmhead_gemm, dim3(grid), dim3(kGT), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -589,9 +629,10 @@ hipError_t launch_lmhead_main(const LMHeadArgs& a, uint16_t* ablk, const int32_t
   b.Mpad = lmhead_mpad(M);
   b.nrows = M;
   b.ablk = ablk;
-  timing_begin("build_a", stream);
-  hipLaunchKernelGGL(k_build_a, dim3((unsigned)b.Mpad), dim3(kThreads), 0, stream, b);
-  timing_end("build_a", stream);
+  PSISPEC_LAUNCH("build_a", k_build_a, dim3((unsigned)b.Mpad), dim3(kThreads), 0, stream, b);
+  if (b.kx > 0 && b.r > 0)
+    PSISPEC_LAUNCH("build_a_lora", k_build_lora, dim3((unsigned)b.nrows), dim3(kThreads), 0,
+                   stream, b);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return run_gemm(a, ablk, M, part, draft, B, gath, out_p, out_q, a.nP, stream, "lmhead_gemm");
@@ -619,9 +660,10 @@ hipError_t launch_lmhead_rows(const LMHeadArgs& a, uint16_t* ablk, int batch, co
   b.desc2 = desc2;
   b.rowstat2 = rowstat2;
   b.ablk = ablk;
-  timing_begin("build_rows", stream);
-  hipLaunchKernelGGL(k_build_a, dim3((unsigned)b.Mpad), dim3(kThreads), 0, stream, b);
-  timing_end("build_rows", stream);
+  PSISPEC_LAUNCH("build_rows", k_build_a, dim3((unsigned)b.Mpad), dim3(kThreads), 0, stream, b);
+  if (b.kx > 0 && b.r > 0)
+    PSISPEC_LAUNCH("build_rows_lora", k_build_lora, dim3((unsigned)b.nrows), dim3(kThreads), 0,
+                   stream, b);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return run_gemm(a, ablk, rows, nullptr, nullptr, 0, nullptr, out, out, rows, stream,

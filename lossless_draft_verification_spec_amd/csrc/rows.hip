@@ -32,14 +32,12 @@ hipError_t launch_rowstats(const RowSet& rs, psispec_dtype dtype, int nchunk, in
   const int vec_ok = ((size_t)rs.V * es) % 16 == 0 && ((size_t)rs.pstride * es) % 16 == 0 &&
                      ((uintptr_t)rs.p % 16) == 0 &&
                      ((uintptr_t)rs.q % 16) == 0 && (chunk_elems % 8) == 0;
-  timing_begin("rowstats", stream);
   if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL((k_rowstats<bf16_t, 8>), dim3((unsigned)tasks), dim3(kThreads), 0, stream,
-                       rs, nchunk, chunk_elems, c, part, vec_ok);
+    PSISPEC_LAUNCH("rowstats", (k_rowstats<bf16_t, 8>), dim3((unsigned)tasks), dim3(kThreads), 0,
+                   stream, rs, nchunk, chunk_elems, c, part, vec_ok);
   else
-    hipLaunchKernelGGL((k_rowstats<float, 8>), dim3((unsigned)tasks), dim3(kThreads), 0, stream,
-                       rs, nchunk, chunk_elems, c, part, vec_ok);
-  timing_end("rowstats", stream);
+    PSISPEC_LAUNCH("rowstats", (k_rowstats<float, 8>), dim3((unsigned)tasks), dim3(kThreads), 0,
+                   stream, rs, nchunk, chunk_elems, c, part, vec_ok);
   return hipGetLastError();
 }
 

@@ -546,14 +546,12 @@ hipError_t launch_topp(const RowSet& rs, psispec_dtype dtype, int nchunk, float 
   const int vec_ok = ((size_t)rs.V * es) % 16 == 0 && ((size_t)rs.pstride * es) % 16 == 0 &&
                      ((uintptr_t)rs.p % 16) == 0 &&
                      ((uintptr_t)rs.q % 16) == 0;
-  timing_begin("topp", stream);
   if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL(k_topp<bf16_t>, dim3((unsigned)rows), dim3(kThreads), 0, stream, rs, nchunk,
-                       c, top_p, (float)pmin, part, topp, rowstat, vec_ok);
+    PSISPEC_LAUNCH("topp", k_topp<bf16_t>, dim3((unsigned)rows), dim3(kThreads), 0, stream, rs,
+                   nchunk, c, top_p, (float)pmin, part, topp, rowstat, vec_ok);
   else
-    hipLaunchKernelGGL(k_topp<float>, dim3((unsigned)rows), dim3(kThreads), 0, stream, rs, nchunk,
-                       c, top_p, (float)pmin, part, topp, rowstat, vec_ok);
-  timing_end("topp", stream);
+    PSISPEC_LAUNCH("topp", k_topp<float>, dim3((unsigned)rows), dim3(kThreads), 0, stream, rs,
+                   nchunk, c, top_p, (float)pmin, part, topp, rowstat, vec_ok);
   return hipGetLastError();
 }
 
@@ -565,10 +563,8 @@ hipError_t launch_rowstats_topp(const RowSet& rs, float c, double top_p, float2*
   if (!(pmin >= 1e-30)) return hipErrorInvalidValue;
   const int vec_ok = ((size_t)rs.V * 2) % 16 == 0 && ((size_t)rs.pstride * 2) % 16 == 0 &&
                      ((uintptr_t)rs.p % 16) == 0 && ((uintptr_t)rs.q % 16) == 0;
-  timing_begin("rowstats_topp", stream);
-  hipLaunchKernelGGL(k_rowstats_topp, dim3((unsigned)rows), dim3(kThreads), 0, stream, rs, c, top_p,
-                     (float)pmin, part, topp, vec_ok);
-  timing_end("rowstats_topp", stream);
+  PSISPEC_LAUNCH("rowstats_topp", k_rowstats_topp, dim3((unsigned)rows), dim3(kThreads), 0, stream,
+                 rs, c, top_p, (float)pmin, part, topp, vec_ok);
   return hipGetLastError();
 }
 

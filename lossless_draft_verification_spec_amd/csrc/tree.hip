@@ -251,12 +251,10 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
 
 hipError_t launch_decide_tree(const TreeArgs& a, psispec_dtype dtype, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  timing_begin("decide_tree", stream);
   if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL(k_decide_tree<bf16_t>, dim3(a.batch), dim3(64), 0, stream, a);
+    PSISPEC_LAUNCH("decide_tree", k_decide_tree<bf16_t>, dim3(a.batch), dim3(64), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_decide_tree<float>, dim3(a.batch), dim3(64), 0, stream, a);
-  timing_end("decide_tree", stream);
+    PSISPEC_LAUNCH("decide_tree", k_decide_tree<float>, dim3(a.batch), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -540,20 +540,19 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
 
 hipError_t launch_tree_children(const TreeQArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  timing_begin("tree_children", stream);
-  hipLaunchKernelGGL(k_tree_children, dim3((unsigned)a.batch), dim3(256), 0, stream, a);
-  timing_end("tree_children", stream);
+  PSISPEC_LAUNCH("tree_children", k_tree_children, dim3((unsigned)a.batch), dim3(256), 0, stream,
+                 a);
   return hipGetLastError();
 }
 
 hipError_t launch_tree_resolve(const TreeQArgs& a, psispec_dtype dtype, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  timing_begin("tree_resolve", stream);
   if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL(k_tree_resolve<bf16_t>, dim3((unsigned)a.rs.nP), dim3(64), 0, stream, a);
+    PSISPEC_LAUNCH("tree_resolve", k_tree_resolve<bf16_t>, dim3((unsigned)a.rs.nP), dim3(64), 0,
+                   stream, a);
   else
-    hipLaunchKernelGGL(k_tree_resolve<float>, dim3((unsigned)a.rs.nP), dim3(64), 0, stream, a);
-  timing_end("tree_resolve", stream);
+    PSISPEC_LAUNCH("tree_resolve", k_tree_resolve<float>, dim3((unsigned)a.rs.nP), dim3(64), 0,
+                   stream, a);
   return hipGetLastError();
 }
 
@@ -579,27 +578,25 @@ hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype d
   const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
   const int vec_ok = ((size_t)a.V * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
                      ((uintptr_t)a.rs.q % 16) == 0;
-  timing_begin("tree_chain", stream);
   auto kern = dtype == PSISPEC_BF16 ? (level == 0 ? k_tree_chain<bf16_t, true> : k_tree_chain<bf16_t, false>)
                                     : (level == 0 ? k_tree_chain<float, true> : k_tree_chain<float, false>);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, level, vec_ok);
-  timing_end("tree_chain", stream);
+  PSISPEC_LAUNCH("tree_chain", kern, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, level,
+                 vec_ok);
   return hipGetLastError();
 }
 
 hipError_t launch_decide_tree_sampled(const TreeQArgs& a, psispec_dtype dtype, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  timing_begin("tree_chain_final", stream);
-  hipLaunchKernelGGL(k_tree_chain_final, dim3((unsigned)a.rs.nP), dim3(64), 0, stream, a);
-  timing_end("tree_chain_final", stream);
+  PSISPEC_LAUNCH("tree_chain_final", k_tree_chain_final, dim3((unsigned)a.rs.nP), dim3(64), 0,
+                 stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  timing_begin("decide_tree_sampled", stream);
   if (dtype == PSISPEC_BF16)
-    hipLaunchKernelGGL(k_decide_tree_sampled<bf16_t>, dim3(a.batch), dim3(64), 0, stream, a);
+    PSISPEC_LAUNCH("decide_tree_sampled", k_decide_tree_sampled<bf16_t>, dim3(a.batch), dim3(64), 0,
+                   stream, a);
   else
-    hipLaunchKernelGGL(k_decide_tree_sampled<float>, dim3(a.batch), dim3(64), 0, stream, a);
-  timing_end("decide_tree_sampled", stream);
+    PSISPEC_LAUNCH("decide_tree_sampled", k_decide_tree_sampled<float>, dim3(a.batch), dim3(64), 0,
+                   stream, a);
   return hipGetLastError();
 }
 
