@@ -21,14 +21,18 @@
 // (ds_read_b64_tr_b16: a 16-lane group reads a 4 x 16 block and each lane receives one column's
 // four values).
 //
-// Tiling.  A BM x BN output tile per 256-thread workgroup (four wave64s, 128 x 128 each = 4 x 4
-// MFMA tiles of 32 x 32), K steps of 32 through NSTAGE LDS stages filled by 16-byte
-// direct-to-LDS buffer loads NSTAGE-1 steps ahead (no register staging), one barrier per step.
-// Workgroup ids are dealt round-robin to the 8 XCDs; each XCD takes a contiguous range of column
-// tiles with the M tiles fastest, so the workgroups that share a W column block run on one XCD
-// at the same time and share it through that XCD's L2.
+// Tiling.  A 256 x 256 output tile per 512-thread workgroup: eight wave64s (two per SIMD), each
+// owning a 128 x 64 block (4 x 2 MFMA tiles of 32 x 32), so one wave's MFMAs overlap the other's
+// LDS reads.  K steps of 32 go through NSTAGE LDS stages filled by 16-byte direct-to-LDS buffer
+// loads NSTAGE-1 steps ahead (no register staging), one barrier per step.  When the rows end in a
+// band of at most 128, that band uses 128 x 512 tiles instead (the same staging and the same
+// 128 x 64 wave blocks, eight side by side), so the short band costs half the tiles of a padded
+// 256-row band.  Tiles form column groups (256 columns, or 512 with a short last band) with the
+// M tiles fastest; workgroup ids are dealt round-robin to the 8 XCDs, and each XCD takes a
+// contiguous range of groups, so the workgroups that share a W column block run on one XCD at
+// the same time and share it through that XCD's L2.
 //
-// Epilogue.  The logits are not stored.  Per (row, column tile) it emits the online softmax pair
+// Epilogue.  The logits are not stored.  Per row and 256-column segment it emits the softmax pair
 // (max, sum exp2((x - max) log2e / T)) that the verify combines in place of an HBM row pass, and
 // the logit at the row's draft token (its one column tile writes it), which the accept test
 // needs.  Storing the logits is an option, used for the stopping rows that the final draw reads
