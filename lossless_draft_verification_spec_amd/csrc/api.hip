@@ -19,6 +19,7 @@ namespace psispec {
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kDrawBlocks = 2048;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -37,8 +38,11 @@ struct Plan {
 // rows: rows of the HBM pass; batch: draws (one per request, or one per drafted token); pool: the
 // draws have a q row (residual draws keep a pool of uncertain-sign tokens).
 // bounded: the drafting step's fp32 sub-chunk records and its list of unsettled draws.
+// wide_draw: the draw pass may give each wave several sub-chunks (not for the sampled-tree chain
+// passes, which share the draw chunking and keep one sub-chunk per wave, nor for the drafting
+// step, whose exact pass runs over the few listed draws and wants many small tasks).
 Plan make_plan(int64_t rows, int64_t batch, int V, size_t es, int excl_stride, int fixed_nchunk = 0,
-               bool pool = true, bool bounded = false) {
+               bool pool = true, bool bounded = false, bool wide_draw = true) {
   Plan pl{};
   const size_t row_bytes = (size_t)V * es;
   int nchunk = (int)((row_bytes + 131071) / 131072);
@@ -58,8 +62,15 @@ Plan make_plan(int64_t rows, int64_t batch, int V, size_t es, int excl_stride, i
     pl.chunk_elems = 0;
   }
   pl.nsub = (V + kSub - 1) / kSub;
-  // draw pass: one 1024-token sub-chunk per wave of a block
-  pl.chunk_elems_draw = (kThreads / 64) * kSub;
+  // draw pass: 1024-token sub-chunks, spw per wave of a block.  spw grows (2, 4) while the draws
+  // still make about kDrawBlocks blocks, which spreads each block's set-up (exp table, descriptor,
+  // normaliser ratio) over more tokens without leaving CUs idle.
+  int spw = 1;
+  while (wide_draw && spw < 4 &&
+         batch * (int64_t)((pl.nsub + 2 * spw * (kThreads / 64) - 1) / (2 * spw * (kThreads / 64))) >=
+             kDrawBlocks)
+    spw *= 2;
+  pl.chunk_elems_draw = spw * (kThreads / 64) * kSub;
   pl.nchunk_draw = (V + pl.chunk_elems_draw - 1) / pl.chunk_elems_draw;
   size_t off = 0;
   pl.off_part = off;
@@ -116,7 +127,7 @@ struct TreeQPlan {
 TreeQPlan make_treeq_plan(int batch, int N, int V, size_t es) {
   TreeQPlan tp{};
   const int64_t nP = (int64_t)batch * (N + 1);
-  tp.pl = make_plan(2 * nP, batch, V, es, N);
+  tp.pl = make_plan(2 * nP, batch, V, es, N, 0, true, false, false);
   const size_t nc = (size_t)tp.pl.nchunk_draw;
   size_t off = tp.pl.total;
   tp.off_nchild = off;
@@ -650,7 +661,7 @@ size_t psispec_sample_drafts_workspace(int32_t batch, int32_t B, int32_t V, psis
   if (batch < 0 || B < 1 || B > 64 || V < 1) return 0;
   if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return 0;
   const int64_t rows = (int64_t)batch * (B + 1), jobs = (int64_t)batch * B;
-  return make_plan(rows, jobs, V, elem_size(dtype), 0, 0, false, true).total + kAlign;
+  return make_plan(rows, jobs, V, elem_size(dtype), 0, 0, false, true, false).total + kAlign;
 }
 
 psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
@@ -669,7 +680,8 @@ psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
   const int64_t rows_plan = (int64_t)batch * (B + 1), jobs = (int64_t)batch * B;
   const int64_t rows_pass = (fft ? batch : 0) + (q_logits ? jobs : 0);
   const bool fuse = fuse_topp(dtype, rows_pass, V, s->top_p);
-  const Plan pl = make_plan(rows_plan, jobs, V, elem_size(dtype), 0, fuse ? 1 : 0, false, true);
+  const Plan pl =
+      make_plan(rows_plan, jobs, V, elem_size(dtype), 0, fuse ? 1 : 0, false, true, false);
   if (rows_plan * pl.nchunk > INT32_MAX || jobs * pl.nchunk_draw > INT32_MAX) return PSISPEC_EINVAL;
   if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace % kAlign) != 0)
     return PSISPEC_EWORKSPACE;

@@ -1,6 +1,8 @@
 // draw.h -- device code of the fp64 final draw, shared by its kernels and the fused verify.
 #pragma once
 
+#include <type_traits>
+
 #include "launch.h"
 
 namespace psispec {
@@ -40,6 +42,55 @@ __device__ inline void load_run(const T* row, int x0, int V, bool vec_ok, float 
   }
 #pragma unroll
   for (int e = 0; e < n; ++e) f[e] = (x0 + e < V) ? to_f32(row[x0 + e]) : -__builtin_huge_valf();
+}
+
+// The 16 logits x0..x0+15 of one lane (x0 a multiple of 16) as raw bits, unpacked one at a time
+// by a compile-time index, so a loop over them needs no register indexing.  Whole 16-byte vectors
+// when the row allows it, else element by element; tokens past V read as -inf.
+template <typename T>
+struct Run16 {
+  static constexpr int kWords = 16 * (int)sizeof(T) / 16;  // 16-byte words: 2 (bf16) or 4 (fp32)
+  u32x4 w[kWords];
+};
+
+template <typename T>
+__device__ inline void load_run16(const T* row, int x0, int V, bool vec_ok, Run16<T>& r) {
+  if (vec_ok && x0 + 16 <= V) {
+    const u32x4* vp = reinterpret_cast<const u32x4*>(row + x0);
+#pragma unroll
+    for (int i = 0; i < Run16<T>::kWords; ++i) r.w[i] = vp[i];
+    return;
+  }
+  uint32_t b[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    if constexpr (sizeof(T) == 2)
+      b[e] = (x0 + e < V) ? (uint32_t)row[x0 + e].bits : 0xff80u;  // bf16 -inf
+    else
+      b[e] = (x0 + e < V) ? __float_as_uint(row[x0 + e]) : 0xff800000u;
+  }
+#pragma unroll
+  for (int i = 0; i < Run16<T>::kWords; ++i) {
+    if constexpr (sizeof(T) == 2)
+      r.w[i] = u32x4{b[8 * i] | (b[8 * i + 1] << 16), b[8 * i + 2] | (b[8 * i + 3] << 16),
+                     b[8 * i + 4] | (b[8 * i + 5] << 16), b[8 * i + 6] | (b[8 * i + 7] << 16)};
+    else
+      r.w[i] = u32x4{b[4 * i], b[4 * i + 1], b[4 * i + 2], b[4 * i + 3]};
+  }
+}
+
+template <typename T, int e>
+__device__ inline float run_at(const Run16<T>& r) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4& v = r.w[e / 8];
+    const int k = (e % 8) / 2;
+    const uint32_t u = k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+    return __uint_as_float((e % 2) ? (u & 0xffff0000u) : (u << 16));
+  } else {
+    const u32x4& v = r.w[e / 4];
+    const int k = e % 4;
+    return __uint_as_float(k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w);
+  }
 }
 
 __device__ inline double wave_sum(double v) {
@@ -119,6 +170,12 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
   for (int i = threadIdx.x; i < nexcl; i += kThreads)
     s_excl[i] = a.excl[(int64_t)r * a.excl_stride + i];
   const double rho = has_q ? rho_estimate(a, d) : 0.0;
+  // exponent-domain form of the band: e_p (1 - kBand) > rho e_q (1 + kBand) is
+  // t_p - t_q > 256 log2 rho + 256 log2((1 + kBand) / (1 - kBand)), t = 256 log2(e) (l - lmax) / T
+  const double c256 = a.inv_T * k256Log2e;
+  const double mp = (double)v.lmax_p * c256, mq = (double)v.lmax_q * c256;
+  const double tau = 256.0 * log2(rho), wband = 256.0 * log2((1.0 + kBand) / (1.0 - kBand));
+  const double t_hi = tau + wband, t_lo = tau - wband;
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub_per_chunk = a.chunk_elems_draw / kSub;
@@ -127,29 +184,51 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
     const int sub = c * sub_per_chunk + j;
     if (sub >= a.nsub) break;
     const int x0 = sub * kSub + lane * kPerLane;
-    float fp[kPerLane], fq[kPerLane];
-    load_run<T, kPerLane>(prow, x0, a.V, vec_ok, fp);
     double Ap = 0.0, Aq = 0.0;
     int unc = 0;
     uint32_t umask = 0;
     if (has_q) {
-      load_run<T, kPerLane>(qrow, x0, a.V, vec_ok, fq);
-      // four tokens' fp64 chains at a time: fewer VGPRs than a full unroll, more waves per SIMD
-#pragma unroll 4
-      for (int e = 0; e < kPerLane; ++e) {
-        const double ep = term<kTopp>(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl);
-        const double eq = term<kTopp>(fq[e], v.lmax_q, v.thr_q, a.inv_T, tbl);
+      // Sign classes in the exponent domain: e_p > rho e_q exactly when t_p - t_q > 256 log2 rho,
+      // so the band test costs one subtraction and two compares; the sums are branch-free.  Both
+      // runs are loaded at once (one memory latency per wave) and taken 4 tokens at a time, with
+      // a barrier between the groups so the compiler does not interleave all 16 exps.
+      Run16<T> rp, rq;
+      load_run16<T>(prow, x0, a.V, vec_ok, rp);
+      load_run16<T>(qrow, x0, a.V, vec_ok, rq);
+      auto pair = [&](float lp, float lq, int e) {
+        double tp = fma((double)lp, c256, -mp), tq = fma((double)lq, c256, -mq);
+        if constexpr (kTopp) {
+          if (!(lp >= v.thr_p)) tp = -__builtin_huge_val();  // outside the nucleus: weight 0
+          if (!(lq >= v.thr_q)) tq = -__builtin_huge_val();
+        }
+        const double ep = exp2_256(tp, tbl), eq = exp2_256(tq, tbl);
         Ep += ep;
         Eq += eq;
-        const double diff = ep - rho * eq, band = kBand * (ep + rho * eq);
-        if (diff > band) {
-          Ap += ep;
-          Aq += eq;
-        } else if (diff >= -band && ep > 0.0) {
-          ++unc;
-          umask |= 1u << e;
-        }
-      }
+        const double dt = tp - tq;
+        // (a token whose weights underflowed may land in the band: its pool entry adds 0)
+        const bool pos = dt > t_hi;
+        const bool amb = (dt >= t_lo) & !pos;  // no short circuit: no branches
+        const double pf = pos ? 1.0 : 0.0;     // ep and eq are finite: pf * e is e or 0
+        Ap = fma(pf, ep, Ap);
+        Aq = fma(pf, eq, Aq);
+        umask |= amb ? 1u << e : 0u;
+      };
+      auto group = [&](auto g) {
+        constexpr int e0 = decltype(g)::value;
+        pair(run_at<T, e0>(rp), run_at<T, e0>(rq), e0);
+        pair(run_at<T, e0 + 1>(rp), run_at<T, e0 + 1>(rq), e0 + 1);
+        pair(run_at<T, e0 + 2>(rp), run_at<T, e0 + 2>(rq), e0 + 2);
+        pair(run_at<T, e0 + 3>(rp), run_at<T, e0 + 3>(rq), e0 + 3);
+        // the group's sums are complete here (an empty asm that reads and writes them), so its
+        // weights die before the next group starts
+        asm volatile("" : "+v"(Ep), "+v"(Eq), "+v"(Ap), "+v"(Aq), "+v"(umask));
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      group(std::integral_constant<int, 0>{});
+      group(std::integral_constant<int, 4>{});
+      group(std::integral_constant<int, 8>{});
+      group(std::integral_constant<int, 12>{});
+      unc = __builtin_popcount(umask);
       // pack this sub-chunk's uncertain tokens, in token order, into one pool segment
       int before = unc;  // inclusive prefix over lanes, then made exclusive
 #pragma unroll
@@ -176,6 +255,8 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
       }
       if (lane == 0) a.suboff[(int64_t)r * a.nsub + sub] = seg;
     } else {
+      float fp[kPerLane];
+      load_run<T, kPerLane>(prow, x0, a.V, vec_ok, fp);
 #pragma unroll
       for (int e = 0; e < kPerLane; ++e) {
         double ep = term<kTopp>(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl);

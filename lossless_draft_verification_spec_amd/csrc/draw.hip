@@ -34,10 +34,15 @@
 namespace psispec {
 namespace {
 
+// at least this many waves per SIMD: a fully unrolled run of 16 token pairs would otherwise take
+// ~190 VGPRs (two waves per SIMD); capped, the compiler interleaves fewer exps per wave and the
+// other waves hide the table reads
+constexpr int kDrawPassWaves = 5;
+
 // kList: the draws are a device-side list (the grid loops over its entries); a separate
 // instantiation, since the loop keeps registers live that the one-task-per-block form does not need
 template <typename T, bool kTopp, bool kList>
-__global__ __launch_bounds__(kThreads) void k_draw_pass(DrawArgs a, int vec_ok) {
+__global__ __launch_bounds__(kThreads, kList ? 4 : kDrawPassWaves) void k_draw_pass(DrawArgs a, int vec_ok) {
   if constexpr (!kList) {
     const int r = blockIdx.x / a.nchunk_draw;
     draw_pass_task<T, kTopp>(a, r, blockIdx.x - r * a.nchunk_draw, vec_ok);

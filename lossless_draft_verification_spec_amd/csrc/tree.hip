@@ -22,9 +22,8 @@ __device__ inline int row_status(float lmax, double Z) {
   return ok ? 0 : PSISPEC_ST_NONFINITE;
 }
 
-template <typename T>
-__device__ inline double node_prob(const TreeArgs& a, int64_t row, float lmax, double Z, int tok) {
-  const float l = to_f32(row_ptr<T>(a.rs, row)[tok]);
+// p'_row(tok) from the token's logit l (read up front by the caller)
+__device__ inline double node_prob(const TreeArgs& a, int64_t row, float lmax, double Z, float l) {
   double pr = exp(((double)l - (double)lmax) * a.inv_T) / Z;
   if (a.use_topp) {
     const ToppStat tp = a.topp[row];
@@ -51,12 +50,17 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
   __shared__ double s_pown[kMaxNodes];
   __shared__ int s_first[kMaxNodes];
   __shared__ float2 s_pair[kStagePairs];
+  __shared__ float s_l[kMaxNodes];
 
-  // 0. the tree, every node's accept uniform (Philox of (request, c+1, accept)) and the row pairs,
-  //    loaded or computed by the whole wave up front: the serial steps below then read LDS only
+  // 0. the tree, every node's accept uniform (Philox of (request, c+1, accept)), the logit of each
+  //    node's token in its parent's row and the row pairs, loaded or computed by the whole wave up
+  //    front (the token gathers go out with the pair loads): the steps below then read LDS only
   for (int j = t; j < N; j += 64) {
-    s_par[j] = par[j];
-    s_tok[j] = tok[j];
+    const int v = par[j], tj = tok[j];
+    s_par[j] = v;
+    s_tok[j] = tj;
+    s_l[j] = (tj >= 0 && tj < V && v >= -1 && v < j) ? to_f32(row_ptr<T>(a.rs, row0 + v + 1)[tj])
+                                                      : 0.f;
     s_u[j] = philox_uniform(a.seed, a.request_base + (uint32_t)r, (uint32_t)(j + 1), kPurposeAccept,
                             a.step);
   }
@@ -116,7 +120,7 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
   for (int j = t; j < N; j += 64) {
     const int v = s_par[j], tj = s_tok[j];
     s_pown[j] = (tj >= 0 && tj < V && v >= -1 && v < j)
-                    ? node_prob<T>(a, row0 + v + 1, s_lmax[v + 1], s_Z[v + 1], tj)
+                    ? node_prob(a, row0 + v + 1, s_lmax[v + 1], s_Z[v + 1], s_l[j])
                     : 0.0;
   }
   // first[s]: no earlier sibling of s carries s's token (each distinct removed token counts once).
