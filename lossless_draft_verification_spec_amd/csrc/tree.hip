@@ -124,35 +124,38 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
                     : 0.0;
   }
   // first[s]: no earlier sibling of s carries s's token (each distinct removed token counts once).
-  // With N <= 64, node s sits in lane s and the loops over the earlier siblings read its parent,
-  // token, flag and probability from that lane (v_readlane, wave-uniform index: scalar values, no
-  // LDS round trips); larger trees read LDS.  Either way R takes the same subtractions in index
-  // order.
+  // With N <= 64, node s sits in lane s: one ballot per distinct parent gives every lane the mask
+  // of its siblings, and each lane then visits only its earlier siblings, in index order (LDS
+  // reads), so R takes the same subtractions in index order as the general form below.
   __syncthreads();
   if (N <= 64) {
     const int pj = t < N ? s_par[t] : -2, tj = t < N ? s_tok[t] : -1;
-    const double pown = t < N ? s_pown[t] : 0.0;
-    const int pown_lo = __double2loint(pown), pown_hi = __double2hiint(pown);
-    int first = 1;
-    for (int s2 = 0; s2 < N; ++s2) {
-      const int ps = __builtin_amdgcn_readlane(pj, s2), ts = __builtin_amdgcn_readlane(tj, s2);
-      first &= !(s2 < t && ps == pj && ts == tj);
+    uint64_t sib = 0;
+    for (uint64_t todo = __ballot(t < N); todo;) {
+      const int v = __builtin_amdgcn_readlane(pj, __builtin_ctzll(todo));
+      const bool same = t < N && pj == v;
+      const uint64_t m = __ballot(same);
+      if (same) sib = m;
+      todo &= ~m;
     }
+    const uint64_t earlier = sib & ((1ull << t) - 1ull);  // t < 64
+    int first = 1;
+    for (uint64_t m = earlier; m; m &= m - 1) first &= s_tok[__builtin_ctzll(m)] != tj;
+    if (t < N) s_first[t] = first;
+    __syncthreads();
     double ratio = 0.0;
     if (t < N) {
       if (tj < 0 || tj >= V) st |= PSISPEC_ST_BAD_TOKEN;
     }
-    double res = pown, R = 1.0;
-    for (int s2 = 0; s2 < N; ++s2) {  // earlier siblings, in index order
-      const int ps = __builtin_amdgcn_readlane(pj, s2), ts = __builtin_amdgcn_readlane(tj, s2);
-      const int fs = __builtin_amdgcn_readlane(first, s2);
-      const double ws = __hiloint2double(__builtin_amdgcn_readlane(pown_hi, s2),
-                                         __builtin_amdgcn_readlane(pown_lo, s2));
-      if (s2 >= t || ps != pj || ts < 0 || ts >= V) continue;
+    double res = t < N ? s_pown[t] : 0.0, R = 1.0;
+    for (uint64_t m = earlier; m; m &= m - 1) {  // earlier siblings, in index order
+      const int s2 = __builtin_ctzll(m);
+      const int ts = s_tok[s2];
+      if (ts < 0 || ts >= V) continue;
       if (ts == tj)
         res = 0.0;  // same token rejected earlier: already removed from the residual
-      else if (fs)
-        R -= ws;
+      else if (s_first[s2])
+        R -= s_pown[s2];
     }
     if (t < N) {
       if (tj >= 0 && tj < V && pj >= -1 && pj < t) ratio = R > 0.0 ? fmin(1.0, res / R) : 0.0;
