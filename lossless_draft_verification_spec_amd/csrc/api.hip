@@ -474,16 +474,6 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
   ToppStat* topp = carve<ToppStat>(workspace, pl.off_topp);
   DrawDesc* desc = carve<DrawDesc>(workspace, pl.off_desc);
 
-  if (fuse) {
-    if (launch_rowstats_topp(rs, c, s->top_p, part, topp, stream) != hipSuccess) return PSISPEC_EHIP;
-  } else {
-    if (launch_rowstats(rs, dtype, pl.nchunk, pl.chunk_elems, c, part, stream) != hipSuccess)
-      return PSISPEC_EHIP;
-    if (use_topp && launch_topp(rs, dtype, pl.nchunk, c, s->top_p, part, topp, stream) !=
-                        hipSuccess)
-      return PSISPEC_EHIP;
-  }
-
   LinearArgs la{};
   la.rs = rs;
   la.draft = draft_tokens;
@@ -507,7 +497,6 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
   la.out_tokens = out_tokens;
   la.ratios = ratios;
   la.accept_mask = accept_mask;
-  if (launch_decide_linear(la, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
 
   DrawArgs da{};
   da.rs = rs;
@@ -535,6 +524,24 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
   da.ucount = carve<int32_t>(workspace, pl.off_ucount);
   da.out_tokens = out_tokens;
   da.status = status;
+
+  // a few kilobytes of logits per request: one launch does the whole verify
+  if (!use_topp && pl.nchunk == 1 &&
+      (size_t)(2 * B + 1) * (size_t)V * elem_size(dtype) <= kSmallVerifyBytes)
+    return launch_verify_small(la, da, part, dtype, stream) == hipSuccess
+               ? PSISPEC_OK
+               : PSISPEC_EHIP;
+
+  if (fuse) {
+    if (launch_rowstats_topp(rs, c, s->top_p, part, topp, stream) != hipSuccess) return PSISPEC_EHIP;
+  } else {
+    if (launch_rowstats(rs, dtype, pl.nchunk, pl.chunk_elems, c, part, stream) != hipSuccess)
+      return PSISPEC_EHIP;
+    if (use_topp && launch_topp(rs, dtype, pl.nchunk, c, s->top_p, part, topp, stream) !=
+                        hipSuccess)
+      return PSISPEC_EHIP;
+  }
+  if (launch_decide_linear(la, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
   if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
   return PSISPEC_OK;
 }
