@@ -180,6 +180,21 @@ def test_linear_first_from_target_layout():
     assert (acc >= 1).all() and (acc <= B).all()  # 1 <= TPF = (k+1)/2 <= (B+1)/2
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("batch,B,V,flags", [(3, 64, 8, 0), (6, 6, 200, PSISPEC_FIRST_FROM_TARGET),
+                                             (40, 8, 64, 0)])
+def test_linear_one_launch_path(dtype, batch, B, V, flags):
+    """Calls whose rows hold at most 32 KiB per request run the whole verify in one launch: many
+    rows per request (B = 64: 129 rows over the block's four waves), the Uno layout, and many small
+    requests, against the oracle."""
+    p, q, d = _rand_linear(batch, B, V, dtype, seed=B * 31 + V)
+    if flags:
+        q[:, 0] = p[:, 0]
+    t = _run_and_compare(p, q, d, steps=range(4), flags=flags)
+    print(t)
+    t.check()
+
+
 def test_linear_request_base_and_steps():
     p, q, d = _rand_linear(4, 4, 777, torch.float32, seed=4)
     t = _run_and_compare(p, q, d, steps=(0, 5, 2**32 - 1), request_base=1000, seed=2**64 - 1)
