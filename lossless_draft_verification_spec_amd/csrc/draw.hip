@@ -13,9 +13,9 @@
 //   k_draw_pass:   one fp64 pass over the stopping row(s): a block per chunk of 4096 spw tokens,
 //                  each wave taking spw sub-chunks of 1024 tokens in turn (spw = 1, 2 or 4: more
 //                  when the draws alone fill the chip, which spreads each block's set-up over more
-//                  tokens), 16 consecutive tokens per lane.  Without a q row (bonus draw, tree draw) the
-//                  weights need no normaliser: w = exp((l - lmax) / T) over the kept, not removed
-//                  tokens, and the pass stores each sub-chunk's mass.  With a q row the sign of
+//                  tokens), 16 consecutive tokens per lane.  Without a q row (bonus draw, tree
+//                  draw) the weights need no normaliser: w = exp((l - lmax) / T) over the kept,
+//                  not removed tokens, and the pass stores each sub-chunk's mass.  With a q row the sign of
 //                  p'(x) - q'(x) = (e_p(x) - rho e_q(x)) / E_p, rho = E_p / E_q, is decided with
 //                  the ratio of the normalisers from the HBM pass (relative error below ~1e-6),
 //                  as a comparison of exponents (t_p - t_q against 256 log2 rho);
