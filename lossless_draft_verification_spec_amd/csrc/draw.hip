@@ -15,10 +15,10 @@
 //                  when the draws alone fill the chip, which spreads each block's set-up over more
 //                  tokens), 16 consecutive tokens per lane.  Without a q row (bonus draw, tree
 //                  draw) the weights need no normaliser: w = exp((l - lmax) / T) over the kept,
-//                  not removed tokens, and the pass stores each sub-chunk's mass.  With a q row the sign of
-//                  p'(x) - q'(x) = (e_p(x) - rho e_q(x)) / E_p, rho = E_p / E_q, is decided with
-//                  the ratio of the normalisers from the HBM pass (relative error below ~1e-6),
-//                  as a comparison of exponents (t_p - t_q against 256 log2 rho);
+//                  not removed tokens, and the pass stores each sub-chunk's mass.  With a q row
+//                  the sign of p'(x) - q'(x) = (e_p(x) - rho e_q(x)) / E_p, rho = E_p / E_q, is
+//                  decided with the ratio of the normalisers from the HBM pass (relative error
+//                  below ~1e-6), as a comparison of exponents (t_p - t_q against 256 log2 rho);
 //                  tokens within a 1e-5 band of the sign change are uncertain: each wave packs the
 //                  exact (e_p, e_q) of its sub-chunk's uncertain tokens, in token order, into a
 //                  segment of a per-request pool.  The pass stores per sub-chunk the sums A_p, A_q
