@@ -653,7 +653,7 @@ def copy_calibration(torch):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (requests would "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (requests would "
               "shard by request_base with no exchange).", file=sys.stderr)
         sys.exit(2)
     import torch
