@@ -99,6 +99,31 @@ __device__ inline double wave_sum(double v) {
   return v;
 }
 
+// The same sum by DPP lane exchanges, register to register: within each row of 16 lanes,
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror and row_mirror pair the lanes
+// symmetrically, so after four steps every lane of a row holds the row's sum with the same bits;
+// the four row sums are then read out and added in row order.  Every lane of the wave must be
+// active; the result is the same in every lane.  The draw pass uses it; the draft bounds kernel
+// measured slower with DPP reductions (they add vector-ALU work to a kernel already bound by it)
+// and keeps the shuffle above.
+template <int kCtrl>
+__device__ inline double dpp_f64(double x) {
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), kCtrl, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), kCtrl, 0xf, 0xf, true);
+  return __hiloint2double(hi, lo);
+}
+__device__ inline double readlane_f64(double x, int lane) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), lane),
+                          __builtin_amdgcn_readlane(__double2loint(x), lane));
+}
+__device__ inline double wave_sum_dpp(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  v += dpp_f64<0x140>(v);  // row_mirror
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
 __device__ inline int wave_max(int v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
@@ -195,12 +220,23 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
       Run16<T> rp, rq;
       load_run16<T>(prow, x0, a.V, vec_ok, rp);
       load_run16<T>(qrow, x0, a.V, vec_ok, rq);
-      auto pair = [&](float lp, float lq, int e) {
-        double tp = fma((double)lp, c256, -mp), tq = fma((double)lq, c256, -mq);
+      // the sign-class arguments of one token pair (the band test below and the re-test of a
+      // wave's band tokens use the same arithmetic, so they classify every token alike)
+      auto targs = [&](float lp, float lq, double& tp, double& tq) {
+        tp = fma((double)lp, c256, -mp);
+        tq = fma((double)lq, c256, -mq);
         if constexpr (kTopp) {
           if (!(lp >= v.thr_p)) tp = -__builtin_huge_val();  // outside the nucleus: weight 0
           if (!(lq >= v.thr_q)) tq = -__builtin_huge_val();
         }
+      };
+      // whether some token of the lane lies in the band: a lane mask in scalar registers, so the
+      // per-token cost is one compare (the lane's bit mask is formed only when some lane of the
+      // wave has one)
+      bool anyamb = false;
+      auto pair = [&](float lp, float lq) {
+        double tp, tq;
+        targs(lp, lq, tp, tq);
         const double ep = exp2_256(tp, tbl), eq = exp2_256(tq, tbl);
         Ep += ep;
         Eq += eq;
@@ -211,35 +247,46 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
         const double pf = pos ? 1.0 : 0.0;     // ep and eq are finite: pf * e is e or 0
         Ap = fma(pf, ep, Ap);
         Aq = fma(pf, eq, Aq);
-        umask |= amb ? 1u << e : 0u;
+        anyamb = anyamb | amb;
       };
       auto group = [&](auto g) {
         constexpr int e0 = decltype(g)::value;
-        pair(run_at<T, e0>(rp), run_at<T, e0>(rq), e0);
-        pair(run_at<T, e0 + 1>(rp), run_at<T, e0 + 1>(rq), e0 + 1);
-        pair(run_at<T, e0 + 2>(rp), run_at<T, e0 + 2>(rq), e0 + 2);
-        pair(run_at<T, e0 + 3>(rp), run_at<T, e0 + 3>(rq), e0 + 3);
+        pair(run_at<T, e0>(rp), run_at<T, e0>(rq));
+        pair(run_at<T, e0 + 1>(rp), run_at<T, e0 + 1>(rq));
+        pair(run_at<T, e0 + 2>(rp), run_at<T, e0 + 2>(rq));
+        pair(run_at<T, e0 + 3>(rp), run_at<T, e0 + 3>(rq));
         // the group's sums are complete here (an empty asm that reads and writes them), so its
         // weights die before the next group starts
-        asm volatile("" : "+v"(Ep), "+v"(Eq), "+v"(Ap), "+v"(Aq), "+v"(umask));
+        asm volatile("" : "+v"(Ep), "+v"(Eq), "+v"(Ap), "+v"(Aq));
         __builtin_amdgcn_sched_barrier(0);
       };
       group(std::integral_constant<int, 0>{});
       group(std::integral_constant<int, 4>{});
       group(std::integral_constant<int, 8>{});
       group(std::integral_constant<int, 12>{});
-      unc = __builtin_popcount(umask);
-      // pack this sub-chunk's uncertain tokens, in token order, into one pool segment
-      int before = unc;  // inclusive prefix over lanes, then made exclusive
+      // pack this sub-chunk's uncertain tokens, in token order, into one pool segment (most
+      // sub-chunks have none: this runs only when some lane has one)
+      int seg = -1, total = 0;
+      if (__ballot(anyamb)) {
+        float fp[kPerLane], fq[kPerLane];  // the run again (cached), for the lanes' bit masks
+        load_run<T, kPerLane>(prow, x0, a.V, vec_ok, fp);
+        load_run<T, kPerLane>(qrow, x0, a.V, vec_ok, fq);
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(before, off, 64);
-        if (lane >= off) before += y;
-      }
-      const int total = __shfl(before, 63, 64);
-      before -= unc;
-      int seg = -1;
-      if (total > 0) {
+        for (int e = 0; e < kPerLane; ++e) {
+          double tp, tq;
+          targs(fp[e], fq[e], tp, tq);
+          const double dt = tp - tq;
+          umask |= ((dt >= t_lo) & !(dt > t_hi)) ? 1u << e : 0u;
+        }
+        unc = __builtin_popcount(umask);
+        int before = unc;  // inclusive prefix over lanes, then made exclusive
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(before, off, 64);
+          if (lane >= off) before += y;
+        }
+        total = __shfl(before, 63, 64);
+        before -= unc;
         if (lane == 0) seg = atomicAdd(a.ucount + r, total);
         seg = __shfl(seg, 0, 64);
         if (seg + total > kUncPool) seg = -1;  // pool full: this sub-chunk is summed token by token
@@ -254,6 +301,7 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
         }
       }
       if (lane == 0) a.suboff[(int64_t)r * a.nsub + sub] = seg;
+      unc = total;  // the sub-chunk's count
     } else {
       float fp[kPerLane];
       load_run<T, kPerLane>(prow, x0, a.V, vec_ok, fp);
@@ -264,18 +312,16 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
         Ap += ep;
       }
     }
-    Ap = wave_sum(Ap);
-    Aq = wave_sum(Aq);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) unc += __shfl_xor(unc, off, 64);
+    Ap = wave_sum_dpp(Ap);
+    Aq = wave_sum_dpp(Aq);
     if (lane == 0) {
       a.suba[(int64_t)r * a.nsub + sub] = make_double2(Ap, Aq);
       a.subn[(int64_t)r * a.nsub + sub] = unc;
     }
   }
   if (!has_q) return;
-  Ep = wave_sum(Ep);
-  Eq = wave_sum(Eq);
+  Ep = wave_sum_dpp(Ep);
+  Eq = wave_sum_dpp(Eq);
   if (lane == 0) s_part[wave] = make_double2(Ep, Eq);
   __syncthreads();
   if (threadIdx.x == 0) {

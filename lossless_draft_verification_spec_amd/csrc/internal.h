@@ -163,25 +163,27 @@ __device__ inline double exp_tang(double x, const double* tbl) {
 
 // 2^(t/256) for t = 256 log2(e) (l - lmax) / T formed by one fused multiply-add,
 // t = l c256 - lmax c256: with r = t - rint(t) (exact, |r| <= 1/2), 2^(t/256) = 2^m 2^(j/256) 2^(r/256)
-// and 2^(r/256) - 1 by its degree-4 Taylor polynomial in r (coefficients (ln 2/256)^i / i!,
-// truncation below 4e-17).  Same table as exp_tang.  Relative error against exp((l - lmax) / T):
-// below 1e-14 for |l - lmax| / T up to 80, 2.2e-13 at 4600 (the rounding of lmax c256 scales with
-// it), as exp_tang's own argument rounding does.  Branch-free and select-free: t is clamped at
+// and 2^(r/256) - 1 = x (1 + x/2 + x^2/6 + x^3/24 + ...) (x = r ln 2/256, |x| <= a = ln 2/512) by a
+// cubic: in the bracket, x^3 is replaced by its Chebyshev economization on [-a, a], (3/4) a^2 x, so
+// the cubic is x + (1/2 + a^2/32) x^2 + x^3/6; it vanishes at r = 0 (integer t stays exact) and its
+// relative error is below 3.5e-14 (one multiply-add fewer than the degree-4 Taylor polynomial,
+// error 4e-17).  Same table as exp_tang.  Relative error against
+// exp((l - lmax) / T): below 5e-14 for |l - lmax| / T up to 80, 2.2e-13 at 4600 (the rounding of
+// lmax c256 scales with it), as exp_tang's own argument rounding does.  Branch-free and
+// select-free: t is clamped at
 // -300000 (which also maps -inf and NaN there), where the final scaling by 2^(-1172) rounds to 0;
 // results below 2^-1074 round to 0 or to a subnormal as the scaling rounds them (0 from
 // t < -275200, i.e. exp(x) for x < -745.13, as the fp64 exp itself).
 constexpr double k256Log2e = 369.3299304675746;  // 256 / ln 2
 __device__ inline double exp2_256(double t, const double* tbl) {
-  const double c1 = 0.0027076061740622863;   // ln 2 / 256
-  const double c2 = 3.6655655969101062e-06;  // (ln 2 / 256)^2 / 2
-  const double c3 = 3.3083026805413713e-09;  // (ln 2 / 256)^3 / 6
-  const double c4 = 2.239395190875157e-12;   // (ln 2 / 256)^4 / 24
+  const double c1 = 0.0027076061740622863;   // c = ln 2 / 256
+  const double c2 = 3.6655660167967044e-06;  // (1/2 + a^2/32) c^2 = c^2 / 2 + c^4 / 128
+  const double c3 = 3.3083026805413713e-09;  // c^3 / 6
   const double tc = fmax(t, -300000.0);
   const double kf = rint(tc);
   const int k = (int)kf;
   const double r = tc - kf;
-  double s = fma(r, c4, c3);
-  s = fma(r, s, c2);
+  double s = fma(r, c3, c2);
   s = fma(r, s, c1);
   const double p = r * s;  // 2^(r/256) - 1
   const double tj = tbl[k & (kExpTable - 1)];

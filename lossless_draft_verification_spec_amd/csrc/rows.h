@@ -12,24 +12,32 @@ namespace {
 
 template <typename T>
 struct Elems;
+// The two bf16 halves of a word as floats.  Written as bf16 -> float conversions (a shift or a
+// mask, the same bits as placing the 16 bits on top of a float) so that the compiler takes the
+// values as canonical and forms three-operand maxima from them without quieting every input first.
+__device__ inline float bf16_lo(uint32_t w) { return (float)__builtin_bit_cast(__bf16, (uint16_t)w); }
+__device__ inline float bf16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(__bf16, (uint16_t)(w >> 16));
+}
+
 template <>
 struct Elems<bf16_t> {
   static constexpr int kPerVec = 8;
-  __device__ static void unpack(const u32x4& v, float (&f)[8]) {
-    f[0] = __uint_as_float(v.x << 16);
-    f[1] = __uint_as_float(v.x & 0xffff0000u);
-    f[2] = __uint_as_float(v.y << 16);
-    f[3] = __uint_as_float(v.y & 0xffff0000u);
-    f[4] = __uint_as_float(v.z << 16);
-    f[5] = __uint_as_float(v.z & 0xffff0000u);
-    f[6] = __uint_as_float(v.w << 16);
-    f[7] = __uint_as_float(v.w & 0xffff0000u);
+  __device__ static void unpack(const u32x4& v, float* f) {  // f[0..8)
+    f[0] = bf16_lo(v.x);
+    f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y);
+    f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z);
+    f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w);
+    f[7] = bf16_hi(v.w);
   }
 };
 template <>
 struct Elems<float> {
   static constexpr int kPerVec = 4;
-  __device__ static void unpack(const u32x4& v, float (&f)[4]) {
+  __device__ static void unpack(const u32x4& v, float* f) {  // f[0..4)
     f[0] = __uint_as_float(v.x);
     f[1] = __uint_as_float(v.y);
     f[2] = __uint_as_float(v.z);
@@ -38,20 +46,20 @@ struct Elems<float> {
 };
 
 // Fold n values into the online pair (m, s), s = sum exp2((x - m) * c).  m starts at a finite floor
-// so that -inf entries contribute exp2(-inf) = 0 and NaN/+inf entries turn s into NaN.
+// so that -inf entries contribute exp2(-inf) = 0 and NaN/+inf entries turn s into NaN (a row with a
+// NaN is rejected by its sum, whatever its maximum).  The rescale runs every time: its factor is
+// exp2(0) = 1 exactly when the maximum did not move, and it costs less than the compare and the
+// selects of a conditional one.
 template <int n>
 __device__ inline void fold(const float (&f)[n], float& m, float& s, float c) {
-  float vm = f[0];
+  float mn = m;
 #pragma unroll
-  for (int j = 1; j < n; ++j) vm = fmaxf(vm, f[j]);
-  if (vm > m) {
-    s *= __builtin_amdgcn_exp2f((m - vm) * c);
-    m = vm;
-  }
-  float acc = 0.f;
+  for (int j = 0; j < n; ++j) mn = fmaxf(mn, f[j]);
+  float acc = __builtin_amdgcn_exp2f((f[0] - mn) * c);
 #pragma unroll
-  for (int j = 0; j < n; ++j) acc += __builtin_amdgcn_exp2f((f[j] - m) * c);
-  s += acc;
+  for (int j = 1; j < n; ++j) acc += __builtin_amdgcn_exp2f((f[j] - mn) * c);
+  s = s * __builtin_amdgcn_exp2f((m - mn) * c) + acc;
+  m = mn;
 }
 
 __device__ inline void block_reduce_pair(float& m, float& s, float c) {
@@ -81,6 +89,7 @@ __device__ inline void block_reduce_pair(float& m, float& s, float c) {
 template <typename T, int kUnroll>
 __device__ inline void rowstats_task(const RowSet& rs, int64_t row, int chunk, int chunk_elems,
                                      float c, float2* out, int vec_ok) {
+  static_assert(kUnroll % 2 == 0, "vectors are folded in pairs");
   const T* rp = row_ptr<T>(rs, row);
   const int start = chunk * chunk_elems;
   const int end = min(rs.V, start + chunk_elems);
@@ -95,10 +104,12 @@ __device__ inline void rowstats_task(const RowSet& rs, int64_t row, int chunk, i
       u32x4 v[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(vp + i + u * kThreads);
+      // two vectors per fold: one rescale per 2E values
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        float f[E];
+      for (int u = 0; u < kUnroll; u += 2) {
+        float f[2 * E];
         Elems<T>::unpack(v[u], f);
+        Elems<T>::unpack(v[u + 1], f + E);
         fold(f, m, s, c);
       }
     }

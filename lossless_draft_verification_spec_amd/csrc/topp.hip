@@ -442,17 +442,15 @@ __global__ __launch_bounds__(kThreads) void k_rowstats_topp(RowSet rs, float c, 
   constexpr int E = 8;
   // one step over U vectors: lane maximum and rescale, anchor, counts, then the sum of exps
   auto step = [&](const u32x4* v, int U) __attribute__((always_inline)) {
-    float bm = kNegBig;
+    float mn = m;
     for (int u = 0; u < U; ++u) {
       float f[E];
       Elems<bf16_t>::unpack(v[u], f);
 #pragma unroll
-      for (int j = 0; j < E; ++j) bm = fmaxf(bm, f[j]);
+      for (int j = 0; j < E; ++j) mn = fmaxf(mn, f[j]);
     }
-    if (bm > m) {
-      s *= __builtin_amdgcn_exp2f((m - bm) * c);
-      m = bm;
-    }
+    s *= __builtin_amdgcn_exp2f((m - mn) * c);  // 1 when the maximum did not move
+    m = mn;
     anchor();
     float acc = 0.f;
     for (int u = 0; u < U; ++u) {
