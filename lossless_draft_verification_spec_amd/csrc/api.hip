@@ -19,7 +19,7 @@ namespace psispec {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int64_t kDrawBlocks = 2048;
+constexpr int64_t kDrawBlocks = 1024;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -62,11 +62,13 @@ Plan make_plan(int64_t rows, int64_t batch, int V, size_t es, int excl_stride, i
     pl.chunk_elems = 0;
   }
   pl.nsub = (V + kSub - 1) / kSub;
-  // draw pass: 1024-token sub-chunks, spw per wave of a block.  spw grows (2, 4) while the draws
-  // still make about kDrawBlocks blocks, which spreads each block's set-up (exp table, descriptor,
-  // normaliser ratio) over more tokens without leaving CUs idle.
+  // draw pass: 1024-token sub-chunks, spw per wave of a block.  spw grows (2, 4, 8) while the
+  // draws still make about kDrawBlocks blocks (about one round of the draw pass's resident blocks),
+  // which spreads each block's set-up (exp table, descriptor, normaliser ratio) over more tokens
+  // and shortens the select's chunk sums without leaving CUs idle: spw = 2 at batch 64, 4 at 128,
+  // 8 at 256.
   int spw = 1;
-  while (wide_draw && spw < 4 &&
+  while (wide_draw && spw < 8 &&
          batch * (int64_t)((pl.nsub + 2 * spw * (kThreads / 64) - 1) / (2 * spw * (kThreads / 64))) >=
              kDrawBlocks)
     spw *= 2;

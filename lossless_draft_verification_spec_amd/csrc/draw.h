@@ -22,14 +22,14 @@ __device__ inline void load_run(const T* row, int x0, int V, bool vec_ok, float 
       for (int v = 0; v < n / E; ++v) {
         const u32x4 w = vp[v];
         if constexpr (sizeof(T) == 2) {
-          f[8 * v + 0] = __uint_as_float(w.x << 16);
-          f[8 * v + 1] = __uint_as_float(w.x & 0xffff0000u);
-          f[8 * v + 2] = __uint_as_float(w.y << 16);
-          f[8 * v + 3] = __uint_as_float(w.y & 0xffff0000u);
-          f[8 * v + 4] = __uint_as_float(w.z << 16);
-          f[8 * v + 5] = __uint_as_float(w.z & 0xffff0000u);
-          f[8 * v + 6] = __uint_as_float(w.w << 16);
-          f[8 * v + 7] = __uint_as_float(w.w & 0xffff0000u);
+          f[8 * v + 0] = bf16_lo(w.x);
+          f[8 * v + 1] = bf16_hi(w.x);
+          f[8 * v + 2] = bf16_lo(w.y);
+          f[8 * v + 3] = bf16_hi(w.y);
+          f[8 * v + 4] = bf16_lo(w.z);
+          f[8 * v + 5] = bf16_hi(w.z);
+          f[8 * v + 6] = bf16_lo(w.w);
+          f[8 * v + 7] = bf16_hi(w.w);
         } else {
           f[4 * v + 0] = __uint_as_float(w.x);
           f[4 * v + 1] = __uint_as_float(w.y);
@@ -85,7 +85,7 @@ __device__ inline float run_at(const Run16<T>& r) {
     const u32x4& v = r.w[e / 8];
     const int k = (e % 8) / 2;
     const uint32_t u = k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
-    return __uint_as_float((e % 2) ? (u & 0xffff0000u) : (u << 16));
+    return (e % 2) ? bf16_hi(u) : bf16_lo(u);
   } else {
     const u32x4& v = r.w[e / 4];
     const int k = e % 4;

@@ -99,8 +99,15 @@ struct bf16_t {
   uint16_t bits;
 };
 
+// bf16 -> float: the 16 bits on top of a float (a shift or a mask).  Written as conversions so that
+// the compiler takes the values as canonical and forms three-operand maxima from them without
+// quieting every input first.
+__device__ inline float bf16_bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(__bf16, b); }
+__device__ inline float bf16_lo(uint32_t w) { return bf16_bits_to_f32((uint16_t)w); }
+__device__ inline float bf16_hi(uint32_t w) { return bf16_bits_to_f32((uint16_t)(w >> 16)); }
+
 __device__ inline float to_f32(float x) { return x; }
-__device__ inline float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.bits << 16); }
+__device__ inline float to_f32(bf16_t x) { return bf16_bits_to_f32(x.bits); }
 
 template <typename T>
 __device__ inline const T* row_ptr(const RowSet& rs, int64_t row) {

@@ -12,14 +12,6 @@ namespace {
 
 template <typename T>
 struct Elems;
-// The two bf16 halves of a word as floats.  Written as bf16 -> float conversions (a shift or a
-// mask, the same bits as placing the 16 bits on top of a float) so that the compiler takes the
-// values as canonical and forms three-operand maxima from them without quieting every input first.
-__device__ inline float bf16_lo(uint32_t w) { return (float)__builtin_bit_cast(__bf16, (uint16_t)w); }
-__device__ inline float bf16_hi(uint32_t w) {
-  return (float)__builtin_bit_cast(__bf16, (uint16_t)(w >> 16));
-}
-
 template <>
 struct Elems<bf16_t> {
   static constexpr int kPerVec = 8;
