@@ -11,7 +11,7 @@
 // (normalisers, weights and prefix sums) with a table-driven fp64 exp; all reductions run in a
 // fixed order.  Two kernels:
 //   k_draw_pass:   one fp64 pass over the stopping row(s): a block per chunk of 4096 spw tokens,
-//                  each wave taking spw sub-chunks of 1024 tokens in turn (spw = 1, 2 or 4: more
+//                  each wave taking spw sub-chunks of 1024 tokens in turn (spw = 1, 2, 4 or 8: more
 //                  when the draws alone fill the chip, which spreads each block's set-up over more
 //                  tokens), 16 consecutive tokens per lane.  Without a q row (bonus draw, tree
 //                  draw) the weights need no normaliser: w = exp((l - lmax) / T) over the kept,
