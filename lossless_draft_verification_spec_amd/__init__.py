@@ -121,16 +121,18 @@ def _out_check(t: torch.Tensor | None, shape, dtype, dev, name: str, exact: bool
     (exactly, or at least that many elements): the library writes through its raw pointer."""
     if t is None:
         return
-    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.get_device() != dev.index:
         raise PsispecError(f"{name} must be a GPU tensor on {dev}")
     if not t.is_contiguous():
         raise PsispecError(f"{name} must be contiguous")
     if t.dtype != dtype:
         raise PsispecError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.shape == shape:  # the common case: exactly the shape asked for
+        return
     need = 1
     for n in shape:
         need *= int(n)
-    if (exact and tuple(t.shape) != tuple(shape)) or t.numel() < need:
+    if exact or t.numel() < need:
         raise PsispecError(f"{name} must hold {tuple(shape)} elements, got {tuple(t.shape)}")
 
 
@@ -154,7 +156,7 @@ def _check_linear_out(out: dict, batch: int, B: int, dev):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()  # an int: ctypes passes it as the void* argument
 
 
 def _sampling(temperature, top_p, seed, step, request_base, flags):
@@ -162,9 +164,17 @@ def _sampling(temperature, top_p, seed, step, request_base, flags):
                             int(step) & 0xFFFFFFFF, int(request_base) & 0xFFFFFFFF, int(flags), 0)
 
 
+# the current device's current stream as a raw pointer (torch's own accessor when it has one:
+# torch.cuda.current_stream() builds a Stream object, a few microseconds per call)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream):
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def linear_workspace_bytes(batch, B, V, dtype) -> int:

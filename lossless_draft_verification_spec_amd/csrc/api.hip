@@ -530,7 +530,7 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
   // a few kilobytes of logits per request: one launch does the whole verify
   if (!use_topp && pl.nchunk == 1 &&
       (size_t)(2 * B + 1) * (size_t)V * elem_size(dtype) <= kSmallVerifyBytes)
-    return launch_verify_small(la, da, part, dtype, stream) == hipSuccess
+    return launch_verify_small(la, da, dtype, stream) == hipSuccess
                ? PSISPEC_OK
                : PSISPEC_EHIP;
 

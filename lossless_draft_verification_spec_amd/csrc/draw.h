@@ -116,6 +116,30 @@ __device__ inline double readlane_f64(double x, int lane) {
   return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), lane),
                           __builtin_amdgcn_readlane(__double2loint(x), lane));
 }
+// update_dpp on both halves of a double: lanes whose row or bank is masked off, or (bound_ctrl)
+// whose source lane lies outside the pattern, receive `old` (0 here: +0.0)
+template <int kCtrl, int kRowMask = 0xf, bool kBound = true>
+__device__ inline double dpp_upd_f64(double x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), kCtrl, kRowMask, 0xf, kBound);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), kCtrl, kRowMask, 0xf, kBound);
+  return __hiloint2double(hi, lo);
+}
+
+// Inclusive prefix sum over the wave's 64 lanes by DPP: within each row of 16 lanes, row_shr by
+// 1, 2, 4 and 8 (lanes shifted in from outside the row add 0); then lane 15's value goes to the
+// next row (row_bcast:15, rows 1 and 3) and lane 31's to rows 2 and 3 (row_bcast:31).
+__device__ inline double wave_incl_scan(double v) {
+  v += dpp_upd_f64<0x111>(v);       // row_shr:1
+  v += dpp_upd_f64<0x112>(v);       // row_shr:2
+  v += dpp_upd_f64<0x114>(v);       // row_shr:4
+  v += dpp_upd_f64<0x118>(v);       // row_shr:8
+  v += dpp_upd_f64<0x142, 0xa>(v);  // row_bcast:15
+  v += dpp_upd_f64<0x143, 0xc>(v);  // row_bcast:31
+  return v;
+}
+// the value of the lane below (0 in lane 0): wave_shr:1
+__device__ inline double wave_shr1(double v) { return dpp_upd_f64<0x138>(v); }
+
 __device__ inline double wave_sum_dpp(double v) {
   v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
@@ -179,8 +203,10 @@ __device__ inline double rho_estimate(const DrawArgs& a, const DrawDesc& d) {
   return d.factor * ep / eq;
 }
 
-// Draw chunk c of request r (every thread of a kThreads block calls it).
-template <typename T, bool kTopp>
+// Draw chunk c of request r (every thread of a kThreads block calls it).  kGrouped: the token pairs
+// are taken 4 at a time (registers for 5 waves per SIMD); the one-block verify, a single block,
+// lets the compiler interleave all 16 instead (latency, not occupancy, is what it is short of).
+template <typename T, bool kTopp, bool kGrouped = true>
 __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_ok) {
   __shared__ double tbl[kExpTable];
   __shared__ int s_excl[1024];
@@ -257,8 +283,10 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
         pair(run_at<T, e0 + 3>(rp), run_at<T, e0 + 3>(rq));
         // the group's sums are complete here (an empty asm that reads and writes them), so its
         // weights die before the next group starts
-        asm volatile("" : "+v"(Ep), "+v"(Eq), "+v"(Ap), "+v"(Aq));
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kGrouped) {
+          asm volatile("" : "+v"(Ep), "+v"(Eq), "+v"(Ap), "+v"(Aq));
+          __builtin_amdgcn_sched_barrier(0);
+        }
       };
       group(std::integral_constant<int, 0>{});
       group(std::integral_constant<int, 4>{});
@@ -339,14 +367,8 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
 // the intervals [lo, hi) tile [0, total) exactly; returns the block total.
 __device__ inline double block_scan(double x, double* s_wave, double* lo, double* hi) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  double incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  double excl = __shfl_up(incl, 1, 64);
-  if (lane == 0) excl = 0.0;
+  const double incl = wave_incl_scan(x);
+  const double excl = wave_shr1(incl);  // bit-identical to the inclusive prefix of the lane below
   __syncthreads();
   if (lane == 63) s_wave[wave] = incl;
   __syncthreads();

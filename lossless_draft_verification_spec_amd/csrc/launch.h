@@ -201,11 +201,12 @@ struct DrawArgs {
 hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t stream);
 
 // linear.hip -- small linear verifies (no nucleus, one chunk per row) in one launch: one block per
-// request computes its rows' pairs (to `part`), then runs the accept test, the draw pass and the
-// select.  Used when a request's rows hold at most kSmallVerifyBytes.
+// request stages its rows in LDS, computes their pairs, then runs the accept test, the draw pass
+// and the select on LDS copies of the rows and records.  Used when a request's rows hold at most
+// kSmallVerifyBytes.
 constexpr size_t kSmallVerifyBytes = 32768;
-hipError_t launch_verify_small(const LinearArgs& la, const DrawArgs& da, float2* part,
-                               psispec_dtype dtype, hipStream_t stream);
+hipError_t launch_verify_small(const LinearArgs& la, const DrawArgs& da, psispec_dtype dtype,
+                               hipStream_t stream);
 
 // kv.hip -- the KV commit after a verify
 constexpr int kMaxKvBlock = 1024;  // block positions of a commit (B or N)

@@ -8,12 +8,15 @@
 // from the start, discard everything after the first rejection).  The final draw (correction at
 // k < B, bonus from the block-end row at k = B) is left to the fp64 draw kernels.
 //
-// Small calls (a request's rows within kSmallVerifyBytes, no nucleus) are launch-latency bound: four
+// Small calls (a request's rows within kSmallVerifyBytes, no nucleus) are latency bound: four
 // launches of a few microseconds each for a few kilobytes of logits.  k_verify_small runs a
-// request's whole verify in one block instead: its rows' statistics (one wave per row, each row one
-// chunk), then the same device functions as the separate kernels, in the same order (accept test,
-// draw pass chunk by chunk, select).  The pairs are reduced by one wave instead of a block, so they
-// may differ from the separate kernels' in the last bit; every later step is the same code.
+// request's whole verify in one block instead: it copies the request's rows into LDS (one round of
+// loads), computes their statistics (one wave per row, each row one chunk), then runs the same
+// device functions as the separate kernels, in the same order (accept test, draw pass chunk by
+// chunk, select), on the request as a one-request call whose rows, pairs, statistics, descriptor
+// and draw records are LDS arrays: the steps hand over through LDS, not through global memory.
+// The pairs are reduced by one wave instead of a block, so they may differ from the separate
+// kernels' in the last bit; every later step is the same code.
 #include "launch.h"
 #include "decide.h"
 #include "draw.h"
@@ -38,57 +41,153 @@ __global__ __launch_bounds__(64) void k_combine_rows(RowSet rs, const float2* __
   if (threadIdx.x == 0) rowstat[row] = RowStat{lmax, row_status(lmax, Z), Z};
 }
 
+// DPP lane exchanges for the one-block verify's row reductions: quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror and row_mirror pair the 16 lanes of a row symmetrically, so after the
+// four steps every lane of a row holds the row's result; the four rows are then combined in order.
+template <int kCtrl>
+__device__ inline float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xf, 0xf, true));
+}
+__device__ inline float lane_f32(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ inline float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+}
+__device__ inline float wave_sum_f32(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
+}
+
+// LDS records of the one-block verify beside its rows: the draw's chunk and sub-chunk records (a
+// request's rows within kSmallVerifyBytes have at most 6 sub-chunks of 1024 tokens)
+constexpr int kSmallChunks = 8, kSmallSubs = 8;
+
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_verify_small(LinearArgs la, DrawArgs da,
-                                                           float2* __restrict__ part,
-                                                           int vec_ok_draw) {
+__global__ __launch_bounds__(kThreads) void k_verify_small(LinearArgs la, DrawArgs da, int vec_ok) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_rows[kSmallVerifyBytes];
+  __shared__ float2 s_pairs[2 * kMaxB + 1];
+  __shared__ RowStat s_rowstat[2 * kMaxB + 1];
+  __shared__ DrawDesc s_desc[1];
+  __shared__ int32_t s_ucount[1];
+  __shared__ double2 s_esum[kSmallChunks], s_suba[kSmallSubs];
+  __shared__ int32_t s_subn[kSmallSubs], s_suboff[kSmallSubs];
+  __shared__ double s_subsum[kSmallSubs];
   const int r = blockIdx.x;
-  const int B = la.B;
+  const int B = la.B, V = la.V, nrows = 2 * B + 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // the request's rows, one wave per row (the launcher checks that a row is one chunk)
-  for (int j = wave; j < 2 * B + 1; j += kThreads / 64) {
-    const int64_t row = j <= B ? (int64_t)r * (B + 1) + j : la.rs.nP + (int64_t)r * B + (j - B - 1);
-    if (row_skipped(la.rs, row)) continue;
-    const T* rp = row_ptr<T>(la.rs, row);
+  T* rows = reinterpret_cast<T*>(s_rows);
+  // the request's global row of local row j (p rows 0..B, then q rows 0..B-1)
+  auto grow = [&](int j) -> int64_t {
+    return j <= B ? (int64_t)r * (B + 1) + j : la.rs.nP + (int64_t)r * B + (j - B - 1);
+  };
+  // 1. the request's rows into LDS (one round of loads; a skipped row is not read)
+  if (vec_ok) {
+    constexpr int E = 16 / (int)sizeof(T);
+    const int nv = V / E;
+    for (int i = threadIdx.x; i < nrows * nv; i += kThreads) {
+      const int j = i / nv, x = i - j * nv;
+      const int64_t row = grow(j);
+      if (row_skipped(la.rs, row)) continue;
+      reinterpret_cast<u32x4*>(rows + (size_t)j * V)[x] =
+          reinterpret_cast<const u32x4*>(row_ptr<T>(la.rs, row))[x];
+    }
+  } else {
+    for (int i = threadIdx.x; i < nrows * V; i += kThreads) {
+      const int j = i / V, x = i - j * V;
+      const int64_t row = grow(j);
+      if (!row_skipped(la.rs, row)) rows[i] = row_ptr<T>(la.rs, row)[x];
+    }
+  }
+  // 2. the same device functions as the separate kernels, on this request alone (request 0 of a
+  //    one-request call whose rows, statistics, descriptor and draw records live in LDS; the
+  //    Philox request word and the outputs keep their place in the whole call)
+  LinearArgs l1 = la;
+  l1.rs.p = rows;
+  l1.rs.q = rows + (size_t)(B + 1) * V;
+  l1.rs.nP = B + 1;
+  l1.rs.nQ = B;
+  l1.rs.pstride = V;
+  l1.draft = la.draft + (int64_t)r * B;
+  l1.batch = 1;
+  l1.request_base = la.request_base + (uint32_t)r;
+  l1.part = s_pairs;
+  l1.rowstat = s_rowstat;
+  l1.rowstat_ready = 0;
+  l1.desc = s_desc;
+  l1.ucount = s_ucount;
+  l1.accept_len = la.accept_len + r;
+  l1.out_tokens = la.out_tokens + (int64_t)r * (B + 1);
+  l1.ratios = la.ratios ? la.ratios + (int64_t)r * B : nullptr;
+  l1.accept_mask = la.accept_mask ? la.accept_mask + r : nullptr;
+  DrawArgs d1 = da;
+  d1.rs = l1.rs;
+  d1.batch = 1;
+  d1.request_base = l1.request_base;
+  d1.rowstat = s_rowstat;
+  d1.desc = s_desc;
+  d1.esum = s_esum;
+  d1.suba = s_suba;
+  d1.subn = s_subn;
+  d1.suboff = s_suboff;
+  d1.subsum = s_subsum;
+  d1.ucount = s_ucount;
+  d1.upool = da.upool ? da.upool + (int64_t)r * kUncPool : nullptr;
+  d1.out_tokens = da.out_tokens + (int64_t)r * (B + 1);
+  d1.status = da.status ? da.status + r : nullptr;
+  __syncthreads();  // the rows are staged
+  // 3. the rows' pairs, one wave per row (the launcher checks that a row is one chunk)
+  for (int j = wave; j < nrows; j += kThreads / 64) {
+    if (row_skipped(l1.rs, j)) continue;
+    const T* rp = row_ptr<T>(l1.rs, j);
     float m = kNegBig, s = 0.f;
-    for (int x = lane; x < la.V; x += 64) {
+    for (int x = lane; x < V; x += 64) {
       const float f[1] = {to_f32(rp[x])};
       fold(f, m, s, la.c);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float m2 = __shfl_xor(m, off, 64);
-      const float s2 = __shfl_xor(s, off, 64);
-      os_combine(m, s, m2, s2, la.c);
-    }
-    if (lane == 0) part[row] = make_float2(m, s);
+    // the wave's pair: its maximum, then every lane's sum rescaled to it and added up (a lane
+    // without tokens holds (floor, 0) and adds 0; a NaN sum stays NaN)
+    const float M = wave_max_f32(m);
+    const float S = wave_sum_f32(s * __builtin_amdgcn_exp2f((m - M) * la.c));
+    if (lane == 0) s_pairs[j] = make_float2(M, S);
   }
   __syncthreads();  // every pair is written
-  decide_linear_request<T>(la, r);  // its first barrier follows the pair reads
-  __syncthreads();                   // the descriptor is written
-  for (int ch = 0; ch < da.nchunk_draw; ++ch) {
-    draw_pass_task<T, false>(da, r, ch, vec_ok_draw);
+  decide_linear_request<T>(l1, 0);  // its first barrier follows the pair reads
+  __syncthreads();                  // the descriptor is written
+  const int vec_lds = ((size_t)V * sizeof(T)) % 16 == 0;  // LDS rows are 16-byte aligned then
+  for (int ch = 0; ch < d1.nchunk_draw; ++ch) {
+    draw_pass_task<T, false, false>(d1, 0, ch, vec_lds);
     __syncthreads();  // the chunk's sums are written; the next chunk refills the LDS
   }
-  draw_select_request<T>(da, r);
+  draw_select_request<T>(d1, 0);
 }
 
 }  // namespace
 
-hipError_t launch_verify_small(const LinearArgs& la, const DrawArgs& da, float2* part,
-                               psispec_dtype dtype, hipStream_t stream) {
+hipError_t launch_verify_small(const LinearArgs& la, const DrawArgs& da, psispec_dtype dtype,
+                               hipStream_t stream) {
   if (la.batch == 0) return hipSuccess;
-  if (la.nchunk != 1 || la.use_topp) return hipErrorInvalidValue;
   const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
+  if (la.nchunk != 1 || la.use_topp || la.gath || la.B < 1 || la.B > kMaxB ||
+      (size_t)(2 * la.B + 1) * (size_t)la.V * es > kSmallVerifyBytes ||
+      da.nchunk_draw > kSmallChunks || da.nsub > kSmallSubs)
+    return hipErrorInvalidValue;
   const RowSet& rs = la.rs;
   const int aligned = ((size_t)rs.V * es) % 16 == 0 && ((size_t)rs.pstride * es) % 16 == 0 &&
                       ((uintptr_t)rs.p % 16) == 0 && ((uintptr_t)rs.q % 16) == 0;
   if (dtype == PSISPEC_BF16)
     PSISPEC_LAUNCH("verify_small", k_verify_small<bf16_t>, dim3((unsigned)la.batch),
-                   dim3(kThreads), 0, stream, la, da, part, aligned);
+                   dim3(kThreads), 0, stream, la, da, aligned);
   else
     PSISPEC_LAUNCH("verify_small", k_verify_small<float>, dim3((unsigned)la.batch),
-                   dim3(kThreads), 0, stream, la, da, part, aligned);
+                   dim3(kThreads), 0, stream, la, da, aligned);
   return hipGetLastError();
 }
 
