@@ -99,6 +99,16 @@ struct bf16_t {
   uint16_t bits;
 };
 
+// Barrier of a one-wave block: its lanes' LDS writes before this point are seen by their LDS
+// reads after it (one wave's LDS operations complete in order; the fences keep the compiler from
+// moving accesses across).  Unlike __syncthreads it does not wait for the wave's global loads in
+// flight, so a gather issued earlier keeps going while the wave works on LDS.
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // bf16 -> float: the 16 bits on top of a float (a shift or a mask).  Written as conversions so that
 // the compiler takes the values as canonical and forms three-operand maxima from them without
 // quieting every input first.

@@ -50,37 +50,55 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
   __shared__ double s_pown[kMaxNodes];
   __shared__ int s_first[kMaxNodes];
   __shared__ float2 s_pair[kStagePairs];
-  __shared__ float s_l[kMaxNodes];
 
-  // 0. the tree, every node's accept uniform (Philox of (request, c+1, accept)), the logit of each
-  //    node's token in its parent's row and the row pairs, loaded or computed by the whole wave up
-  //    front (the token gathers go out with the pair loads): the steps below then read LDS only
+  // 0. the tree, every node's accept uniform (Philox of (request, c+1, accept)) and the row pairs,
+  //    loaded or computed by the whole wave up front; then the logit of each node's token in its
+  //    parent's row, gathered into the lane that scores the node.  The block is one wave and syncs
+  //    with wave barriers, which do not wait for the gathers: they stay in flight through the row
+  //    statistics and the structure check, and only the ratios wait for them.
   for (int j = t; j < N; j += 64) {
-    const int v = par[j], tj = tok[j];
-    s_par[j] = v;
-    s_tok[j] = tj;
-    s_l[j] = (tj >= 0 && tj < V && v >= -1 && v < j) ? to_f32(row_ptr<T>(a.rs, row0 + v + 1)[tj])
-                                                      : 0.f;
+    s_par[j] = par[j];
+    s_tok[j] = tok[j];
     s_u[j] = philox_uniform(a.seed, a.request_base + (uint32_t)r, (uint32_t)(j + 1), kPurposeAccept,
                             a.step);
   }
   const bool staged = (int64_t)(N + 1) * a.nchunk <= kStagePairs;
   if (staged)
     for (int i = t; i < (N + 1) * a.nchunk; i += 64) s_pair[i] = a.part[row0 * a.nchunk + i];
-  __syncthreads();
+  wave_sync();
+  constexpr int kGl = kMaxNodes / 64;  // nodes per lane
+  float gl[kGl];                       // node t + 64 k's token logit
+#pragma unroll
+  for (int k = 0; k < kGl; ++k) {
+    const int j = t + 64 * k;
+    gl[k] = 0.f;
+    if (j < N) {
+      const int v = s_par[j], tj = s_tok[j];
+      if (tj >= 0 && tj < V && v >= -1 && v < j) gl[k] = to_f32(row_ptr<T>(a.rs, row0 + v + 1)[tj]);
+    }
+  }
 
   // 1. row statistics of the root and node rows (pairs in chunk order)
   int st = 0;
-  for (int j = t; j <= N; j += 64) {
-    const int64_t row = row0 + j;
-    const float2* pr = staged ? s_pair + j * a.nchunk : a.part + row * a.nchunk;
-    float lmax = kNegBig;
+  // (LDS and global pairs in separate branches: a pointer that may be either would be read by
+  // flat loads, whose waits also wait for the gathers)
+  auto pair_stats = [&](const float2* pr, float& lmax, double& Z) {
+    lmax = kNegBig;
     for (int k = 0; k < a.nchunk; ++k) lmax = fmaxf(lmax, pr[k].x);
-    double Z = 0.0;
+    Z = 0.0;
     for (int k = 0; k < a.nchunk; ++k) {
       const float2 pk = pr[k];
       Z += (double)pk.y * exp2((double)(pk.x - lmax) * (double)a.c);
     }
+  };
+  for (int j = t; j <= N; j += 64) {
+    const int64_t row = row0 + j;
+    float lmax;
+    double Z;
+    if (staged)
+      pair_stats(s_pair + j * a.nchunk, lmax, Z);
+    else
+      pair_stats(a.part + row * a.nchunk, lmax, Z);
     const int rs = row_status(lmax, Z);
     st |= rs;
     s_lmax[j] = lmax;
@@ -112,22 +130,25 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
       if (t == 0) s_st = bm ? PSISPEC_ST_BAD_PARENT : 0;
     }
   }
-  __syncthreads();
+  wave_sync();
 
   // 3. data-parallel node ratios.  An earlier sibling s of node j has the same parent row, so the
   //    probability it removes from j's residual is s's own probability p_own[s]: one gather per
   //    node, all in parallel, then the sibling sums read LDS.
-  for (int j = t; j < N; j += 64) {
+#pragma unroll
+  for (int k = 0; k < kGl; ++k) {
+    const int j = t + 64 * k;
+    if (j >= N) break;
     const int v = s_par[j], tj = s_tok[j];
     s_pown[j] = (tj >= 0 && tj < V && v >= -1 && v < j)
-                    ? node_prob(a, row0 + v + 1, s_lmax[v + 1], s_Z[v + 1], s_l[j])
+                    ? node_prob(a, row0 + v + 1, s_lmax[v + 1], s_Z[v + 1], gl[k])
                     : 0.0;
   }
   // first[s]: no earlier sibling of s carries s's token (each distinct removed token counts once).
   // With N <= 64, node s sits in lane s: one ballot per distinct parent gives every lane the mask
   // of its siblings, and each lane then visits only its earlier siblings, in index order (LDS
   // reads), so R takes the same subtractions in index order as the general form below.
-  __syncthreads();
+  wave_sync();
   if (N <= 64) {
     const int pj = t < N ? s_par[t] : -2, tj = t < N ? s_tok[t] : -1;
     uint64_t sib = 0;
@@ -142,7 +163,7 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
     int first = 1;
     for (uint64_t m = earlier; m; m &= m - 1) first &= s_tok[__builtin_ctzll(m)] != tj;
     if (t < N) s_first[t] = first;
-    __syncthreads();
+    wave_sync();
     double ratio = 0.0;
     if (t < N) {
       if (tj < 0 || tj >= V) st |= PSISPEC_ST_BAD_TOKEN;
@@ -170,7 +191,7 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
       for (int s2 = 0; s2 < N; ++s2) first &= !(s2 < j && s_par[s2] == v && s_tok[s2] == tj);
       s_first[j] = first;
     }
-    __syncthreads();
+    wave_sync();
     for (int j = t; j < N; j += 64) {
       const int v = s_par[j];
       double ratio = 0.0;
@@ -197,7 +218,7 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) st |= __shfl_xor(st, off, 64);
-  __syncthreads();
+  wave_sync();
 
   // 4. the walk.  At each node the children are scanned in index order by the whole wave, 64 at a
   //    time: a ballot finds the first accepted child; the valid tokens of the children rejected
