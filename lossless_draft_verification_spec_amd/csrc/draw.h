@@ -203,10 +203,11 @@ __device__ inline double rho_estimate(const DrawArgs& a, const DrawDesc& d) {
   return d.factor * ep / eq;
 }
 
-// Draw chunk c of request r (every thread of a kThreads block calls it).  kGrouped: the token pairs
-// are taken 4 at a time (registers for 5 waves per SIMD); the one-block verify, a single block,
-// lets the compiler interleave all 16 instead (latency, not occupancy, is what it is short of).
-template <typename T, bool kTopp, bool kGrouped = true>
+// Draw chunk c of request r (every thread of a kThreads block calls it).  kShared: the block's
+// waves share each sub-chunk (wave w takes tokens 4w .. 4w+3 of every lane's 16), for the one-block
+// verify, whose few sub-chunks would leave most waves idle; a sub-chunk with a token in the band is
+// then left to the select's token-by-token sum instead of the pool.
+template <typename T, bool kTopp, bool kShared = false>
 __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_ok) {
   __shared__ double tbl[kExpTable];
   __shared__ int s_excl[1024];
@@ -231,6 +232,66 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub_per_chunk = a.chunk_elems_draw / kSub;
   double Ep = 0.0, Eq = 0.0;
+  if constexpr (kShared) {
+    __shared__ double2 s_sum[kThreads / 64];
+    __shared__ int s_band[kThreads / 64];
+    const int sub_end = min((c + 1) * sub_per_chunk, a.nsub);
+    for (int sub = c * sub_per_chunk; sub < sub_end; ++sub) {
+      const int x0 = sub * kSub + lane * kPerLane + 4 * wave;
+      double Ap = 0.0, Aq = 0.0;
+      bool anyamb = false;
+      float fp[4], fq[4];
+      load_run<T, 4>(prow, x0, a.V, vec_ok, fp);
+      if (has_q) {
+        load_run<T, 4>(qrow, x0, a.V, vec_ok, fq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          double tp = fma((double)fp[e], c256, -mp), tq = fma((double)fq[e], c256, -mq);
+          if constexpr (kTopp) {
+            if (!(fp[e] >= v.thr_p)) tp = -__builtin_huge_val();
+            if (!(fq[e] >= v.thr_q)) tq = -__builtin_huge_val();
+          }
+          const double ep = exp2_256(tp, tbl), eq = exp2_256(tq, tbl);
+          Ep += ep;
+          Eq += eq;
+          const double dt = tp - tq;
+          const bool pos = dt > t_hi;
+          anyamb = anyamb | ((dt >= t_lo) & !pos);
+          const double pf = pos ? 1.0 : 0.0;
+          Ap = fma(pf, ep, Ap);
+          Aq = fma(pf, eq, Aq);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          double ep = term<kTopp>(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl);
+          if (nexcl && excluded(x0 + e, s_excl, nexcl)) ep = 0.0;
+          Ap += ep;
+        }
+      }
+      Ap = wave_sum_dpp(Ap);
+      Aq = wave_sum_dpp(Aq);
+      const int band = __ballot(anyamb) != 0;
+      if (lane == 0) {
+        s_sum[wave] = make_double2(Ap, Aq);
+        s_band[wave] = band;
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        double2 A = s_sum[0];
+        int any = s_band[0];
+        for (int w = 1; w < kThreads / 64; ++w) {
+          A.x += s_sum[w].x;
+          A.y += s_sum[w].y;
+          any |= s_band[w];
+        }
+        a.suba[(int64_t)r * a.nsub + sub] = A;
+        a.subn[(int64_t)r * a.nsub + sub] = any;
+        a.suboff[(int64_t)r * a.nsub + sub] = -1;  // with band tokens: summed by the select
+      }
+      __syncthreads();
+    }
+  } else
   for (int j = wave; j < sub_per_chunk; j += kThreads / 64) {
     const int sub = c * sub_per_chunk + j;
     if (sub >= a.nsub) break;
@@ -283,10 +344,8 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
         pair(run_at<T, e0 + 3>(rp), run_at<T, e0 + 3>(rq));
         // the group's sums are complete here (an empty asm that reads and writes them), so its
         // weights die before the next group starts
-        if constexpr (kGrouped) {
-          asm volatile("" : "+v"(Ep), "+v"(Eq), "+v"(Ap), "+v"(Aq));
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        asm volatile("" : "+v"(Ep), "+v"(Eq), "+v"(Ap), "+v"(Aq));
+        __builtin_amdgcn_sched_barrier(0);
       };
       group(std::integral_constant<int, 0>{});
       group(std::integral_constant<int, 4>{});

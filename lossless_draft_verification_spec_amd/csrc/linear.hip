@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void k_verify_small(LinearArgs la, DrawAr
   __syncthreads();                  // the descriptor is written
   const int vec_lds = ((size_t)V * sizeof(T)) % 16 == 0;  // LDS rows are 16-byte aligned then
   for (int ch = 0; ch < d1.nchunk_draw; ++ch) {
-    draw_pass_task<T, false, false>(d1, 0, ch, vec_lds);
+    draw_pass_task<T, false, true>(d1, 0, ch, vec_lds);
     __syncthreads();  // the chunk's sums are written; the next chunk refills the LDS
   }
   draw_select_request<T>(d1, 0);
