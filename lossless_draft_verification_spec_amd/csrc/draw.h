@@ -203,6 +203,32 @@ __device__ inline double rho_estimate(const DrawArgs& a, const DrawDesc& d) {
   return d.factor * ep / eq;
 }
 
+// Sum of the weights of a lane's n consecutive tokens x0 .. x0+n-1 (no q row), the removed tokens
+// counted 0.  The removed list is scanned once per run, into a bit mask of the run's positions;
+// the tokens are then tested against it only in a wave where some lane has one (few tokens are
+// removed: most waves have none).  Every lane of the wave must call it.
+template <bool kTopp, int n>
+__device__ inline double run_mass(const float (&fp)[n], int x0, const RowView& v, double inv_T,
+                                  const double* tbl, const int* excl, int nexcl) {
+  uint32_t xm = 0;
+  for (int i = 0; i < nexcl; ++i) {
+    const uint32_t o = (uint32_t)(excl[i] - x0);
+    if (o < (uint32_t)n) xm |= 1u << o;
+  }
+  double A = 0.0;
+  if (__ballot(xm != 0)) {
+#pragma unroll
+    for (int e = 0; e < n; ++e) {
+      const double ep = term<kTopp>(fp[e], v.lmax_p, v.thr_p, inv_T, tbl);
+      A += ((xm >> e) & 1u) ? 0.0 : ep;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < n; ++e) A += term<kTopp>(fp[e], v.lmax_p, v.thr_p, inv_T, tbl);
+  }
+  return A;
+}
+
 // Draw chunk c of request r (every thread of a kThreads block calls it).  kShared: the block's
 // waves share each sub-chunk (wave w takes tokens 4w .. 4w+3 of every lane's 16), for the one-block
 // verify, whose few sub-chunks would leave most waves idle; a sub-chunk with a token in the band is
@@ -262,12 +288,7 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
           Aq = fma(pf, eq, Aq);
         }
       } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          double ep = term<kTopp>(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl);
-          if (nexcl && excluded(x0 + e, s_excl, nexcl)) ep = 0.0;
-          Ap += ep;
-        }
+        Ap = run_mass<kTopp, 4>(fp, x0, v, a.inv_T, tbl, s_excl, nexcl);
       }
       Ap = wave_sum_dpp(Ap);
       Aq = wave_sum_dpp(Aq);
@@ -395,12 +416,7 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
     } else {
       float fp[kPerLane];
       load_run<T, kPerLane>(prow, x0, a.V, vec_ok, fp);
-#pragma unroll
-      for (int e = 0; e < kPerLane; ++e) {
-        double ep = term<kTopp>(fp[e], v.lmax_p, v.thr_p, a.inv_T, tbl);
-        if (nexcl && excluded(x0 + e, s_excl, nexcl)) ep = 0.0;
-        Ap += ep;
-      }
+      Ap = run_mass<kTopp, kPerLane>(fp, x0, v, a.inv_T, tbl, s_excl, nexcl);
     }
     Ap = wave_sum_dpp(Ap);
     Aq = wave_sum_dpp(Aq);
