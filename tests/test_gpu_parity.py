@@ -381,6 +381,27 @@ def test_tree_temperature_top_p(T, top_p):
     t.check()
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_tree_removed_token_runs(dtype):
+    """Wide root, every child rejected (its token made improbable), so the final draw removes many
+    tokens: a contiguous block crossing several 16-token runs (many removed bits in one run), and
+    scattered tokens at run and row edges (0, 15, 16, V-1).  The draw pass marks them per run."""
+    batch, N, V = 3, 40, 4096
+    gen = torch.Generator().manual_seed(77)
+    p = torch.randn(batch, N + 1, V, generator=gen) * 2.0
+    parent = np.full((batch, N), -1, dtype=np.int32)
+    tokens = np.zeros((batch, N), dtype=np.int32)
+    tokens[0] = np.arange(1000, 1000 + N)
+    tokens[1] = np.array([0, 15, 16, V - 1, 31, 32, 33, 2047, 2048] + list(range(500, 500 + N - 9)))
+    tokens[2] = np.concatenate([np.arange(8, 8 + N // 2), np.arange(V - N // 2, V)])
+    for b in range(batch):
+        p[b, 0, torch.from_numpy(tokens[b]).long()] = -30.0  # root row: the children's tokens
+    p = p.to(dtype).to(DEV)
+    t = _tree_compare(p, parent, tokens, 4, steps=range(4))
+    print(t)
+    t.check()
+
+
 def test_tree_bad_parent_status():
     p, parent, tokens = _rand_tree(3, 6, 50, torch.float32, seed=22)
     parent[1, 3] = 5  # parent after child
