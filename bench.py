@@ -150,23 +150,24 @@ def roofline_mfma(kernel, flops, us, peaks, traffic=None):
 # ------------------------------------------------------------------------------------------------
 def measure_peaks(torch, pkg):
     """The HBM read bandwidth of 16-byte nontemporal loads over a 4 GiB buffer (16x the last-level
-    cache) and the bf16 MFMA issue rate with no memory traffic, each the best of five launches
-    (library kernel timing)."""
+    cache), the best over three segment sizes per workgroup and three launches each, and the bf16
+    MFMA issue rate with no memory traffic, the best of five launches (library kernel timing)."""
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
-    blocks = 256 * 16
-    out = torch.empty(blocks, dtype=torch.int32, device="cuda")
-    pkg.peak_read(buf, out, blocks)
+    sweep = (256 * 16, 256 * 64, 256 * 128)  # 1 MiB, 256 KiB and 128 KiB per workgroup
+    out = torch.empty(max(sweep), dtype=torch.int32, device="cuda")
+    pkg.peak_read(buf, out, sweep[0])
     torch.cuda.synchronize()
     best_read = None
-    for _ in range(5):
-        pkg.timing_enable(True)
-        pkg.peak_read(buf, out, blocks)
-        k = pkg.timing_read()
-        pkg.timing_enable(False)
-        us = 1e3 * k["peak_read"][0] / max(1, k["peak_read"][1])
-        best_read = us if best_read is None else min(best_read, us)
+    for blocks in sweep:
+        for _ in range(3):
+            pkg.timing_enable(True)
+            pkg.peak_read(buf, out, blocks)
+            k = pkg.timing_read()
+            pkg.timing_enable(False)
+            us = 1e3 * k["peak_read"][0] / max(1, k["peak_read"][1])
+            best_read = us if best_read is None else min(best_read, us)
     del buf
     torch.cuda.empty_cache()
     mblocks, iters = 256 * 4, 4000
@@ -187,11 +188,12 @@ def measure_peaks(torch, pkg):
                 mfma_bf16_tflops=round(flops / (best_mfma / 1e6) / 1e12, 1),
                 mfma_flops=flops, mfma_us=round(best_mfma, 2),
                 datasheet={"hbm_gbs": HBM_PEAK_GBS, "mfma_bf16_tflops": MFMA_BF16_PEAK_TFLOPS},
-                method="best of 5 launches; read: every 16-byte word of a 4 GiB buffer once, "
-                       "nontemporal 16-byte loads, 4096 workgroups of 256 threads each streaming "
-                       "a contiguous 1 MiB segment, 8 loads in flight per thread; mfma: 1024 "
-                       "workgroups of 4 waves, 4000 x 16 independent v_mfma_f32_32x32x16_bf16 "
-                       "per wave, no memory traffic")
+                method="read: every 16-byte word of a 4 GiB buffer once, nontemporal 16-byte "
+                       "loads, 4096, 16384 or 32768 workgroups of 256 threads each streaming a "
+                       "contiguous 1 MiB, 256 KiB or 128 KiB segment, 8 loads in flight per "
+                       "thread, best of 3 launches of each; mfma: 1024 workgroups of 4 waves, "
+                       "4000 x 16 independent v_mfma_f32_32x32x16_bf16 per wave, no memory "
+                       "traffic, best of 5 launches")
 
 
 # ------------------------------------------------------------------------------------------------
