@@ -182,11 +182,13 @@ def test_linear_first_from_target_layout():
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("batch,B,V,flags", [(3, 64, 8, 0), (6, 6, 200, PSISPEC_FIRST_FROM_TARGET),
-                                             (40, 8, 64, 0)])
+                                             (40, 8, 64, 0), (4, 1, 2700, 0), (2, 1, 5000, 0)])
 def test_linear_one_launch_path(dtype, batch, B, V, flags):
     """Calls whose rows hold at most 32 KiB per request run the whole verify in one launch: many
-    rows per request (B = 64: 129 rows over the block's four waves), the Uno layout, and many small
-    requests, against the oracle."""
+    rows per request (B = 64: 129 rows over the block's four waves), the Uno layout, many small
+    requests, and rows of several 1024-token sub-chunks (V = 2700: three; V = 5000 in bf16: five,
+    over two draw chunks; in fp32 it exceeds 32 KiB and takes the separate kernels), against the
+    oracle."""
     p, q, d = _rand_linear(batch, B, V, dtype, seed=B * 31 + V)
     if flags:
         q[:, 0] = p[:, 0]
