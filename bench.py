@@ -280,12 +280,19 @@ def run_tree(name, steps, warmup, ncalls, torch, pkg, workloads, peaks):
     elem = 2 if preset.dtype == torch.bfloat16 else 4
     dt = pkg.PSISPEC_BF16 if elem == 2 else pkg.PSISPEC_F32
     ws = torch.empty(pkg.tree_workspace_bytes(b, N, V, dt), dtype=torch.uint8, device="cuda")
+    # the drafter's fan-out, known to the caller from its branching schedule: passed as the bound on
+    # children per node, so that the residual passes for wider nodes are not launched
+    fan = 0
+    if sampled:
+        par = sets[0].parent[0].cpu().tolist()
+        fan = max(par.count(v) for v in set(par))
 
     def call(s):
         inp = sets[s % R]
         o = pkg.psispec_verify_tree(inp.p, inp.parent, inp.node_tokens, preset.depth,
                                     temperature=preset.T, top_p=preset.top_p, seed=inp.seed,
-                                    step=s, workspace=ws, q_logits=inp.q if sampled else None)
+                                    step=s, workspace=ws, q_logits=inp.q if sampled else None,
+                                    max_children=fan)
         return o["accept_len"]
 
     m = measure(torch, pkg, call, steps, warmup, ncalls)
@@ -293,8 +300,8 @@ def run_tree(name, steps, warmup, ncalls, torch, pkg, workloads, peaks):
     torch.cuda.empty_cache()
     row_bytes = b * (N + 1) * V * elem * (2 if sampled else 1)
     ms = m["ms_per_step"]
-    rule = "candidates drawn from the draft (recursive rejection)" if sampled else \
-        "top-4 candidates"
+    rule = f"candidates drawn from the draft (recursive rejection, at most {fan} children per " \
+        "node, given)" if sampled else "top-4 candidates"
     return dict(workload=f"{name}: tree verify batch={b} N={N} nodes depth<={preset.depth} V={V} "
                          f"{'bf16' if elem == 2 else 'fp32'} logits, T={preset.T}, {rule}",
                 ms_per_step=round(ms, 5),

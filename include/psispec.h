@@ -63,6 +63,13 @@ typedef enum { PSISPEC_F32 = 0, PSISPEC_BF16 = 1 } psispec_dtype;
 /* flags */
 #define PSISPEC_FIRST_FROM_TARGET 1u /* Uno layout: position 0 is the AR's own sample and is always
                                         kept ([alphalab] walkthrough step 1); q row 0 is not read */
+/* Tree verify with q_logits only: PSISPEC_MAX_CHILDREN(k), 1 <= k <= 8, says that no node has more
+   than k children (the drafter's branching), so the residual chain is built for k children only
+   and its passes for more are not launched.  A node with more than k children is then reported
+   with PSISPEC_ST_BAD_PARENT.  0 (not given) means 8.  Every other call rejects these bits. */
+#define PSISPEC_MAX_CHILDREN_SHIFT 4
+#define PSISPEC_MAX_CHILDREN_MASK (0xfu << PSISPEC_MAX_CHILDREN_SHIFT)
+#define PSISPEC_MAX_CHILDREN(k) ((uint32_t)(k) << PSISPEC_MAX_CHILDREN_SHIFT)
 
 /* per-request status bits */
 #define PSISPEC_ST_NONFINITE 1   /* a row read by the request holds NaN/+Inf or no finite logit */
@@ -79,7 +86,7 @@ typedef struct {
   uint64_t seed;         /* Philox key */
   uint32_t step;         /* Philox counter word 3 */
   uint32_t request_base; /* global id of request 0 (counter word 0 = request_base + request) */
-  uint32_t flags;        /* PSISPEC_FIRST_FROM_TARGET or 0 */
+  uint32_t flags;        /* PSISPEC_FIRST_FROM_TARGET, PSISPEC_MAX_CHILDREN(k) or 0 */
   uint32_t reserved;     /* must be 0 */
 } psispec_sampling;
 

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libpsispec.so")
 
 PSISPEC_F32, PSISPEC_BF16 = 0, 1
 PSISPEC_FIRST_FROM_TARGET = 1
+PSISPEC_MAX_CHILDREN_SHIFT = 4  # flags bits 4..7: bound on children per node (sampled tree)
 ST_NONFINITE, ST_BAD_TOKEN, ST_Q_ZERO, ST_RESID_ZERO, ST_BAD_PARENT = 1, 2, 4, 8, 16
 ST_BAD_KEEP = 32
 
@@ -263,14 +264,16 @@ def psispec_verify_linear_noalloc(p_logits: torch.Tensor, q_logits: torch.Tensor
 def psispec_verify_tree(p_logits: torch.Tensor, parent: torch.Tensor, node_tokens: torch.Tensor,
                         max_depth: int, temperature: float = 1.0, top_p: float = 1.0, seed: int = 0,
                         step: int = 0, request_base: int = 0, q_logits: torch.Tensor | None = None,
-                        workspace: torch.Tensor | None = None, out: dict | None = None,
-                        stream=None) -> dict:
+                        max_children: int = 0, workspace: torch.Tensor | None = None,
+                        out: dict | None = None, stream=None) -> dict:
     """Tree verify.  p_logits [batch][N+1][V] (row 0 = root, row j+1 = node j), parent and
     node_tokens int32 [batch][N].  With q_logits ([batch][N+1][V], p's dtype: row v+1 is the
     distribution node v's children were drawn from) the candidates are taken as drawn from the
     draft and verified by recursive rejection; without it, as chosen (e.g. top-k).  Returns
     accept_len, accept_nodes [batch][max_depth], out_tokens [batch][max_depth+1], node_ratios
-    [batch][N], status."""
+    [batch][N], status.  max_children (with q_logits only, 1..8; 0 = not given): no node has more
+    children than this, so the verify skips the residual passes for more; a node with more is
+    reported as ST_BAD_PARENT."""
     if p_logits.dim() != 3:
         raise PsispecError("p_logits must be [batch][N+1][V]")
     batch, Np1, V = p_logits.shape
@@ -305,7 +308,12 @@ def psispec_verify_tree(p_logits: torch.Tensor, parent: torch.Tensor, node_token
         raise PsispecError("unsupported sizes (N must be 1..1024)")
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    s = _sampling(temperature, top_p, seed, step, request_base, 0)
+    if not 0 <= int(max_children) <= 8:
+        raise PsispecError("max_children must be 0..8")
+    if max_children and q_logits is None:
+        raise PsispecError("max_children applies to trees drawn from the draft (q_logits)")
+    s = _sampling(temperature, top_p, seed, step, request_base,
+                  int(max_children) << PSISPEC_MAX_CHILDREN_SHIFT)
     rc = lib().psispec_verify_tree(
         _ptr(p_logits), _ptr(q_logits), dt, _ptr(parent), _ptr(node_tokens), batch, N, V,
         int(max_depth), ctypes.byref(s), _ptr(out["accept_len"]), _ptr(out["accept_nodes"]),

@@ -148,12 +148,18 @@ TreeQPlan make_treeq_plan(int batch, int N, int V, size_t es) {
   return tp;
 }
 
-bool sampling_ok(const psispec_sampling* s) {
+// children_bound: the call accepts PSISPEC_MAX_CHILDREN (the tree verify)
+bool sampling_ok(const psispec_sampling* s, bool children_bound = false) {
   if (!s) return false;
   if (!(s->temperature > 0.0) || !isfinite(s->temperature)) return false;
   if (!(s->top_p > 0.0) || !(s->top_p <= 1.0)) return false;
   if (s->reserved != 0) return false;
-  if (s->flags & ~PSISPEC_FIRST_FROM_TARGET) return false;
+  const uint32_t known =
+      PSISPEC_FIRST_FROM_TARGET | (children_bound ? PSISPEC_MAX_CHILDREN_MASK : 0u);
+  if (s->flags & ~known) return false;
+  if (((s->flags & PSISPEC_MAX_CHILDREN_MASK) >> PSISPEC_MAX_CHILDREN_SHIFT) >
+      (uint32_t)kMaxSampledChildren)
+    return false;
   return true;
 }
 
@@ -310,8 +316,11 @@ psispec_status verify_tree_sampled(const void* p_logits, const void* q_logits, p
   ta.accept_nodes = accept_nodes;
   ta.out_tokens = out_tokens;
   ta.node_ratios = node_ratios;
+  // the caller's bound on children per node, if given: the levels past it would find no work
+  const int bound = (int)((s->flags & PSISPEC_MAX_CHILDREN_MASK) >> PSISPEC_MAX_CHILDREN_SHIFT);
+  ta.max_children = bound > 0 ? bound : kMaxSampledChildren;
   if (launch_tree_children(ta, stream) != hipSuccess) return PSISPEC_EHIP;
-  for (int level = 0; level < kMaxSampledChildren; ++level) {
+  for (int level = 0; level < ta.max_children; ++level) {
     if (level == 1 && launch_tree_resolve(ta, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
     if (launch_tree_chain_pass(ta, level, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
   }
@@ -578,7 +587,8 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
   if (dtype != PSISPEC_F32 && dtype != PSISPEC_BF16) return PSISPEC_EDTYPE;
   if (batch < 0 || N < 1 || N > 1024 || V < 1 || max_depth < 1 || max_depth > 64)
     return PSISPEC_EINVAL;
-  if (!sampling_ok(s) || (s->flags & PSISPEC_FIRST_FROM_TARGET)) return PSISPEC_EINVAL;
+  if (!sampling_ok(s, true) || (s->flags & PSISPEC_FIRST_FROM_TARGET)) return PSISPEC_EINVAL;
+  if (!q_logits && (s->flags & PSISPEC_MAX_CHILDREN_MASK)) return PSISPEC_EINVAL;
   if (batch == 0) return PSISPEC_OK;
   if (!p_logits || !parent || !node_tokens || !accept_len || !accept_nodes || !out_tokens)
     return PSISPEC_EINVAL;

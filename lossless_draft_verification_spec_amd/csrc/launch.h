@@ -152,7 +152,8 @@ struct TreeQArgs {
   uint32_t step, request_base;
   const RowStat* rowstat;   // every p and q row (combined)
   const ToppStat* topp;
-  int32_t* nchild;          // [nP] children per node row (written by the level-0 pass)
+  int max_children;         // most children per node: the caller's bound, else kMaxSampledChildren
+  int32_t* nchild;          // [nP] children per node row (written by k_tree_children)
   double2* e_part;          // [nP][nchunk_c] (sum e_p, sum e_q) over the kept tokens
   double* s_part;           // [kMaxSampledChildren - 1][nP][nchunk_c] residual masses
   BandPart* band;           // [nP][nchunk_c] level 0's split of S_1

@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
     const int64_t w = blockIdx.x;
     const int64_t g = w / a.nchunk_c;
     const int m = a.nchild[g];
-    if (m < 2 || m > kMaxSampledChildren) return;
+    if (m < 2 || m > a.max_children) return;
     exp_table_fill(tbl);  // read after do_item's first barrier
     do_item(g, (int)(w - g * a.nchunk_c));
     return;
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_chain(TreeQArgs a, int level,
       const int m = a.nchild[g];
       // the resolve's flag, read for every item; used where m >= 2 only
       const int redo = level == 1 ? a.fb[g * a.nchunk_c + j / a.rs.nP] : 1;
-      if (m >= mmin && m <= kMaxSampledChildren && redo) s_items[atomicAdd(&s_cnt, 1)] = threadIdx.x;
+      if (m >= mmin && m <= a.max_children && redo) s_items[atomicAdd(&s_cnt, 1)] = threadIdx.x;
     }
     __syncthreads();
     const int nit = s_cnt;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(64) void k_tree_resolve(TreeQArgs a) {
   exp_table_fill(tbl);
   const int64_t g = blockIdx.x;
   const int m = a.nchild[g];
-  if (m < 2 || m > kMaxSampledChildren) return;
+  if (m < 2 || m > a.max_children) return;
   const int lane = threadIdx.x;
   const int64_t prow = g, qrow = a.rs.nP + g;
   const T* pr = row_ptr<T>(a.rs, prow);
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(64) void k_tree_resolve(TreeQArgs a) {
 __global__ __launch_bounds__(64) void k_tree_chain_final(TreeQArgs a) {
   const int64_t g = blockIdx.x;
   const int m = a.nchild[g];
-  if (m < 1 || m > kMaxSampledChildren) return;
+  if (m < 1 || m > a.max_children) return;
   const int64_t nP = a.rs.nP;
   const int lane = threadIdx.x;
   // the normalisers (two or more children) and S_1 .. S_{m-1}: every array's entries in one round of
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
   }
   __syncthreads();
 
-  // 1. structure: parents precede children, depth within max_depth, at most kMaxSampledChildren
+  // 1. structure: parents precede children, depth within max_depth, at most a.max_children
   //    children per node (the level-0 pass counted them); row statistics of the request's rows
   int bad = 0, st = 0;
   for (int j = t; j < N; j += 64) {
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
     if (d > a.max_depth) bad = 1;
   }
   for (int j = t; j <= N; j += 64) {
-    if (a.nchild[row0 + j] > kMaxSampledChildren) bad = 1;
+    if (a.nchild[row0 + j] > a.max_children) bad = 1;
     st |= a.rowstat[row0 + j].st | a.rowstat[nP + row0 + j].st;
   }
   {
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
       int i = 1;
       for (int s = 0; s < j; ++s) i += s_par[s] == v;
       const int64_t g = row0 + v + 1;
-      if (i <= kMaxSampledChildren) {
+      if (i <= a.max_children) {
         const NodeChain& ch = a.chain[g];
         const double pp = gathered_prob<T>(a, g, tj, ch.Ep);
         const double qq = gathered_prob<T>(a, nP + g, tj, ch.Eq);

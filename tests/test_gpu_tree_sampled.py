@@ -1,6 +1,7 @@
 """Parity of the tree verify with candidates drawn from the draft (recursive rejection) on the GPU
 (through the C ABI) with the CPU oracle: small, ragged and full-size trees, temperature and top-p,
-draft rows equal to the target rows, too many children, non-finite rows."""
+draft rows equal to the target rows, too many children, non-finite rows, the caller's bound on
+children per node."""
 import numpy as np
 import pytest
 import torch
@@ -16,7 +17,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _compare(tin, T=1.0, top_p=1.0, steps=(0,), rows=None, seed=None, q=None):
+def _compare(tin, T=1.0, top_p=1.0, steps=(0,), rows=None, seed=None, q=None, max_children=0):
     p, q = tin.p, (tin.q if q is None else q)
     ph, qh = host_logits(p), host_logits(q)
     par = tin.parent.cpu().numpy()
@@ -27,7 +28,7 @@ def _compare(tin, T=1.0, top_p=1.0, steps=(0,), rows=None, seed=None, q=None):
     tally = Tally()
     for step in steps:
         out = psispec_verify_tree(p, tin.parent, tin.node_tokens, D, temperature=T, top_p=top_p,
-                                  seed=seed, step=step, q_logits=q)
+                                  seed=seed, step=step, q_logits=q, max_children=max_children)
         torch.cuda.synchronize()
         g = {k: v.cpu().numpy() for k, v in out.items()}
         o = oracle_tree_sampled_requests(ph, qh, par, tok, rows, D, float(T), float(top_p), seed, step)
@@ -200,3 +201,59 @@ def test_chain_passes_over_several_grid_rounds():
         compare_tree(tally, g, o, rows, 1.0)
     print(tally)
     tally.check()
+
+
+def _verify(tin, **kw):
+    out = psispec_verify_tree(tin.p, tin.parent, tin.node_tokens, tin.preset.depth, seed=tin.seed,
+                              q_logits=tin.q, **kw)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("N,branching,bounds", [
+    (30, (4, 2, 2, 1, 1, 1, 1, 1), (4, 5, 8)), (7, (1,) * 7, (1, 2)), (40, (8, 2, 1, 1), (8,)),
+    (20, (2, 3, 1, 1), (3, 6))])
+def test_max_children_bound_same_outputs(dtype, N, branching, bounds):
+    """A bound on children per node at or above the tree's largest fan-out gives the outputs of the
+    call without it, bit for bit (the passes it skips have no node to work on), and they agree with
+    the oracle."""
+    from dataclasses import replace
+    pr = replace(workloads.PRESETS["c4s"], dtype=dtype, depth=8)
+    tin = workloads.make_tree_sampled(pr, device=DEV, batch=4, V=3001, N=N, branching=branching)
+    for step in (0, 1):
+        base = _verify(tin, step=step)
+        for k in bounds:
+            got = _verify(tin, step=step, max_children=k)
+            for key in base:
+                np.testing.assert_array_equal(got[key], base[key], err_msg=f"{key} bound {k}")
+    t = _compare(tin, steps=range(2), max_children=bounds[0])
+    print(t)
+    t.check()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_max_children_bound_below_fanout(dtype):
+    """Requests holding a node with more children than the bound are reported with ST_BAD_PARENT;
+    the other requests of the same call keep the outputs of the call without the bound."""
+    from dataclasses import replace
+    pr = replace(workloads.PRESETS["c4s"], dtype=dtype, depth=8)
+    wide = workloads.make_tree_sampled(pr, device=DEV, batch=2, V=2000, N=24,
+                                       branching=(4, 2, 2, 1, 1))
+    narrow = workloads.make_tree_sampled(pr, device=DEV, batch=2, V=2000, N=24, rotation=1,
+                                         branching=(2, 2, 2, 1, 1))
+    cat = lambda a, b: torch.cat([a, b]).contiguous()
+    mixed = replace(wide, p=cat(wide.p, narrow.p), q=cat(wide.q, narrow.q),
+                    parent=cat(wide.parent, narrow.parent),
+                    node_tokens=cat(wide.node_tokens, narrow.node_tokens))
+    base = _verify(mixed, top_p=0.9)
+    for k in (2, 3):
+        got = _verify(mixed, top_p=0.9, max_children=k)
+        assert (got["status"][:2] & ST_BAD_PARENT).all()
+        assert not (got["status"][2:] & ST_BAD_PARENT).any()
+        for key in base:
+            np.testing.assert_array_equal(got[key][2:], base[key][2:], err_msg=f"{key} bound {k}")
+    got = _verify(mixed, top_p=0.9, max_children=1)
+    assert (got["status"] & ST_BAD_PARENT).all()
+    t = _compare(mixed, top_p=0.9, steps=range(2))
+    t.check()
