@@ -10,13 +10,14 @@
 //
 // Small calls (a request's rows within kSmallVerifyBytes, no nucleus) are latency bound: four
 // launches of a few microseconds each for a few kilobytes of logits.  k_verify_small runs a
-// request's whole verify in one block instead: it copies the request's rows into LDS (one round of
-// loads), computes their statistics (one wave per row, each row one chunk), then runs the same
-// device functions as the separate kernels, in the same order (accept test, draw pass chunk by
-// chunk, select), on the request as a one-request call whose rows, pairs, statistics, descriptor
-// and draw records are LDS arrays: the steps hand over through LDS, not through global memory.
-// The pairs are reduced by one wave instead of a block, so they may differ from the separate
-// kernels' in the last bit; every later step is the same code.
+// request's whole verify in one block instead: it copies the request's rows into LDS (one round
+// of loads), computes their statistics (each row one chunk, reduced by a wave, or by 16 lanes when
+// there are more rows than waves), then runs the same device functions as the separate kernels, in
+// the same order (accept test, draw pass chunk by chunk, select), on the request as a one-request
+// call whose rows, pairs, statistics, descriptor and draw records are LDS arrays: the steps hand
+// over through LDS, not through global memory.  The pairs are reduced by a
+// wave or 16 lanes instead of a block, so they may differ from the separate kernels' in the last
+// bit; every later step is the same code.
 #include "launch.h"
 #include "decide.h"
 #include "draw.h"
@@ -42,8 +43,9 @@ __global__ __launch_bounds__(64) void k_combine_rows(RowSet rs, const float2* __
 }
 
 // DPP lane exchanges for the one-block verify's row reductions: quad_perm [1,0,3,2], quad_perm
-// [2,3,0,1], row_half_mirror and row_mirror pair the 16 lanes of a row symmetrically, so after the
-// four steps every lane of a row holds the row's result; the four rows are then combined in order.
+// [2,3,0,1], row_half_mirror and row_mirror pair the 16 lanes of a DPP row symmetrically, so after
+// the four steps every lane of the row holds the row's result; for a whole wave the four rows are
+// then combined in order.
 template <int kCtrl>
 __device__ inline float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xf, 0xf, true));
@@ -51,18 +53,24 @@ __device__ inline float dpp_f32(float x) {
 __device__ inline float lane_f32(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
-__device__ inline float wave_max_f32(float v) {
+__device__ inline float row16_max_f32(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(v));
   v = fmaxf(v, dpp_f32<0x4E>(v));
   v = fmaxf(v, dpp_f32<0x141>(v));
-  v = fmaxf(v, dpp_f32<0x140>(v));
-  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+  return fmaxf(v, dpp_f32<0x140>(v));
 }
-__device__ inline float wave_sum_f32(float v) {
+__device__ inline float row16_sum_f32(float v) {
   v += dpp_f32<0xB1>(v);
   v += dpp_f32<0x4E>(v);
   v += dpp_f32<0x141>(v);
-  v += dpp_f32<0x140>(v);
+  return v + dpp_f32<0x140>(v);
+}
+__device__ inline float wave_max_f32(float v) {
+  v = row16_max_f32(v);
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+}
+__device__ inline float wave_sum_f32(float v) {
+  v = row16_sum_f32(v);
   return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
 
@@ -143,20 +151,41 @@ __global__ __launch_bounds__(kThreads) void k_verify_small(LinearArgs la, DrawAr
   d1.out_tokens = da.out_tokens + (int64_t)r * (B + 1);
   d1.status = da.status ? da.status + r : nullptr;
   __syncthreads();  // the rows are staged
-  // 3. the rows' pairs, one wave per row (the launcher checks that a row is one chunk)
-  for (int j = wave; j < nrows; j += kThreads / 64) {
-    if (row_skipped(l1.rs, j)) continue;
-    const T* rp = row_ptr<T>(l1.rs, j);
-    float m = kNegBig, s = 0.f;
-    for (int x = lane; x < V; x += 64) {
-      const float f[1] = {to_f32(rp[x])};
-      fold(f, m, s, la.c);
+  // 3. the rows' pairs (the launcher checks that a row is one chunk): with more rows than waves,
+  //    each 16-lane row of the block reduces one logit row in one round (all lanes take part in the
+  //    DPP steps; a lane past the rows or in a skipped row holds (floor, 0)); else one wave per row
+  if (nrows > kThreads / 64) {
+    const int grp = threadIdx.x >> 4, l16 = threadIdx.x & 15;
+    for (int j0 = 0; j0 < nrows; j0 += kThreads / 16) {
+      const int j = j0 + grp;
+      const bool live = j < nrows && !row_skipped(l1.rs, j);
+      float m = kNegBig, s = 0.f;
+      if (live) {
+        const T* rp = row_ptr<T>(l1.rs, j);
+        for (int x = l16; x < V; x += 16) {
+          const float f[1] = {to_f32(rp[x])};
+          fold(f, m, s, la.c);
+        }
+      }
+      const float M = row16_max_f32(m);
+      const float S = row16_sum_f32(s * __builtin_amdgcn_exp2f((m - M) * la.c));
+      if (live && l16 == 0) s_pairs[j] = make_float2(M, S);
     }
-    // the wave's pair: its maximum, then every lane's sum rescaled to it and added up (a lane
-    // without tokens holds (floor, 0) and adds 0; a NaN sum stays NaN)
-    const float M = wave_max_f32(m);
-    const float S = wave_sum_f32(s * __builtin_amdgcn_exp2f((m - M) * la.c));
-    if (lane == 0) s_pairs[j] = make_float2(M, S);
+  } else {
+    for (int j = wave; j < nrows; j += kThreads / 64) {
+      if (row_skipped(l1.rs, j)) continue;
+      const T* rp = row_ptr<T>(l1.rs, j);
+      float m = kNegBig, s = 0.f;
+      for (int x = lane; x < V; x += 64) {
+        const float f[1] = {to_f32(rp[x])};
+        fold(f, m, s, la.c);
+      }
+      // the wave's pair: its maximum, then every lane's sum rescaled to it and added up (a lane
+      // without tokens holds (floor, 0) and adds 0; a NaN sum stays NaN)
+      const float M = wave_max_f32(m);
+      const float S = wave_sum_f32(s * __builtin_amdgcn_exp2f((m - M) * la.c));
+      if (lane == 0) s_pairs[j] = make_float2(M, S);
+    }
   }
   __syncthreads();  // every pair is written
   decide_linear_request<T>(l1, 0);  // its first barrier follows the pair reads
