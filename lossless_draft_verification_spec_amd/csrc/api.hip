@@ -27,7 +27,7 @@ struct Plan {
   int nchunk, chunk_elems;          // main pass split of a row
   int nchunk_draw, chunk_elems_draw, nsub;
   size_t off_part, off_rowstat, off_topp, off_desc, off_excl, off_esum, off_suba, off_subn,
-      off_subsum, off_suboff, off_upool, off_ucount, off_rec, off_list, off_extra;
+      off_subsum, off_suboff, off_upool, off_rec, off_list, off_extra;
   size_t total;
 };
 
@@ -97,8 +97,6 @@ Plan make_plan(int64_t rows, int64_t batch, int V, size_t es, int excl_stride, i
   off = align_up(off + sizeof(int32_t) * (size_t)batch * pl.nsub);
   pl.off_upool = off;
   off = align_up(off + (pool ? sizeof(double2) * (size_t)batch * kUncPool : 0));
-  pl.off_ucount = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)batch);
   pl.off_rec = off;
   off = align_up(off + (bounded ? sizeof(BoundRec) * (size_t)batch * pl.nsub : 0));
   // the count, then (256 bytes on) the list of draws left to the exact pass
@@ -311,7 +309,6 @@ psispec_status verify_tree_sampled(const void* p_logits, const void* q_logits, p
   ta.fb = carve<int32_t>(workspace, tp.off_fb);
   ta.chain = carve<NodeChain>(workspace, tp.off_chain);
   ta.desc = desc;
-  ta.ucount = carve<int32_t>(workspace, pl.off_ucount);
   ta.accept_len = accept_len;
   ta.accept_nodes = accept_nodes;
   ta.out_tokens = out_tokens;
@@ -349,7 +346,6 @@ psispec_status verify_tree_sampled(const void* p_logits, const void* q_logits, p
   da.subn = carve<int32_t>(workspace, pl.off_subn);
   da.suboff = carve<int32_t>(workspace, pl.off_suboff);
   da.upool = carve<double2>(workspace, pl.off_upool);
-  da.ucount = carve<int32_t>(workspace, pl.off_ucount);
   da.out_tokens = out_tokens;
   da.status = status;
   if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
@@ -503,7 +499,6 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
   la.topp = topp;
   la.rowstat = rowstat;
   la.desc = desc;
-  la.ucount = carve<int32_t>(workspace, pl.off_ucount);
   la.accept_len = accept_len;
   la.out_tokens = out_tokens;
   la.ratios = ratios;
@@ -532,7 +527,6 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
   da.subn = carve<int32_t>(workspace, pl.off_subn);
   da.suboff = carve<int32_t>(workspace, pl.off_suboff);
   da.upool = carve<double2>(workspace, pl.off_upool);
-  da.ucount = carve<int32_t>(workspace, pl.off_ucount);
   da.out_tokens = out_tokens;
   da.status = status;
 
@@ -552,8 +546,7 @@ psispec_status psispec_verify_linear(const void* p_logits, const void* q_logits,
                         hipSuccess)
       return PSISPEC_EHIP;
   }
-  if (launch_decide_linear(la, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
-  if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
+  if (launch_decide_draw(la, da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
   return PSISPEC_OK;
 }
 
@@ -636,7 +629,6 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
   ta.topp = topp;
   ta.rowstat = rowstat;
   ta.desc = desc;
-  ta.ucount = carve<int32_t>(workspace, pl.off_ucount);
   ta.excl = excl;
   ta.accept_len = accept_len;
   ta.accept_nodes = accept_nodes;
@@ -667,7 +659,6 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
   da.subn = carve<int32_t>(workspace, pl.off_subn);
   da.suboff = carve<int32_t>(workspace, pl.off_suboff);
   da.upool = carve<double2>(workspace, pl.off_upool);
-  da.ucount = carve<int32_t>(workspace, pl.off_ucount);
   da.out_tokens = out_tokens;
   da.status = status;
   if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
@@ -788,7 +779,6 @@ psispec_status psispec_sample_drafts(const void* ar_logits, int64_t ar_stride,
   da.subn = carve<int32_t>(workspace, pl.off_subn);
   da.suboff = carve<int32_t>(workspace, pl.off_suboff);
   da.upool = nullptr;  // draws without a q row keep no pool
-  da.ucount = carve<int32_t>(workspace, pl.off_ucount);
   da.out_tokens = draft_tokens;
   da.status = status;
   da.list = bounded ? list : nullptr;  // the draws the bounded pass could not settle
@@ -962,7 +952,6 @@ psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, cons
   la.rowstat_ready = 1;
   la.gath = gath;
   la.desc = desc;
-  la.ucount = carve<int32_t>(workspace, pl.off_ucount);
   la.accept_len = accept_len;
   la.out_tokens = out_tokens;
   la.ratios = ratios;
@@ -1003,7 +992,6 @@ psispec_status psispec_lmhead_verify(const void* h_ar, const void* h_draft, cons
   da.subn = carve<int32_t>(workspace, pl.off_subn);
   da.suboff = carve<int32_t>(workspace, pl.off_suboff);
   da.upool = carve<double2>(workspace, pl.off_upool);
-  da.ucount = carve<int32_t>(workspace, pl.off_ucount);
   da.subsum = carve<double>(workspace, pl.off_subsum);
   da.out_tokens = out_tokens;
   da.status = status;

@@ -44,6 +44,11 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
   __shared__ double s_Z[2 * kMaxB + 1];
   __shared__ int s_st[2 * kMaxB + 1];
   __shared__ float2 s_pair[kStagePairs];
+  // a row's statistics: to the workspace (unless quiet) and to the caller's LDS copy (local row j)
+  auto put_stat = [&](int j, int64_t row, const RowStat& rs) {
+    if (!a.quiet) a.rowstat[row] = rs;
+    if (a.rowstat_local) a.rowstat_local[j] = rs;
+  };
 
   // 1. finish the row statistics (rows 0..B of p, then rows 0..B-1 of q).  When the request's pairs
   //    fit in LDS: one lane per row; else (LM-head column tiles at large B) the wave reduces each
@@ -64,6 +69,7 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
       s_lmax[j] = rw.lmax;
       s_Z[j] = rw.Z;
       s_st[j] = rw.st;
+      if (a.rowstat_local) a.rowstat_local[j] = rw;
     }
   } else if ((2 * B + 1) * a.nchunk <= kStagePairs) {
     // the request's pairs: p rows then q rows, each a contiguous run of the workspace, loaded by
@@ -93,7 +99,7 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
       s_lmax[j] = lmax;
       s_Z[j] = Z;
       s_st[j] = st;
-      a.rowstat[row] = RowStat{lmax, st, Z};
+      put_stat(j, row, RowStat{lmax, st, Z});
     }
   } else {
     for (int j = 0; j < 2 * B + 1; ++j) {
@@ -114,7 +120,7 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
         s_lmax[j] = lmax;
         s_Z[j] = Z;
         s_st[j] = st;
-        a.rowstat[row] = RowStat{lmax, st, Z};
+        put_stat(j, row, RowStat{lmax, st, Z});
       }
     }
   }
@@ -162,7 +168,7 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
     const double u = philox_uniform(a.seed, a.request_base + (uint32_t)r, (uint32_t)t,
                                      kPurposeAccept, a.step);
     acc = u < ratio;
-    if (a.ratios) a.ratios[(int64_t)r * B + t] = (float)ratio;
+    if (a.ratios && !a.quiet) a.ratios[(int64_t)r * B + t] = (float)ratio;
   }
   const uint64_t mask = __ballot(acc);
   const uint64_t full = B == 64 ? ~0ull : ((1ull << B) - 1ull);
@@ -171,11 +177,15 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
   for (int off = 32; off >= 1; off >>= 1) st |= __shfl_xor(st, off, 64);
 
   // 3. kept prefix; slot k is filled by the final draw, later slots are discarded (-1)
-  if (t < B) a.out_tokens[(int64_t)r * Bp1 + t] = t < k ? d : -1;
-  if (t == 0) a.out_tokens[(int64_t)r * Bp1 + B] = -1;  // block-end slot: the draw fills it if k == B
+  if (!a.quiet) {
+    if (t < B) a.out_tokens[(int64_t)r * Bp1 + t] = t < k ? d : -1;
+    if (t == 0) a.out_tokens[(int64_t)r * Bp1 + B] = -1;  // block-end slot: the draw fills it if k == B
+  }
   if (t == 0) {
-    a.accept_len[r] = k;
-    if (a.accept_mask) a.accept_mask[r] = mask & full;
+    if (!a.quiet) {
+      a.accept_len[r] = k;
+      if (a.accept_mask) a.accept_mask[r] = mask & full;
+    }
     DrawDesc dd;
     dd.prow = (int32_t)(prow0 + k);
     dd.qrow = k < B ? (int32_t)(qrow0 + k) : -1;
@@ -186,8 +196,8 @@ __device__ inline void decide_linear_request(const LinearArgs& a, int r) {
     dd.ph_req = r;
     dd.purpose = kPurposeDraw;
     dd.factor = 1.0;
-    a.desc[r] = dd;
-    a.ucount[r] = 0;
+    if (!a.quiet) a.desc[r] = dd;
+    if (a.desc_local) *a.desc_local = dd;
   }
 }
 

@@ -229,25 +229,28 @@ __device__ inline double run_mass(const float (&fp)[n], int x0, const RowView& v
   return A;
 }
 
-// Draw chunk c of request r (every thread of a kThreads block calls it).  kShared: the block's
-// waves share each sub-chunk (wave w takes tokens 4w .. 4w+3 of every lane's 16), for the one-block
-// verify, whose few sub-chunks would leave most waves idle; a sub-chunk with a token in the band is
-// then left to the select's token-by-token sum instead of the pool.
+// Draw chunk c of request r, given its description d, the stopping rows' view v and (with a q row)
+// the normaliser ratio rho estimated from the HBM pass; tbl is the exp table, filled before the
+// call (its first block barrier orders the fill).  Every thread of a kThreads block calls it.
+// kShared: the block's waves share each sub-chunk (wave w takes tokens 4w .. 4w+3 of every lane's
+// 16), for the one-block verify, whose few sub-chunks would leave most waves idle; a sub-chunk with
+// a token in the band is then left to the select's token-by-token sum instead of the pool.
+// Uncertain-sign tokens go to the chunk's own slice of the request's pool (kUncPool / nchunk_draw
+// entries, handed out by an LDS counter), so the pool needs no counter in global memory.
 template <typename T, bool kTopp, bool kShared = false>
-__device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_ok) {
-  __shared__ double tbl[kExpTable];
+__device__ inline void draw_pass_run(const DrawArgs& a, int r, int c, int vec_ok, const DrawDesc& d,
+                                     const RowView& v, double rho, const double* tbl) {
   __shared__ int s_excl[1024];
   __shared__ double2 s_part[kThreads / 64];
-  exp_table_fill(tbl);
-  const DrawDesc d = a.desc[r];
-  const RowView v = row_view(a, d);
+  __shared__ int s_ucnt;  // pool entries of the chunk's slice handed out
   const T* prow = row_ptr<T>(a.rs, d.prow);
   const bool has_q = d.qrow >= 0;
   const T* qrow = has_q ? row_ptr<T>(a.rs, d.qrow) : nullptr;
   const int nexcl = has_q ? 0 : min(d.nexcl, 1024);
   for (int i = threadIdx.x; i < nexcl; i += kThreads)
     s_excl[i] = a.excl[(int64_t)r * a.excl_stride + i];
-  const double rho = has_q ? rho_estimate(a, d) : 0.0;
+  if (threadIdx.x == 0) s_ucnt = 0;
+  const int slice = kUncPool / a.nchunk_draw;
   // exponent-domain form of the band: e_p (1 - kBand) > rho e_q (1 + kBand) is
   // t_p - t_q > 256 log2 rho + 256 log2((1 + kBand) / (1 - kBand)), t = 256 log2(e) (l - lmax) / T
   const double c256 = a.inv_T * k256Log2e;
@@ -398,9 +401,10 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
         }
         total = __shfl(before, 63, 64);
         before -= unc;
-        if (lane == 0) seg = atomicAdd(a.ucount + r, total);
+        if (lane == 0) seg = atomicAdd(&s_ucnt, total);
         seg = __shfl(seg, 0, 64);
-        if (seg + total > kUncPool) seg = -1;  // pool full: this sub-chunk is summed token by token
+        // slice full: this sub-chunk is summed token by token
+        seg = seg + total > slice ? -1 : c * slice + seg;
         if (seg >= 0 && umask) {
           double2* dst = a.upool + (int64_t)r * kUncPool + seg + before;
           // the few uncertain tokens re-read their logits (cached): no register copy of the run
@@ -438,6 +442,16 @@ __device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_o
     }
     a.esum[(int64_t)r * a.nchunk_draw + c] = make_double2(sp, sq);
   }
+}
+
+// Draw chunk c of request r from the description and row statistics in global memory.
+template <typename T, bool kTopp, bool kShared = false>
+__device__ inline void draw_pass_task(const DrawArgs& a, int r, int c, int vec_ok) {
+  __shared__ double tbl[kExpTable];
+  exp_table_fill(tbl);
+  const DrawDesc d = a.desc[r];
+  draw_pass_run<T, kTopp, kShared>(a, r, c, vec_ok, d, row_view(a, d),
+                                   d.qrow >= 0 ? rho_estimate(a, d) : 0.0, tbl);
 }
 
 // Fixed-order scan of one double per thread across the block.  Returns the exclusive prefix in

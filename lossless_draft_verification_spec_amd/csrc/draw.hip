@@ -32,6 +32,7 @@
 //                  masses locates u' S, then a block scan over that sub-chunk's 1024 weights
 //                  picks the token.
 #include "launch.h"
+#include "decide.h"
 #include "draw.h"
 
 namespace psispec {
@@ -73,24 +74,79 @@ __global__ __launch_bounds__(kThreads) void k_draw_select(DrawArgs a) {
   }
 }
 
+// The linear verify's accept test fused with the draw pass: block (r, c) runs request r's accept
+// test (wave 0, on the row pass's pairs) into LDS, then draws chunk c of the stopping row(s) from
+// those copies.  The test is repeated by each of the request's nchunk_draw blocks (a few hundred
+// bytes of pairs and two gathered logits per position); the chunk-0 block also writes the call's
+// outputs, the row statistics and the description that the select reads.  Against an accept-test
+// launch followed by the draw pass this saves a launch and the pass's dependent reads of the
+// description and then of the stopping rows' statistics.
+template <typename T, bool kTopp>
+__global__ __launch_bounds__(kThreads, kDrawPassWaves) void k_decide_draw(LinearArgs la, DrawArgs da,
+                                                                          int vec_ok) {
+  __shared__ double tbl[kExpTable];
+  __shared__ RowStat s_rs[2 * kMaxB + 1];
+  __shared__ DrawDesc s_d;
+  exp_table_fill(tbl);  // read after the barriers below
+  const int r = blockIdx.x / da.nchunk_draw;
+  const int c = blockIdx.x - r * da.nchunk_draw;
+  LinearArgs l = la;
+  l.rowstat_local = s_rs;
+  l.desc_local = &s_d;
+  l.quiet = c != 0;
+  decide_linear_request<T>(l, r);
+  __syncthreads();  // the description and the statistics are in LDS
+  const DrawDesc d = s_d;
+  const int k = d.pos, qj = la.B + 1 + k;  // local rows of the stopping p and q rows
+  const bool has_q = d.qrow >= 0;
+  RowView v;
+  v.lmax_p = s_rs[k].lmax;
+  v.thr_p = kTopp ? la.topp[d.prow].thr : -__builtin_huge_valf();
+  v.lmax_q = has_q ? s_rs[qj].lmax : 0.f;
+  v.thr_q = has_q ? (kTopp ? la.topp[d.qrow].thr : -__builtin_huge_valf()) : 0.f;
+  double rho = 0.0;
+  if (has_q) {  // as rho_estimate computes it from the workspace copies
+    double ep = s_rs[k].Z, eq = s_rs[qj].Z;
+    if (kTopp) {
+      ep *= la.topp[d.prow].M;
+      eq *= la.topp[d.qrow].M;
+    }
+    rho = d.factor * ep / eq;
+  }
+  draw_pass_run<T, kTopp>(da, r, c, vec_ok, d, v, rho, tbl);
+}
+
 constexpr unsigned kListPassBlocks = 1024;   // grid of the pass over listed draws
 constexpr unsigned kListSelectBlocks = 256;  // grid of the select over listed draws
 
 
 }  // namespace
 
+namespace {
+
+int draw_vec_ok(const DrawArgs& a, psispec_dtype dtype) {
+  const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
+  return ((size_t)a.V * es) % 16 == 0 && ((size_t)a.rs.pstride * es) % 16 == 0 &&
+         ((uintptr_t)a.rs.p % 16) == 0 && ((uintptr_t)a.rs.q % 16) == 0;
+}
+
+hipError_t launch_draw_select(const DrawArgs& a, psispec_dtype dtype, hipStream_t stream) {
+  unsigned sgrid = (unsigned)a.batch;
+  if (a.list) sgrid = sgrid < kListSelectBlocks ? sgrid : kListSelectBlocks;
+  if (dtype == PSISPEC_BF16)
+    PSISPEC_LAUNCH("draw_select", k_draw_select<bf16_t>, dim3(sgrid), dim3(kThreads), 0, stream, a);
+  else
+    PSISPEC_LAUNCH("draw_select", k_draw_select<float>, dim3(sgrid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   unsigned grid = (unsigned)((int64_t)a.batch * a.nchunk_draw);
-  unsigned sgrid = (unsigned)a.batch;
-  if (a.list) {
-    grid = grid < kListPassBlocks ? grid : kListPassBlocks;
-    sgrid = sgrid < kListSelectBlocks ? sgrid : kListSelectBlocks;
-  }
-  const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
-  const int vec_ok = ((size_t)a.V * es) % 16 == 0 &&
-                     ((size_t)a.rs.pstride * es) % 16 == 0 && ((uintptr_t)a.rs.p % 16) == 0 &&
-                     ((uintptr_t)a.rs.q % 16) == 0;
+  if (a.list) grid = grid < kListPassBlocks ? grid : kListPassBlocks;
+  const int vec_ok = draw_vec_ok(a, dtype);
   const bool bf = dtype == PSISPEC_BF16, tp = a.use_topp, li = a.list != nullptr;
   auto kern = bf ? (tp ? (li ? k_draw_pass<bf16_t, true, true> : k_draw_pass<bf16_t, true, false>)
                        : (li ? k_draw_pass<bf16_t, false, true> : k_draw_pass<bf16_t, false, false>))
@@ -99,11 +155,23 @@ hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t strea
   PSISPEC_LAUNCH("draw_pass", kern, dim3(grid), dim3(kThreads), 0, stream, a, vec_ok);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (dtype == PSISPEC_BF16)
-    PSISPEC_LAUNCH("draw_select", k_draw_select<bf16_t>, dim3(sgrid), dim3(kThreads), 0, stream, a);
-  else
-    PSISPEC_LAUNCH("draw_select", k_draw_select<float>, dim3(sgrid), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_draw_select(a, dtype, stream);
+}
+
+hipError_t launch_decide_draw(const LinearArgs& la, const DrawArgs& da, psispec_dtype dtype,
+                              hipStream_t stream) {
+  if (da.batch == 0) return hipSuccess;
+  if (da.list || la.gath || la.rowstat_ready || la.batch != da.batch || la.use_topp != da.use_topp)
+    return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((int64_t)da.batch * da.nchunk_draw);
+  const int vec_ok = draw_vec_ok(da, dtype);
+  const bool bf = dtype == PSISPEC_BF16, tp = da.use_topp;
+  auto kern = bf ? (tp ? k_decide_draw<bf16_t, true> : k_decide_draw<bf16_t, false>)
+                 : (tp ? k_decide_draw<float, true> : k_decide_draw<float, false>);
+  PSISPEC_LAUNCH("decide_draw", kern, dim3(grid), dim3(kThreads), 0, stream, la, da, vec_ok);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_draw_select(da, dtype, stream);
 }
 
 }  // namespace psispec

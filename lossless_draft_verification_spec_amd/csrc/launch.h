@@ -52,11 +52,17 @@ struct LinearArgs {
   int rowstat_ready;  // rowstat already holds every row's statistics (launch_combine_rows)
   const float* gath;  // logit at each row's draft token (LM-head epilogue), or null: read the rows
   DrawDesc* desc;
-  int32_t* ucount;
   int32_t* accept_len;
   int32_t* out_tokens;
   float* ratios;
   uint64_t* accept_mask;
+  // the accept test fused with the draw pass: the statistics of the request's rows (local row j:
+  // p rows 0..B, then q rows) and its draw description also go to these LDS copies; quiet: no
+  // output, statistic or description is written to global memory (another block of the request
+  // writes them)
+  RowStat* rowstat_local;
+  DrawDesc* desc_local;
+  int quiet;
 };
 hipError_t launch_decide_linear(const LinearArgs& a, psispec_dtype dtype, hipStream_t stream);
 // Row statistics from many per-chunk pairs (the LM-head column tiles), one wave per row.
@@ -111,7 +117,6 @@ struct TreeArgs {
   const ToppStat* topp;
   RowStat* rowstat;
   DrawDesc* desc;
-  int32_t* ucount;
   int32_t* excl;      // [batch][N] excluded tokens of the stopping node
   int32_t* accept_len;
   int32_t* accept_nodes;
@@ -160,7 +165,6 @@ struct TreeQArgs {
   int32_t* fb;              // [nP][nchunk_c] 1: the level-1 pass recomputes the chunk
   NodeChain* chain;         // [nP]
   DrawDesc* desc;
-  int32_t* ucount;
   int32_t* accept_len;
   int32_t* accept_nodes;
   int32_t* out_tokens;
@@ -189,8 +193,8 @@ struct DrawArgs {
   double2* suba;      // [batch][nsub] per sub-chunk sums of e_p, e_q over positive tokens
   int32_t* subn;      // [batch][nsub] uncertain-sign tokens per sub-chunk
   int32_t* suboff;    // [batch][nsub] pool offset of the sub-chunk's uncertain tokens, -1 = none kept
-  double2* upool;     // [batch][kUncPool] exact (e_p, e_q) of uncertain-sign tokens
-  int32_t* ucount;    // [batch] pool entries handed out (zeroed by the decide kernels)
+  double2* upool;     // [batch][kUncPool] exact (e_p, e_q) of uncertain-sign tokens, chunk c
+                      // of a draw in entries [c s, (c + 1) s), s = kUncPool / nchunk_draw
   double* subsum;     // [batch][nsub] sub-chunk masses (written by the select)
   int32_t* out_tokens;
   int32_t* status;
@@ -200,6 +204,10 @@ struct DrawArgs {
   const int32_t* count;
 };
 hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t stream);
+// The linear verify's accept test and draw pass in one launch (block (r, c) decides request r and
+// draws chunk c; the chunk-0 block writes the outputs), then the select.
+hipError_t launch_decide_draw(const LinearArgs& la, const DrawArgs& da, psispec_dtype dtype,
+                              hipStream_t stream);
 
 // linear.hip -- small linear verifies (no nucleus, one chunk per row) in one launch: one block per
 // request stages its rows in LDS, computes their pairs, then runs the accept test, the draw pass

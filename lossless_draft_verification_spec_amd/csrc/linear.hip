@@ -84,7 +84,6 @@ __global__ __launch_bounds__(kThreads) void k_verify_small(LinearArgs la, DrawAr
   __shared__ float2 s_pairs[2 * kMaxB + 1];
   __shared__ RowStat s_rowstat[2 * kMaxB + 1];
   __shared__ DrawDesc s_desc[1];
-  __shared__ int32_t s_ucount[1];
   __shared__ double2 s_esum[kSmallChunks], s_suba[kSmallSubs];
   __shared__ int32_t s_subn[kSmallSubs], s_suboff[kSmallSubs];
   __shared__ double s_subsum[kSmallSubs];
@@ -130,7 +129,6 @@ __global__ __launch_bounds__(kThreads) void k_verify_small(LinearArgs la, DrawAr
   l1.rowstat = s_rowstat;
   l1.rowstat_ready = 0;
   l1.desc = s_desc;
-  l1.ucount = s_ucount;
   l1.accept_len = la.accept_len + r;
   l1.out_tokens = la.out_tokens + (int64_t)r * (B + 1);
   l1.ratios = la.ratios ? la.ratios + (int64_t)r * B : nullptr;
@@ -146,7 +144,6 @@ __global__ __launch_bounds__(kThreads) void k_verify_small(LinearArgs la, DrawAr
   d1.subn = s_subn;
   d1.suboff = s_suboff;
   d1.subsum = s_subsum;
-  d1.ucount = s_ucount;
   d1.upool = da.upool ? da.upool + (int64_t)r * kUncPool : nullptr;
   d1.out_tokens = da.out_tokens + (int64_t)r * (B + 1);
   d1.status = da.status ? da.status + r : nullptr;

@@ -271,7 +271,6 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
     dd.purpose = kPurposeDraw;
     dd.factor = 1.0;
     a.desc[r] = dd;
-    a.ucount[r] = 0;
   }
 }
 

@@ -532,7 +532,6 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
     dd.purpose = kPurposeDraw;
     dd.factor = m >= 1 ? a.chain[g].c[m] : 1.0;
     a.desc[r] = dd;
-    a.ucount[r] = 0;
   }
 }
 
