@@ -505,6 +505,8 @@ def peak_read(buf: torch.Tensor, out: torch.Tensor, blocks: int, stream=None):
     """Read every 16-byte word of `buf` once (measured HBM read ceiling); out: uint32/int32 [blocks]."""
     _dev(buf, "buf")
     _dev(out, "out")
+    if out.numel() < blocks or out.element_size() != 4:
+        raise PsispecError("out must hold one 32-bit word per block")
     _check(lib().psispec_peak_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
                                    int(blocks), _stream(stream)), "psispec_peak_read")
 
