@@ -169,6 +169,29 @@ def test_draw_regimes(regime, dtype):
     t.check()
 
 
+@pytest.mark.parametrize("batch,B,V", [(2, 2, 151936), (3, 4, 40013)])
+def test_draw_pool_slices_kept_and_overflowing(batch, B, V):
+    """Draft rows that are the target rows with 30% of the positions' logits permuted among
+    themselves: the normalisers are equal, so every untouched token's residual sign lies in the
+    band (p' = q' there) and goes to the draw pass's pool, while the permuted tokens make the drafts
+    rejected often.  At V = 151,936 and batch 2 each of the 38 draw chunks owns 215 pool entries and
+    nearly every sub-chunk overflows its slice (the select then sums it token by token); at
+    V = 40,013 and batch 3 the slices hold 819 entries, about what a sub-chunk brings, so some fit
+    and some do not.  Every token must match the oracle."""
+    g = torch.Generator(device="cpu").manual_seed(V % 1000 + batch)
+    p = (torch.randn(batch, B + 1, V, generator=g) * 3.0).to(torch.bfloat16)
+    q = p[:, :B].clone()
+    for r in range(batch):
+        for i in range(B):
+            idx = torch.nonzero(torch.rand(V, generator=g) < 0.3).flatten()
+            q[r, i, idx] = q[r, i, idx[torch.randperm(idx.numel(), generator=g)]]
+    d = workloads.sample_drafts(q.float(), 1.0, 1.0, g)
+    t = _run_and_compare(p.to(DEV), q.to(DEV), d.to(DEV), steps=range(6))
+    print(t)
+    assert t.decisions > 0
+    t.check()
+
+
 def test_linear_first_from_target_layout():
     batch, B, V = 8, 6, 2048
     p, q, d = _rand_linear(batch, B, V, torch.bfloat16, seed=3)
