@@ -634,7 +634,6 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
   ta.accept_nodes = accept_nodes;
   ta.out_tokens = out_tokens;
   ta.node_ratios = node_ratios;
-  if (launch_decide_tree(ta, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
 
   DrawArgs da{};
   da.rs = rs;
@@ -661,6 +660,9 @@ psispec_status psispec_verify_tree(const void* p_logits, const void* q_logits, p
   da.upool = carve<double2>(workspace, pl.off_upool);
   da.out_tokens = out_tokens;
   da.status = status;
+  if (N <= 64)  // the walk runs in each draw block: one launch fewer
+    return launch_decide_tree_draw(ta, da, dtype, stream) == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
+  if (launch_decide_tree(ta, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
   if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
   return PSISPEC_OK;
 }

@@ -184,6 +184,10 @@ __device__ inline double term(float l, float lmax, float thr, double inv_T, cons
 }
 
 constexpr double kBand = 1e-5;  // relative band of uncertain residual signs
+// draw-pass kernels run at least this many waves per SIMD: a fully unrolled run of 16 token pairs
+// would otherwise take ~190 VGPRs (two waves per SIMD); capped, the compiler interleaves fewer exps
+// per wave and the other waves hide the table reads
+constexpr int kDrawPassWaves = 5;
 constexpr int kEsLds = 512;     // chunk normaliser pairs staged in LDS by the select
 
 __device__ inline bool excluded(int x, const int* excl, int nexcl) {

@@ -38,11 +38,6 @@
 namespace psispec {
 namespace {
 
-// at least this many waves per SIMD: a fully unrolled run of 16 token pairs would otherwise take
-// ~190 VGPRs (two waves per SIMD); capped, the compiler interleaves fewer exps per wave and the
-// other waves hide the table reads
-constexpr int kDrawPassWaves = 5;
-
 // kList: the draws are a device-side list (the grid loops over its entries); a separate
 // instantiation, since the loop keeps registers live that the one-task-per-block form does not need
 template <typename T, bool kTopp, bool kList>
@@ -122,8 +117,6 @@ constexpr unsigned kListSelectBlocks = 256;  // grid of the select over listed d
 
 }  // namespace
 
-namespace {
-
 int draw_vec_ok(const DrawArgs& a, psispec_dtype dtype) {
   const size_t es = dtype == PSISPEC_BF16 ? 2 : 4;
   return ((size_t)a.V * es) % 16 == 0 && ((size_t)a.rs.pstride * es) % 16 == 0 &&
@@ -139,8 +132,6 @@ hipError_t launch_draw_select(const DrawArgs& a, psispec_dtype dtype, hipStream_
     PSISPEC_LAUNCH("draw_select", k_draw_select<float>, dim3(sgrid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
-
-}  // namespace
 
 hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;

@@ -124,6 +124,11 @@ struct TreeArgs {
   float* node_ratios;
 };
 hipError_t launch_decide_tree(const TreeArgs& a, psispec_dtype dtype, hipStream_t stream);
+// Trees of at most 64 nodes: the walk and the draw pass in one launch (block (r, c) walks request r
+// and draws chunk c of its stopping row; the chunk-0 block writes the outputs), then the select.
+struct DrawArgs;
+hipError_t launch_decide_tree_draw(const TreeArgs& ta, const DrawArgs& da, psispec_dtype dtype,
+                                   hipStream_t stream);
 
 // treeq.hip -- tree verify with candidates drawn from the draft (recursive rejection)
 constexpr int kMaxSampledChildren = 8;  // children per node under the sampled rule
@@ -208,6 +213,9 @@ hipError_t launch_draw(const DrawArgs& a, psispec_dtype dtype, hipStream_t strea
 // draws chunk c; the chunk-0 block writes the outputs), then the select.
 hipError_t launch_decide_draw(const LinearArgs& la, const DrawArgs& da, psispec_dtype dtype,
                               hipStream_t stream);
+// The select alone, and whether the pass may read the rows with 16-byte loads.
+hipError_t launch_draw_select(const DrawArgs& a, psispec_dtype dtype, hipStream_t stream);
+int draw_vec_ok(const DrawArgs& a, psispec_dtype dtype);
 
 // linear.hip -- small linear verifies (no nucleus, one chunk per row) in one launch: one block per
 // request stages its rows in LDS, computes their pairs, then runs the accept test, the draw pass

@@ -10,12 +10,15 @@
 // tokens its rejected children remove from the residual.  The draw itself runs in the fp64 draw
 // kernels.
 #include "launch.h"
+#include "draw.h"
 
 namespace psispec {
 namespace {
 
 constexpr int kMaxNodes = 1024;
 constexpr int kStagePairs = 4096;  // row pairs of a request staged in LDS (more: read in place)
+constexpr int kSmallNodes = 64;    // trees the accept walk fused with the draw pass takes
+constexpr int kSmallPairs = 1024;  // row pairs it stages in LDS (more: read in place)
 
 __device__ inline int row_status(float lmax, double Z) {
   const bool ok = (lmax > kNegBig) && (lmax < __builtin_huge_valf()) && (Z > 0.0) && (Z < 1e300);
@@ -32,24 +35,34 @@ __device__ inline double node_prob(const TreeArgs& a, int64_t row, float lmax, d
   return pr;
 }
 
-template <typename T>
-__global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
-  const int r = blockIdx.x;
+// What the draw pass of the fused kernel takes from the walk, in LDS: the draw description, the
+// stopping row's maximum logit and the tokens its rejected children remove.
+struct TreeWalkLocal {
+  DrawDesc desc;
+  float lmax;
+  int32_t excl[kSmallNodes];
+};
+
+// Node ratios and the walk of request r, by one wave (threads 0..63 of the calling block; it syncs
+// with wave barriers only).  kMaxN: most nodes per tree (its LDS arrays); loc: the fused kernel's
+// LDS copies (with quiet, the only output: another block of the request writes the call's).
+template <typename T, int kMaxN, int kPairs>
+__device__ inline void decide_tree_request(const TreeArgs& a, int r, bool quiet, TreeWalkLocal* loc) {
   const int t = threadIdx.x;
   const int N = a.N, V = a.V;
   const int64_t row0 = (int64_t)r * (N + 1);
   const int32_t* par = a.parent + (int64_t)r * N;
   const int32_t* tok = a.node_tokens + (int64_t)r * N;
 
-  __shared__ float s_lmax[kMaxNodes + 1];
-  __shared__ double s_Z[kMaxNodes + 1];
-  __shared__ double s_ratio[kMaxNodes];
+  __shared__ float s_lmax[kMaxN + 1];
+  __shared__ double s_Z[kMaxN + 1];
+  __shared__ double s_ratio[kMaxN];
   __shared__ int s_st;
-  __shared__ int32_t s_par[kMaxNodes], s_tok[kMaxNodes];
-  __shared__ double s_u[kMaxNodes];
-  __shared__ double s_pown[kMaxNodes];
-  __shared__ int s_first[kMaxNodes];
-  __shared__ float2 s_pair[kStagePairs];
+  __shared__ int32_t s_par[kMaxN], s_tok[kMaxN];
+  __shared__ double s_u[kMaxN];
+  __shared__ double s_pown[kMaxN];
+  __shared__ int s_first[kMaxN];
+  __shared__ float2 s_pair[kPairs];
 
   // 0. the tree, every node's accept uniform (Philox of (request, c+1, accept)) and the row pairs,
   //    loaded or computed by the whole wave up front; then the logit of each node's token in its
@@ -62,11 +75,11 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
     s_u[j] = philox_uniform(a.seed, a.request_base + (uint32_t)r, (uint32_t)(j + 1), kPurposeAccept,
                             a.step);
   }
-  const bool staged = (int64_t)(N + 1) * a.nchunk <= kStagePairs;
+  const bool staged = (int64_t)(N + 1) * a.nchunk <= kPairs;
   if (staged)
     for (int i = t; i < (N + 1) * a.nchunk; i += 64) s_pair[i] = a.part[row0 * a.nchunk + i];
   wave_sync();
-  constexpr int kGl = kMaxNodes / 64;  // nodes per lane
+  constexpr int kGl = kMaxN / 64;  // nodes per lane
   float gl[kGl];                       // node t + 64 k's token logit
 #pragma unroll
   for (int k = 0; k < kGl; ++k) {
@@ -103,7 +116,7 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
     st |= rs;
     s_lmax[j] = lmax;
     s_Z[j] = Z;
-    a.rowstat[row] = RowStat{lmax, rs, Z};
+    if (!quiet) a.rowstat[row] = RowStat{lmax, rs, Z};
   }
   // 2. structure: parents precede children, depth within max_depth.  Each lane climbs its node's
   //    parent chain (indices strictly decrease along a valid chain; a chain that meets an invalid
@@ -149,7 +162,7 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
   // of its siblings, and each lane then visits only its earlier siblings, in index order (LDS
   // reads), so R takes the same subtractions in index order as the general form below.
   wave_sync();
-  if (N <= 64) {
+  if (kMaxN <= 64 || N <= 64) {
     const int pj = t < N ? s_par[t] : -2, tj = t < N ? s_tok[t] : -1;
     uint64_t sib = 0;
     for (uint64_t todo = __ballot(t < N); todo;) {
@@ -181,9 +194,9 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
     if (t < N) {
       if (tj >= 0 && tj < V && pj >= -1 && pj < t) ratio = R > 0.0 ? fmin(1.0, res / R) : 0.0;
       s_ratio[t] = ratio;
-      if (a.node_ratios) a.node_ratios[(int64_t)r * N + t] = (float)ratio;
+      if (a.node_ratios && !quiet) a.node_ratios[(int64_t)r * N + t] = (float)ratio;
     }
-  } else {
+  } else if constexpr (kMaxN > 64) {
     for (int j = t; j < N; j += 64) {
       const int v = s_par[j], tj = s_tok[j];
       int first = 1;
@@ -213,7 +226,7 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
         ratio = R > 0.0 ? fmin(1.0, res / R) : 0.0;
       }
       s_ratio[j] = ratio;
-      if (a.node_ratios) a.node_ratios[(int64_t)r * N + j] = (float)ratio;
+      if (a.node_ratios && !quiet) a.node_ratios[(int64_t)r * N + j] = (float)ratio;
     }
   }
 #pragma unroll
@@ -226,7 +239,9 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
   const int Dp1 = a.max_depth + 1;
   int32_t* nodes = a.accept_nodes + (int64_t)r * a.max_depth;
   int32_t* out = a.out_tokens + (int64_t)r * Dp1;
-  int32_t* excl = a.excl + (int64_t)r * N;
+  // the removed tokens: the fused kernel's LDS list (copied to the workspace after the walk unless
+  // quiet), else the workspace
+  int32_t* excl = loc ? loc->excl : a.excl + (int64_t)r * N;
   int cur = -1, dep = 0, nexcl = 0;
   if (t < 64) {
     st |= s_st;
@@ -247,7 +262,7 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
           if (firstacc < 64) next = c0 + firstacc;
         }
         if (next < 0) break;
-        if (t == 0) {
+        if (t == 0 && !quiet) {
           nodes[dep] = next;
           out[dep] = s_tok[next];
         }
@@ -256,10 +271,16 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
       }
     }
   }
+  if (loc && !quiet) {
+    wave_sync();  // the LDS list is complete
+    for (int i = t; i < nexcl; i += 64) a.excl[(int64_t)r * N + i] = loc->excl[i];
+  }
   if (t == 0) {
-    for (int i = dep; i < a.max_depth; ++i) nodes[i] = -1;
-    for (int i = dep; i < Dp1; ++i) out[i] = -1;
-    a.accept_len[r] = dep;
+    if (!quiet) {
+      for (int i = dep; i < a.max_depth; ++i) nodes[i] = -1;
+      for (int i = dep; i < Dp1; ++i) out[i] = -1;
+      a.accept_len[r] = dep;
+    }
     DrawDesc dd;
     dd.prow = (int32_t)(row0 + cur + 1);
     dd.qrow = -1;
@@ -270,11 +291,64 @@ __global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
     dd.ph_req = r;
     dd.purpose = kPurposeDraw;
     dd.factor = 1.0;
-    a.desc[r] = dd;
+    if (!quiet) a.desc[r] = dd;
+    if (loc) {
+      loc->desc = dd;
+      loc->lmax = s_lmax[cur + 1];
+    }
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(64) void k_decide_tree(TreeArgs a) {
+  decide_tree_request<T, kMaxNodes, kStagePairs>(a, blockIdx.x, false, nullptr);
+}
+
+// The chosen-candidate tree's walk fused with its draw pass (trees of at most kSmallNodes nodes):
+// block (r, c) runs request r's walk in wave 0 into LDS, then draws chunk c of the stopping row from
+// those copies; the chunk-0 block also writes the call's outputs and the records the select
+// reads.  One launch fewer than the walk followed by the pass, and no dependent reads of the
+// description, the row statistics and the removed tokens.
+template <typename T, bool kTopp>
+__global__ __launch_bounds__(kThreads, kDrawPassWaves) void k_decide_tree_draw(TreeArgs ta,
+                                                                               DrawArgs da,
+                                                                               int vec_ok) {
+  __shared__ double tbl[kExpTable];
+  __shared__ TreeWalkLocal loc;
+  exp_table_fill(tbl);  // read after the barriers below
+  const int r = blockIdx.x / da.nchunk_draw;
+  const int c = blockIdx.x - r * da.nchunk_draw;
+  if (threadIdx.x < 64) decide_tree_request<T, kSmallNodes, kSmallPairs>(ta, r, c != 0, &loc);
+  __syncthreads();  // the description, the stopping row's maximum and the removed tokens are in LDS
+  const DrawDesc d = loc.desc;
+  RowView v;
+  v.lmax_p = loc.lmax;
+  v.thr_p = kTopp ? ta.topp[d.prow].thr : -__builtin_huge_valf();
+  v.lmax_q = 0.f;
+  v.thr_q = 0.f;
+  DrawArgs dl = da;
+  dl.excl = loc.excl;  // read at excl[r * excl_stride + i]: the LDS list
+  dl.excl_stride = 0;
+  draw_pass_run<T, kTopp>(dl, r, c, vec_ok, d, v, 0.0, tbl);
+}
+
 }  // namespace
+
+hipError_t launch_decide_tree_draw(const TreeArgs& ta, const DrawArgs& da, psispec_dtype dtype,
+                                   hipStream_t stream) {
+  if (da.batch == 0) return hipSuccess;
+  if (ta.N > kSmallNodes || da.list || ta.batch != da.batch || ta.use_topp != da.use_topp)
+    return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((int64_t)da.batch * da.nchunk_draw);
+  const int vec_ok = draw_vec_ok(da, dtype);
+  const bool bf = dtype == PSISPEC_BF16, tp = da.use_topp;
+  auto kern = bf ? (tp ? k_decide_tree_draw<bf16_t, true> : k_decide_tree_draw<bf16_t, false>)
+                 : (tp ? k_decide_tree_draw<float, true> : k_decide_tree_draw<float, false>);
+  PSISPEC_LAUNCH("decide_tree_draw", kern, dim3(grid), dim3(kThreads), 0, stream, ta, da, vec_ok);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_draw_select(da, dtype, stream);
+}
 
 hipError_t launch_decide_tree(const TreeArgs& a, psispec_dtype dtype, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
