@@ -321,7 +321,6 @@ psispec_status verify_tree_sampled(const void* p_logits, const void* q_logits, p
     if (level == 1 && launch_tree_resolve(ta, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
     if (launch_tree_chain_pass(ta, level, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
   }
-  if (launch_decide_tree_sampled(ta, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
 
   DrawArgs da{};
   da.rs = rs;
@@ -348,6 +347,10 @@ psispec_status verify_tree_sampled(const void* p_logits, const void* q_logits, p
   da.upool = carve<double2>(workspace, pl.off_upool);
   da.out_tokens = out_tokens;
   da.status = status;
+  if (N <= 64)  // the walk runs in each draw block: one launch fewer
+    return launch_decide_tree_sampled_draw(ta, da, dtype, stream) == hipSuccess ? PSISPEC_OK
+                                                                               : PSISPEC_EHIP;
+  if (launch_decide_tree_sampled(ta, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
   if (launch_draw(da, dtype, stream) != hipSuccess) return PSISPEC_EHIP;
   return PSISPEC_OK;
 }

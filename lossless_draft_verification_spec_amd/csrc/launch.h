@@ -129,6 +129,11 @@ hipError_t launch_decide_tree(const TreeArgs& a, psispec_dtype dtype, hipStream_
 struct DrawArgs;
 hipError_t launch_decide_tree_draw(const TreeArgs& ta, const DrawArgs& da, psispec_dtype dtype,
                                    hipStream_t stream);
+struct TreeQArgs;
+// Sampled candidates, trees of at most 64 nodes: the chains, then the walk and the draw pass in one
+// launch, then the select.
+hipError_t launch_decide_tree_sampled_draw(const TreeQArgs& ta, const DrawArgs& da,
+                                           psispec_dtype dtype, hipStream_t stream);
 
 // treeq.hip -- tree verify with candidates drawn from the draft (recursive rejection)
 constexpr int kMaxSampledChildren = 8;  // children per node under the sampled rule

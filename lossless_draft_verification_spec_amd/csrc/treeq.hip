@@ -398,10 +398,13 @@ __device__ inline double gathered_prob(const TreeQArgs& a, int64_t row, int tok,
   return exp(((double)l - (double)a.rowstat[row].lmax) * a.inv_T) / E;
 }
 
-// One wave per request: structure, node ratios, the walk, the draw description.
-template <typename T>
-__global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
-  const int r = blockIdx.x;
+// Structure, node ratios, the walk and the draw description of request r, by one wave (threads
+// 0..63 of the calling block; it syncs with wave barriers only).  kMaxN: most nodes per tree (its
+// LDS arrays).  desc_local: the fused kernel's LDS copy of the description (with quiet, the only
+// output: another block of the request writes the call's).
+template <typename T, int kMaxN>
+__device__ inline void decide_tree_sampled_request(const TreeQArgs& a, int r, bool quiet,
+                                                   DrawDesc* desc_local) {
   const int t = threadIdx.x;
   const int N = a.N, V = a.V;
   const int64_t row0 = (int64_t)r * (N + 1);
@@ -409,8 +412,8 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
   const int32_t* par = a.parent + (int64_t)r * N;
   const int32_t* tok = a.node_tokens + (int64_t)r * N;
 
-  __shared__ int32_t s_par[1024], s_tok[1024];
-  __shared__ double s_u[1024], s_ratio[1024];
+  __shared__ int32_t s_par[kMaxN], s_tok[kMaxN];
+  __shared__ double s_u[kMaxN], s_ratio[kMaxN];
   __shared__ int s_st;
 
   for (int j = t; j < N; j += 64) {
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
     s_u[j] = philox_uniform(a.seed, a.request_base + (uint32_t)r, (uint32_t)(j + 1), kPurposeAccept,
                             a.step);
   }
-  __syncthreads();
+  wave_sync();
 
   // 1. structure: parents precede children, depth within max_depth, at most a.max_children
   //    children per node (the level-0 pass counted them); row statistics of the request's rows
@@ -474,11 +477,11 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
       }
     }
     s_ratio[j] = ratio;
-    if (a.node_ratios) a.node_ratios[(int64_t)r * N + j] = (float)ratio;
+    if (a.node_ratios && !quiet) a.node_ratios[(int64_t)r * N + j] = (float)ratio;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) st |= __shfl_xor(st, off, 64);
-  __syncthreads();
+  wave_sync();
 
   // 3. the walk: at each node the children in index order, 64 at a time; the first accepted
   //    child (ballot) is the next node
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
         if (m >= 1 && rejected >= a.chain[row0 + cur + 1].stuck) st |= PSISPEC_ST_RESID_ZERO;
       }
       if (next < 0) break;
-      if (t == 0) {
+      if (t == 0 && !quiet) {
         nodes[dep] = next;
         out[dep] = s_tok[next];
       }
@@ -516,9 +519,11 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
     }
   }
   if (t == 0) {
-    for (int i = dep; i < a.max_depth; ++i) nodes[i] = -1;
-    for (int i = dep; i < Dp1; ++i) out[i] = -1;
-    a.accept_len[r] = dep;
+    if (!quiet) {
+      for (int i = dep; i < a.max_depth; ++i) nodes[i] = -1;
+      for (int i = dep; i < Dp1; ++i) out[i] = -1;
+      a.accept_len[r] = dep;
+    }
     const int64_t g = row0 + cur + 1;
     const int m = (s_st & PSISPEC_ST_BAD_PARENT) ? 0 : a.nchild[g];
     DrawDesc dd;
@@ -531,8 +536,33 @@ __global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
     dd.ph_req = r;
     dd.purpose = kPurposeDraw;
     dd.factor = m >= 1 ? a.chain[g].c[m] : 1.0;
-    a.desc[r] = dd;
+    if (!quiet) a.desc[r] = dd;
+    if (desc_local) *desc_local = dd;
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void k_decide_tree_sampled(TreeQArgs a) {
+  decide_tree_sampled_request<T, 1024>(a, blockIdx.x, false, nullptr);
+}
+
+// The sampled tree's walk fused with its draw pass (trees of at most 64 nodes): block (r, c) runs
+// request r's walk in wave 0 into an LDS copy of the draw description, then draws chunk c of the
+// stopping rows; the chunk-0 block also writes the call's outputs and the description the select
+// reads.  One launch fewer than the walk followed by the pass, and no read of the description.
+template <typename T, bool kTopp>
+__global__ __launch_bounds__(kThreads, kDrawPassWaves) void k_decide_tree_sampled_draw(
+    TreeQArgs ta, DrawArgs da, int vec_ok) {
+  __shared__ double tbl[kExpTable];
+  __shared__ DrawDesc s_d;
+  exp_table_fill(tbl);  // read after the barriers below
+  const int r = blockIdx.x / da.nchunk_draw;
+  const int c = blockIdx.x - r * da.nchunk_draw;
+  if (threadIdx.x < 64) decide_tree_sampled_request<T, 64>(ta, r, c != 0, &s_d);
+  __syncthreads();  // the description is in LDS
+  const DrawDesc d = s_d;
+  draw_pass_run<T, kTopp>(da, r, c, vec_ok, d, row_view(da, d),
+                          d.qrow >= 0 ? rho_estimate(da, d) : 0.0, tbl);
 }
 
 }  // namespace
@@ -582,6 +612,29 @@ hipError_t launch_tree_chain_pass(const TreeQArgs& a, int level, psispec_dtype d
   PSISPEC_LAUNCH("tree_chain", kern, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, level,
                  vec_ok);
   return hipGetLastError();
+}
+
+hipError_t launch_decide_tree_sampled_draw(const TreeQArgs& ta, const DrawArgs& da,
+                                           psispec_dtype dtype, hipStream_t stream) {
+  if (ta.batch == 0) return hipSuccess;
+  if (ta.N > 64 || da.list || ta.batch != da.batch || ta.use_topp != da.use_topp)
+    return hipErrorInvalidValue;
+  PSISPEC_LAUNCH("tree_chain_final", k_tree_chain_final, dim3((unsigned)ta.rs.nP), dim3(64), 0,
+                 stream, ta);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)((int64_t)da.batch * da.nchunk_draw);
+  const int vec_ok = draw_vec_ok(da, dtype);
+  const bool bf = dtype == PSISPEC_BF16, tp = da.use_topp;
+  auto kern = bf ? (tp ? k_decide_tree_sampled_draw<bf16_t, true>
+                       : k_decide_tree_sampled_draw<bf16_t, false>)
+                 : (tp ? k_decide_tree_sampled_draw<float, true>
+                       : k_decide_tree_sampled_draw<float, false>);
+  PSISPEC_LAUNCH("decide_tree_sampled_draw", kern, dim3(grid), dim3(kThreads), 0, stream, ta, da,
+                 vec_ok);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_draw_select(da, dtype, stream);
 }
 
 hipError_t launch_decide_tree_sampled(const TreeQArgs& a, psispec_dtype dtype, hipStream_t stream) {
