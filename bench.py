@@ -210,6 +210,30 @@ def measure_peaks(torch, pkg):
                        "traffic, best of 5 launches")
 
 
+def best_peaks(a, b):
+    """The better of two measurements of the ceilings (each figure on its own), with both kept."""
+    out = dict(a)
+    for key, us_key in (("hbm_read_gbs", "hbm_read_us"), ("mfma_bf16_tflops", "mfma_us")):
+        out[key + "_runs"] = [a[key], b[key]]
+        if b[key] > a[key]:
+            out[key], out[us_key] = b[key], b[us_key]
+    out["method"] = a["method"] + "; measured before the legs and again after them, the better kept"
+    return out
+
+
+def apply_peaks(leg, peaks):
+    """Re-derive a leg's measured-peak fractions from the final ceilings."""
+    rf = leg.get("roofline")
+    if rf and rf.get("bound") == "hbm":
+        rf["peak_measured"] = peaks["hbm_read_gbs"]
+        rf["frac_measured"] = round(rf["achieved"] / peaks["hbm_read_gbs"], 4)
+    elif rf and rf.get("bound") == "mfma":
+        rf["peak_measured"] = peaks["mfma_bf16_tflops"]
+        rf["frac_measured"] = round(rf["achieved"] / peaks["mfma_bf16_tflops"], 4)
+    if leg.get("hbm_gbs_step") is not None and "hbm_frac_step_measured" in leg:
+        leg["hbm_frac_step_measured"] = round(leg["hbm_gbs_step"] / peaks["hbm_read_gbs"], 4)
+
+
 # ------------------------------------------------------------------------------------------------
 # legs
 # ------------------------------------------------------------------------------------------------
@@ -733,6 +757,14 @@ def main():
         legs[key] = fn()
         ms = legs[key].get("ms_per_step", legs[key].get("us_per_call", 0) / 1e3)
         log(f"{key}: {1e3 * ms:.1f} us/call, call {legs[key].get('call_us')}")
+    # the ceilings again, on a warm GPU: every measured fraction takes the better of the two runs
+    # (a ceiling measured low would overstate them)
+    end_peaks = measure_peaks(torch, pkg)
+    log(f"peaks at the end: read {end_peaks['hbm_read_gbs']} GB/s, bf16 MFMA "
+        f"{end_peaks['mfma_bf16_tflops']} TFLOP/s")
+    peaks = best_peaks(peaks, end_peaks)
+    for d in (res, *legs.values()):
+        apply_peaks(d, peaks)
     pr = workloads.PRESETS["c2"]
     cpu = None if args.no_cpu else cpu_baseline(host, pr, args.cpu_seconds)
     line = {
