@@ -9,7 +9,7 @@
 //
 // The draw decides an integer from floating point, so it is computed in fp64 end to end
 // (normalisers, weights and prefix sums) with a table-driven fp64 exp; all reductions run in a
-// fixed order.  Two kernels:
+// fixed order.  Two steps:
 //   k_draw_pass:   one fp64 pass over the stopping row(s): a block per chunk of 4096 spw tokens,
 //                  each wave taking spw sub-chunks of 1024 tokens in turn (spw = 1, 2, 4 or 8: more
 //                  when the draws alone fill the chip, which spreads each block's set-up over more
@@ -21,12 +21,14 @@
 //                  below ~1e-6), as a comparison of exponents (t_p - t_q against 256 log2 rho);
 //                  tokens within a 1e-5 band of the sign change are uncertain: each wave packs the
 //                  exact (e_p, e_q) of its sub-chunk's uncertain tokens, in token order, into a
-//                  segment of a per-request pool.  The pass stores per sub-chunk the sums A_p, A_q
-//                  of e_p, e_q over the positive tokens and the segment, and per chunk the partial
-//                  normalisers E_p, E_q.
+//                  segment of its chunk's slice of the request's pool.  The pass stores per
+//                  sub-chunk the sums A_p, A_q of e_p, e_q over the positive tokens and the
+//                  segment, and per chunk the partial normalisers E_p, E_q.  The linear verify,
+//                  and the trees of at most 64 nodes (tree.hip, treeq.hip), run the same pass
+//                  fused after their accept test or walk (k_decide_draw and its tree forms).
 //   k_draw_select: per request, the exact E_p, E_q give rho; each sub-chunk's mass is
 //                  (A_p - rho A_q) / E_p plus the residual weights of its uncertain tokens (added
-//                  in token order); it is recomputed token by token only when the pool overflowed
+//                  in token order); it is recomputed token by token only when the slice overflowed
 //                  or rho strays from the HBM-pass ratio by more than a quarter of the band (which
 //                  voids the classification); a block scan over the
 //                  masses locates u' S, then a block scan over that sub-chunk's 1024 weights
