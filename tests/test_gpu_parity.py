@@ -388,6 +388,18 @@ def test_tree_small(dtype, batch, N, V):
     t.check()
 
 
+@pytest.mark.parametrize("N", [63, 64, 65])
+@pytest.mark.parametrize("dtype,top_p", [(torch.float32, 1.0), (torch.bfloat16, 0.9)])
+def test_tree_walk_fused_boundary(N, dtype, top_p):
+    """Trees of up to 64 nodes run their walk inside the draw pass's blocks, larger ones as a
+    launch of its own: 63, 64 and 65 nodes on either side of that boundary, with and without the
+    nucleus."""
+    p, parent, tokens = _rand_tree(3, N, 2049, dtype, seed=N * 7, dup=True)
+    t = _tree_compare(p, parent, tokens, 8, top_p=top_p, steps=range(4))
+    print(t)
+    t.check()
+
+
 @pytest.mark.parametrize("k,depth,seed", [(200, 4, 31), (3, 64, 32)])
 def test_tree_max_nodes(k, depth, seed):
     """N = 1024, the largest tree: a wide one (a node may have up to 200 children, so the walk's

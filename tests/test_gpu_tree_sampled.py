@@ -50,6 +50,20 @@ def test_sampled_tree_small(dtype, batch, N, V, branching):
     t.check()
 
 
+@pytest.mark.parametrize("N", [63, 64, 65])
+@pytest.mark.parametrize("dtype,T,top_p", [(torch.float32, 1.0, 1.0), (torch.bfloat16, 0.7, 0.9)])
+def test_sampled_tree_walk_fused_boundary(N, dtype, T, top_p):
+    """Trees of up to 64 nodes run their walk inside the draw pass's blocks, larger ones as a
+    launch of its own: 63, 64 and 65 nodes on either side of that boundary."""
+    from dataclasses import replace
+    pr = replace(workloads.PRESETS["c4s"], dtype=dtype, depth=8, T=T, top_p=top_p)
+    tin = workloads.make_tree_sampled(pr, device=DEV, batch=3, V=2049, N=N,
+                                      branching=(4, 3, 2, 2, 1, 1))
+    t = _compare(tin, T=T, top_p=top_p, steps=range(4))
+    print(t)
+    t.check()
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_sampled_tree_max_nodes(dtype):
     """1024 nodes, eight children for every node down to depth 4 (the largest tree and fan-out the
