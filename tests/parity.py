@@ -10,6 +10,9 @@
   input-error bits -- non-finite row, bad token, bad parent -- when one of those is set, since the
   other bits then come from arithmetic on invalid data); their other outputs are unspecified.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -157,13 +160,20 @@ def gpu_linear_numpy(out: dict) -> dict:
 
 def oracle_linear_requests(p_host, q_host, drafts_host, rows, T, top_p, seed, step, flags=0,
                            request_base=0):
-    """Oracle outputs for the listed requests (each with its own global request id)."""
-    outs = []
-    for r in rows:
-        o = oracle.verify_linear(p_host[r:r + 1], q_host[r:r + 1], drafts_host[r:r + 1], T=T,
-                                 top_p=top_p, seed=seed, step=step,
-                                 request_base=request_base + r, flags=flags)
-        outs.append(o)
+    """Oracle outputs for the listed requests (each with its own global request id).  The requests
+    are independent single-threaded oracle calls; ctypes releases the GIL during each, so they run
+    on up to 16 host threads (results in request order)."""
+    def one(r):
+        return oracle.verify_linear(p_host[r:r + 1], q_host[r:r + 1], drafts_host[r:r + 1], T=T,
+                                    top_p=top_p, seed=seed, step=step,
+                                    request_base=request_base + r, flags=flags)
+
+    workers = min(16, len(os.sched_getaffinity(0)), max(1, len(rows)))
+    if workers > 1:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            outs = list(ex.map(one, rows))
+    else:
+        outs = [one(r) for r in rows]
     return {k: np.concatenate([o[k] for o in outs]) for k in outs[0]}
 
 
